@@ -1,0 +1,340 @@
+"""float64 oracle of the V-JEPA 2 / 2.1 encoder forward and the V-JEPA 2 masked predictor.
+
+Test infrastructure (see the package docstring): plain numpy, float64, no blocking,
+fusion or reordering beyond what each cited definition states.  The only liberty taken
+is that attention is evaluated a slab of query rows at a time, which changes nothing:
+each output row is a function of its own query row and all keys/values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "IMAGENET_MEAN", "IMAGENET_STD", "EncoderSpec", "PredictorSpec",
+    "normalize_frames", "patchify", "id_to_thw", "rope_positions", "rope_axis_dim",
+    "rope_omegas", "rope_angle_index", "rope_angles", "rope_rotate", "rope_rotate_with_angles",
+    "layer_norm", "gelu_erf", "linear", "attention", "block", "encoder_forward",
+    "encode_tokens", "encoder_forward_batch", "predictor_forward",
+]
+
+# [Notes §1 "pre.mean / std / rescale": ImageNet, 1/255]; values as given on [HFport
+# "Preprocessing"] and [Notes §5].
+IMAGENET_MEAN = (0.485, 0.456, 0.406)
+IMAGENET_STD = (0.229, 0.224, 0.225)
+
+
+@dataclasses.dataclass(frozen=True)
+class EncoderSpec:
+    """Hyper-parameters of one encoder ([Notes §1 table])."""
+    embed_dim: int
+    n_layer: int
+    n_head: int
+    ffn_dim: int
+    patch: int = 16
+    tubelet: int = 2
+    in_chans: int = 3
+    has_mod_embed: bool = False
+    final_norm: bool = True
+    layout: str = "tiled"          # "tiled" (V-JEPA 2) or "interleaved" (V-JEPA 2.1)
+    ref_grid: int = 0              # 0: no interpolation; else R ([Notes §4.3], R = 16)
+    ln_eps: float = 1e-6
+    theta: float = 10000.0
+
+    @property
+    def head_dim(self) -> int:
+        return self.embed_dim // self.n_head
+
+
+@dataclasses.dataclass(frozen=True)
+class PredictorSpec:
+    """V-JEPA 2 masked predictor ([Notes §1]: 384 / 12 / 12 / 1536, 10 mask tokens,
+    out_dim 1024, tiled, not interpolated)."""
+    enc_dim: int
+    embed_dim: int
+    n_layer: int
+    n_head: int
+    ffn_dim: int
+    n_mask_tokens: int
+    out_dim: int
+    layout: str = "tiled"
+    ln_eps: float = 1e-6
+    theta: float = 10000.0
+
+    @property
+    def head_dim(self) -> int:
+        return self.embed_dim // self.n_head
+
+
+# --------------------------------------------------------------------------- pixels
+
+
+def normalize_frames(u8: np.ndarray) -> np.ndarray:
+    """uint8 frames [T, H, W, 3] -> model input X [3, T, H, W] float64.
+
+    Rescale by 1/255 then subtract the ImageNet mean and divide by the std, per channel
+    ([Notes §5], [HFport "Preprocessing"]); the model layout is channels first, then
+    time, height, width ([Notes §5]: the HF processor's [B, T, C, H, W] is permuted to
+    [B, C, T, H, W] before the Conv3d).
+    """
+    x = u8.astype(np.float64) / 255.0
+    x = (x - np.asarray(IMAGENET_MEAN)) / np.asarray(IMAGENET_STD)
+    return np.transpose(x, (3, 0, 1, 2))
+
+
+def patchify(X: np.ndarray, tubelet: int = 2, patch: int = 16) -> np.ndarray:
+    """Tubelet patchify [C, T, H, W] -> [N, C*tubelet*patch*patch].
+
+    Token order is T-major, then H, then W ([Notes §4]: t = i // (gh*gw), ...).  Feature
+    order is C, T, H, W: the Conv3d kernel [D, 3, 2, 16, 16] flattened row-major to
+    [D, 1536] ([Notes §2], first row of the key-map table), so feature
+    f = ((c*tubelet + dt)*patch + dy)*patch + dx reads X[c, tubelet*t' + dt,
+    patch*h' + dy, patch*w' + dx].
+    """
+    C, T, H, W = X.shape
+    if T % tubelet or H % patch or W % patch:
+        raise ValueError("clip not divisible into tubelets")
+    gt, gh, gw = T // tubelet, H // patch, W // patch
+    p = X.reshape(C, gt, tubelet, gh, patch, gw, patch)      # c t' dt h' dy w' dx
+    p = np.transpose(p, (1, 3, 5, 0, 2, 4, 6))                # t' h' w' | c dt dy dx
+    return p.reshape(gt * gh * gw, C * tubelet * patch * patch)
+
+
+# --------------------------------------------------------------------------- positions
+
+
+def id_to_thw(ids: np.ndarray, gh: int, gw: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Token id -> integer grid coordinates, T-major ([Notes §4]):
+    t = i // (gh*gw), h = (i mod gh*gw) // gw, w = i mod gw."""
+    ids = np.asarray(ids, dtype=np.int64)
+    t = ids // (gh * gw)
+    h = (ids % (gh * gw)) // gw
+    w = ids % gw
+    return t, h, w
+
+
+def rope_positions(ids: np.ndarray, gh: int, gw: int, ref_grid: int = 0) -> np.ndarray:
+    """float64 positions [N, 3] = (p_t, p_h, p_w) of the token ids.
+
+    Without interpolation the positions are the integer coordinates cast to float
+    ([Notes §4.2]: positions cast to float).  With interpolation (V-JEPA 2.1 encoder,
+    [Notes §4.3]): h' = h*(R-1)/(gh-1), w' = w*(R-1)/(gw-1), t unchanged; a grid side of
+    1 is rejected (division by zero).
+    """
+    t, h, w = id_to_thw(ids, gh, gw)
+    pt, ph, pw = t.astype(np.float64), h.astype(np.float64), w.astype(np.float64)
+    if ref_grid:
+        if gh <= 1 or gw <= 1:
+            raise ValueError("position interpolation needs gh > 1 and gw > 1")
+        ph = ph * (ref_grid - 1) / (gh - 1)
+        pw = pw * (ref_grid - 1) / (gw - 1)
+    return np.stack([pt, ph, pw], axis=1)
+
+
+# --------------------------------------------------------------------------- RoPE
+
+
+def rope_axis_dim(head_dim: int) -> int:
+    """Rotated dims per axis, d = 2*((head_dim // 3) // 2) ([Notes §1], [Notes §4])."""
+    return 2 * ((head_dim // 3) // 2)
+
+
+def rope_omegas(d: int, theta: float = 10000.0) -> np.ndarray:
+    """omega_k = 1 / theta**(k / (d/2)), k = 0 .. d/2-1 ([Notes §4], frequencies)."""
+    k = np.arange(d // 2, dtype=np.float64)
+    return 1.0 / theta ** (k / (d / 2.0))
+
+
+def rope_angle_index(d: int, layout: str) -> np.ndarray:
+    """Which of the d/2 frequencies each of the d rotated dims of an axis uses.
+
+    tiled ([Notes §4.1]): the length-d/2 table is repeated whole, dim j uses j mod d/2.
+    interleaved ([Notes §4.2]): each entry is repeated twice in place, dim j uses j // 2.
+    """
+    j = np.arange(d)
+    if layout == "tiled":
+        return j % (d // 2)
+    if layout == "interleaved":
+        return j // 2
+    raise ValueError(f"unknown RoPE layout {layout!r}")
+
+
+def rope_angles(pos: np.ndarray, head_dim: int, layout: str, theta: float = 10000.0) -> np.ndarray:
+    """Per-dim angles [N, 3d]: axis a in (t, h, w) owns dims [a*d, (a+1)*d) and dim
+    a*d + j gets angle pos[:, a] * omega[idx(j)] ([Notes §4])."""
+    d = rope_axis_dim(head_dim)
+    om = rope_omegas(d, theta)[rope_angle_index(d, layout)]
+    return np.concatenate([pos[:, a:a + 1] * om[None, :] for a in range(3)], axis=1)
+
+
+def rope_rotate_with_angles(u: np.ndarray, ang: np.ndarray) -> np.ndarray:
+    """u * COS + rot90(u) * SIN over the first ang.shape[-1] dims, rest unchanged.
+
+    rot90 acts on adjacent pairs: rot90(u)[2k] = -u[2k+1], rot90(u)[2k+1] = u[2k]
+    ([Notes §4]).  u: [..., N, hd]; ang: [N, r] with r even and r <= hd.
+    """
+    r = ang.shape[-1]
+    out = np.array(u, dtype=np.float64, copy=True)
+    seg = out[..., :r].copy()
+    rot = np.empty_like(seg)
+    rot[..., 0::2] = -seg[..., 1::2]
+    rot[..., 1::2] = seg[..., 0::2]
+    out[..., :r] = seg * np.cos(ang) + rot * np.sin(ang)
+    return out
+
+
+def rope_rotate(u: np.ndarray, pos: np.ndarray, layout: str, theta: float = 10000.0) -> np.ndarray:
+    """3-D RoPE of head vectors u [..., N, hd] at positions pos [N, 3] ([Notes §4]);
+    the last hd - 3d dims pass through unchanged."""
+    return rope_rotate_with_angles(u, rope_angles(pos, u.shape[-1], layout, theta))
+
+
+# --------------------------------------------------------------------------- layers
+
+
+def layer_norm(x: np.ndarray, weight: np.ndarray, bias: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """LayerNorm over the last axis: centred (two-pass) biased variance, eps inside the
+    square root, then the affine weight and bias.  eps = 1e-6 ([Notes §1]); the centred
+    variance is the CPU backend's ([Parity "Parity on a GPU", backend table])."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * weight + bias
+
+
+def gelu_erf(z: np.ndarray) -> np.ndarray:
+    """Exact GELU, z/2 * (1 + erf(z / sqrt 2)) ([Notes §1]: gelu = exact erf GELU)."""
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
+    """y = x W^T + b with W stored [out, in] ([Notes §2] key map)."""
+    y = x @ np.asarray(w, dtype=np.float64).T
+    if b is not None:
+        y = y + b
+    return y
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_head: int,
+              pos_q: np.ndarray, pos_k: np.ndarray, layout: str, theta: float = 10000.0,
+              rows: Optional[np.ndarray] = None, slab: int = 1024) -> np.ndarray:
+    """Multi-head softmax attention with 3-D RoPE on q and k.
+
+    q [Nq, D], k, v [Nk, D]; head e owns columns [e*hd, (e+1)*hd) (contiguous split of
+    the fused projection).  RoPE is applied to q and k, not v, after the projection and
+    before the 1/sqrt(hd) scaling ([Notes §4]); softmax runs over every key, no mask
+    ([Notes §2] attentive-pool head uses the same softmax(q k^T / sqrt(hd)) v form).
+    ``rows`` selects query rows (default all); each output row depends only on its own
+    query row, so the result is evaluated a slab of rows at a time.
+    """
+    Nq, D = q.shape
+    hd = D // n_head
+    if rows is None:
+        rows = np.arange(Nq)
+    out = np.zeros((len(rows), D))
+    for e in range(n_head):
+        cs = slice(e * hd, (e + 1) * hd)
+        kh = rope_rotate(k[:, cs], pos_k, layout, theta)
+        vh = v[:, cs]
+        for s0 in range(0, len(rows), slab):
+            r = rows[s0:s0 + slab]
+            qh = rope_rotate(q[r, cs], pos_q[r], layout, theta)
+            s = qh @ kh.T / math.sqrt(hd)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)
+            out[s0:s0 + len(r), cs] = p @ vh
+    return out
+
+
+def block(x: np.ndarray, W: Dict[str, np.ndarray], prefix: str, n_head: int, pos: np.ndarray,
+          layout: str, theta: float = 10000.0, eps: float = 1e-6) -> np.ndarray:
+    """One pre-norm transformer block ([Notes §2]: norm1 / fused q,k,v / proj / norm2 /
+    fc1 / fc2; the residual form x += attn(ln1(x)); x += mlp(ln2(x)) is written out for
+    the attentive-pool blocks; [Notes §1]: no layer-scale, no CLS, no registers)."""
+    D = x.shape[1]
+    h = layer_norm(x, W[f"{prefix}.ln1.weight"], W[f"{prefix}.ln1.bias"], eps)
+    qkv = linear(h, W[f"{prefix}.attn_qkv.weight"], W[f"{prefix}.attn_qkv.bias"])
+    # fused rows are [q; k; v] ([Notes §2], attn_qkv)
+    q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
+    o = attention(q, k, v, n_head, pos, pos, layout, theta)
+    x = x + linear(o, W[f"{prefix}.attn_out.weight"], W[f"{prefix}.attn_out.bias"])
+    h2 = layer_norm(x, W[f"{prefix}.ln2.weight"], W[f"{prefix}.ln2.bias"], eps)
+    g = gelu_erf(linear(h2, W[f"{prefix}.ffn_up.weight"], W[f"{prefix}.ffn_up.bias"]))
+    return x + linear(g, W[f"{prefix}.ffn_down.weight"], W[f"{prefix}.ffn_down.bias"])
+
+
+def _f64(W: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    return {k: np.asarray(v, dtype=np.float64) for k, v in W.items()}
+
+
+def encode_tokens(x: np.ndarray, W: Dict[str, np.ndarray], spec: EncoderSpec,
+                  ids: np.ndarray, grid: Tuple[int, int, int],
+                  n_layer: Optional[int] = None) -> np.ndarray:
+    """The encoder's blocks (and final norm when ``spec.final_norm``) on token
+    activations x [N, D] whose grid ids are ``ids`` on ``grid`` = (gt, gh, gw).
+    Positions come from the ids ([Notes §4], [Notes §4.4])."""
+    W = _f64(W)
+    _, gh, gw = grid
+    pos = rope_positions(ids, gh, gw, spec.ref_grid)
+    x = np.asarray(x, dtype=np.float64)
+    L = spec.n_layer if n_layer is None else n_layer
+    for i in range(L):
+        x = block(x, W, f"enc.blk.{i}", spec.n_head, pos, spec.layout, spec.theta, spec.ln_eps)
+    if spec.final_norm:
+        x = layer_norm(x, W["enc.norm.weight"], W["enc.norm.bias"], spec.ln_eps)
+    return x
+
+
+def encoder_forward(clip: np.ndarray, W: Dict[str, np.ndarray], spec: EncoderSpec) -> np.ndarray:
+    """One clip, uint8 [T, H, W, 3] -> token map [N, D] float64.
+
+    tokens = patchify(x) Wpe^T + bpe (+ mod_embed_video for V-JEPA 2.1) ([Notes §3
+    "2.1 encoder forward"], [Notes §2] patch_embed), then the blocks with 3-D RoPE on the
+    clip's own grid, then the final norm ([Notes §3]: out = enc.norm(x)).
+    """
+    X = normalize_frames(clip)
+    p = patchify(X, spec.tubelet, spec.patch)
+    Wd = _f64(W)
+    x = linear(p, Wd["enc.patch_embed.weight"], Wd["enc.patch_embed.bias"])
+    if spec.has_mod_embed:
+        x = x + Wd["enc.mod_embed_video"]
+    T, H, Wd_ = clip.shape[0], clip.shape[1], clip.shape[2]
+    grid = (T // spec.tubelet, H // spec.patch, Wd_ // spec.patch)
+    ids = np.arange(grid[0] * grid[1] * grid[2])
+    return encode_tokens(x, W, spec, ids, grid)
+
+
+def encoder_forward_batch(clips: np.ndarray, W, spec: EncoderSpec) -> np.ndarray:
+    """[B, T, H, W, 3] -> [B, N, D]; each clip is encoded on its own."""
+    return np.stack([encoder_forward(c, W, spec) for c in clips])
+
+
+def predictor_forward(z: np.ndarray, W: Dict[str, np.ndarray], spec: PredictorSpec,
+                      ids_ctx: np.ndarray, ids_tgt: np.ndarray, mask_index: int,
+                      grid: Tuple[int, int, int]) -> np.ndarray:
+    """Masked predictor: encoder token map z [N, D_enc] -> predictions [len(ids_tgt), out].
+
+    ctx = z[ids_ctx] Wemb^T + b; every target row is mask_tokens[mask_index mod n];
+    x = concat(ctx, tgt) with positions decoded from concat(ids_ctx, ids_tgt) on the
+    encoder grid; blocks with 3-D RoPE (tiled, not interpolated); final norm; the output
+    projection on the target rows ([Notes §3 "2.1 predictor forward"] for the order of
+    operations, [Notes §2] for the V-JEPA 2 tensors, [Notes §4.4] for the ids).  Tokens
+    are not sorted by id: attention is permutation-equivariant ([Notes §3]).
+    """
+    W = _f64(W)
+    ids_ctx = np.asarray(ids_ctx, dtype=np.int64)
+    ids_tgt = np.asarray(ids_tgt, dtype=np.int64)
+    ctx = linear(np.asarray(z, dtype=np.float64)[ids_ctx], W["pred.embed.weight"], W["pred.embed.bias"])
+    tok = W["pred.mask_tokens"][mask_index % spec.n_mask_tokens]
+    tgt = np.broadcast_to(tok, (len(ids_tgt), spec.embed_dim))
+    x = np.concatenate([ctx, tgt], axis=0)
+    _, gh, gw = grid
+    pos = rope_positions(np.concatenate([ids_ctx, ids_tgt]), gh, gw, 0)
+    for i in range(spec.n_layer):
+        x = block(x, W, f"pred.blk.{i}", spec.n_head, pos, spec.layout, spec.theta, spec.ln_eps)
+    x = layer_norm(x, W["pred.norm.weight"], W["pred.norm.bias"], spec.ln_eps)
+    return linear(x[len(ids_ctx):], W["pred.proj.weight"], W["pred.proj.bias"])
