@@ -1,0 +1,231 @@
+/*
+ * jepa.h -- C ABI of libjepa, a gfx950 (MI355X) implementation of the V-JEPA 2 / 2.1
+ * video ViT encoder forward and of the V-JEPA 2 masked predictor.
+ *
+ * Sources, cited by page and section:
+ *   [Notes]  "V-JEPA 2 / 2.1 tensor maps and RoPE derivation"
+ *            (aselimc.github.io/jepa.cpp/vjepa-notes/)
+ *   [Parity] "Parity -- image ViT encoders ... and video encoders (V-JEPA 2 / V-JEPA 2.1,
+ *            LeVJEPA)" (aselimc.github.io/jepa.cpp/parity/)
+ *   [HFport] "V-JEPA 2.1 ViT-B/16 384 -- HuggingFace port"
+ *            (aimarketly.com/model/apiantonio/vjepa2.1-vit-base-384)
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named *_dev are device memory (HIP), allocated and owned by the caller;
+ *     the library never frees caller memory.  Pointers named *_host are host memory,
+ *     read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Compute entry points only
+ *     enqueue work on it and return without synchronising; outputs are valid once the
+ *     stream reaches that point.
+ *   - Every call returns a jepa_status.  On an argument, shape or state error nothing is
+ *     enqueued and no output is touched.  JEPA_ERR_HIP reports a HIP runtime error
+ *     (allocation or launch); the state of the outputs is then unspecified.
+ *   - Row-major everywhere.  bf16 data is passed as raw 16-bit patterns (uint16).
+ *   - Token ids index a T-major grid (gt, gh, gw): id = t*gh*gw + h*gw + w ([Notes §4]).
+ *     An ids pointer may be NULL, meaning ids 0..N-1.  Device ids outside [0, gt*gh*gw)
+ *     are clamped to that range by the kernels (memory-safe; the result for such a
+ *     token is unspecified).
+ *   - A handle may be used by one stream at a time.
+ */
+#ifndef JEPA_H
+#define JEPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ enums */
+
+enum jepa_status {
+  JEPA_OK = 0,
+  JEPA_ERR_ARG = -1,    /* null pointer, bad enum, unsupported configuration value */
+  JEPA_ERR_SHAPE = -2,  /* sizes that the method or this library does not accept */
+  JEPA_ERR_STATE = -3,  /* handle not ready (a required tensor was never set) */
+  JEPA_ERR_NAME = -4,   /* unknown tensor name, or a shape that does not match it */
+  JEPA_ERR_OOM = -5,    /* device allocation failed */
+  JEPA_ERR_HIP = -6     /* HIP runtime error (launch, copy) */
+};
+
+/* RoPE frequency layouts ([Notes §4.1] tiled = V-JEPA 2, [Notes §4.2] interleaved =
+ * V-JEPA 2.1). */
+enum jepa_rope_layout { JEPA_ROPE_TILED = 0, JEPA_ROPE_INTERLEAVED = 1 };
+
+/* Element types.  JEPA_F32 also selects the fp32 compute path (plain fp32 FMA
+ * kernels); JEPA_BF16 selects bf16 MFMA operands with fp32 accumulation. */
+enum jepa_dtype { JEPA_F32 = 0, JEPA_BF16 = 1 };
+
+/* Epilogues of jepa_linear. */
+enum jepa_epilogue {
+  JEPA_EPI_STORE = 0,    /* C = A W^T + bias                  (C in out_dtype)        */
+  JEPA_EPI_GELU = 1,     /* C = GELU_erf(A W^T + bias)         (C in out_dtype)        */
+  JEPA_EPI_RESIDUAL = 2  /* C += A W^T + bias, C fp32 in place (out_dtype must be F32) */
+};
+
+/* Library version: major*10000 + minor*100 + patch. */
+int jepa_version(void);
+
+/* Human-readable text of a jepa_status (static storage). */
+const char* jepa_status_str(int status);
+
+/* ------------------------------------------------------------------ encoder */
+
+/* Hyper-parameters of one encoder ([Notes §1] table).  ViT-L: 1024/24/16/4096,
+ * 2.1 ViT-B: 768/12/12/3072; patch 16, tubelet 2, 3 channels, ln_eps 1e-6,
+ * rope_theta 10000.  head_dim = embed_dim / n_head must be 64 or 32. */
+typedef struct jepa_encoder_config {
+  int32_t embed_dim;      /* D, a multiple of 128 on the bf16 path, of 64 on fp32 */
+  int32_t n_layer;        /* >= 0 (0: patch embedding (+ final norm) only)        */
+  int32_t n_head;
+  int32_t ffn_dim;        /* F, a multiple of 128 on the bf16 path                */
+  int32_t patch;          /* must be 16                                          */
+  int32_t tubelet;        /* must be 2                                           */
+  int32_t in_chans;       /* must be 3                                           */
+  int32_t rope_layout;    /* jepa_rope_layout                                    */
+  int32_t rope_ref_grid;  /* 0: integer positions; R > 1: interpolate the spatial
+                             positions onto [0, R-1] ([Notes §4.3], R = 16)      */
+  int32_t has_mod_embed;  /* 1: add enc.mod_embed_video after the patch embedding
+                             ([Notes §3] "2.1 encoder forward")                   */
+  int32_t final_norm;     /* 1: apply enc.norm at the end ([Notes §2], §3)        */
+  int32_t compute;        /* jepa_dtype                                          */
+  int32_t max_rows;       /* largest B*N a call may use (sizes the workspace)    */
+  float ln_eps;           /* 1e-6                                                */
+  float rope_theta;       /* 10000                                               */
+} jepa_encoder_config;
+
+typedef struct jepa_encoder jepa_encoder;
+
+/* Validate the configuration and allocate the handle: device weights (bf16 matrices,
+ * fp32 vectors) and a workspace for max_rows token rows.  Must be called with the
+ * target device current.  Errors: JEPA_ERR_ARG (null, bad value), JEPA_ERR_OOM. */
+int jepa_encoder_create(const jepa_encoder_config* cfg, jepa_encoder** out);
+
+/* Release the handle and everything it allocated.  NULL is ignored.  The caller must
+ * make sure no enqueued work still uses it. */
+void jepa_encoder_free(jepa_encoder* enc);
+
+/* Upload one tensor by its GGUF name ([Notes §2] and [Notes §3] key maps):
+ *   enc.patch_embed.weight [D, 1536] (feature order C, T, H, W), enc.patch_embed.bias [D],
+ *   enc.mod_embed_video [D] (only when has_mod_embed),
+ *   enc.blk.{i}.ln1.weight/bias [D], enc.blk.{i}.attn_qkv.weight [3D, D] (rows q; k; v),
+ *   enc.blk.{i}.attn_qkv.bias [3D], enc.blk.{i}.attn_out.weight [D, D] / .bias [D],
+ *   enc.blk.{i}.ln2.weight/bias [D], enc.blk.{i}.ffn_up.weight [F, D] / .bias [F],
+ *   enc.blk.{i}.ffn_down.weight [D, F] / .bias [D], enc.norm.weight/bias [D].
+ * `host` holds numel(shape) values of src_dtype (JEPA_F32 floats or JEPA_BF16 bit
+ * patterns), row-major.  Matrices are stored on the device in the compute dtype
+ * (fp32 -> bf16 by round-to-nearest-even); vectors stay fp32.  Synchronous.
+ * Errors: JEPA_ERR_ARG, JEPA_ERR_NAME (unknown name or shape mismatch), JEPA_ERR_HIP. */
+int jepa_encoder_set_tensor(jepa_encoder* enc, const char* name, const void* host,
+                            int src_dtype, const int64_t* shape, int ndim);
+
+/* Encode B uint8 clips ([Notes §3] "2.1 encoder forward"; [Notes §5] preprocessing):
+ *   clip_dev: uint8 [B, T, H, W, 3] (frames, channels last, RGB);
+ *   out_dev:  fp32 [B, N, D], N = (T/2)*(H/16)*(W/16), tokens T-major ([Notes §4]).
+ * Pixels are normalised with the ImageNet mean/std in the fused form
+ * (px - 255*mean)/(255*std) ([Parity "Preprocessing parity"]), patchified into
+ * 2x16x16x3 tubelets and embedded; then the blocks and the final norm.
+ * Shape errors (JEPA_ERR_SHAPE): T odd or < 2, H or W not a multiple of 16, B < 1,
+ * B*N > max_rows, interpolation with a grid side of 1 ([Notes §4.3]).
+ * JEPA_ERR_STATE if a required tensor was never set. */
+int jepa_encode(jepa_encoder* enc, const uint8_t* clip_dev, int B, int T, int H, int W,
+                float* out_dev, void* stream);
+
+/* Run the blocks (and the final norm when configured) on token activations:
+ *   x_dev: fp32 [B, N, D] (not modified); ids_dev: int32 [N] grid ids shared by all B
+ *   rows of the batch (NULL = 0..N-1) on the grid (gt, gh, gw); out_dev: fp32 [B, N, D]
+ *   (may alias x_dev).  Positions come from the ids ([Notes §4], [Notes §4.4]). */
+int jepa_encode_tokens(jepa_encoder* enc, const float* x_dev, int B, int N,
+                       const int32_t* ids_dev, int gt, int gh, int gw, float* out_dev,
+                       void* stream);
+
+/* ------------------------------------------------------------------ predictor */
+
+/* V-JEPA 2 masked predictor ([Notes §1]: 384 / 12 / 12 / 1536, 10 mask tokens, output
+ * 1024, tiled RoPE, no interpolation).  head_dim = embed_dim / n_head must be 64 or 32. */
+typedef struct jepa_predictor_config {
+  int32_t enc_dim;        /* encoder width (input rows)   */
+  int32_t embed_dim;      /* predictor width              */
+  int32_t n_layer;
+  int32_t n_head;
+  int32_t ffn_dim;
+  int32_t n_mask_tokens;
+  int32_t out_dim;
+  int32_t rope_layout;
+  int32_t compute;        /* jepa_dtype */
+  int32_t max_rows;       /* largest n_ctx + n_tgt */
+  float ln_eps;
+  float rope_theta;
+} jepa_predictor_config;
+
+typedef struct jepa_predictor jepa_predictor;
+
+int jepa_predictor_create(const jepa_predictor_config* cfg, jepa_predictor** out);
+void jepa_predictor_free(jepa_predictor* pred);
+
+/* Names ([Notes §2]): pred.embed.weight [E, Denc] / .bias [E], pred.mask_tokens [n, E],
+ * pred.blk.{i}.* as the encoder blocks at width E, pred.norm.weight/bias [E],
+ * pred.proj.weight [Dout, E] / .bias [Dout].  Same rules as jepa_encoder_set_tensor. */
+int jepa_predictor_set_tensor(jepa_predictor* pred, const char* name, const void* host,
+                              int src_dtype, const int64_t* shape, int ndim);
+
+/* Predict the target tokens ([Notes §3] "2.1 predictor forward" order of operations,
+ * [Notes §4.4] ids):
+ *   z_dev: fp32 [n_enc, Denc] encoder token map of one clip;
+ *   ids_ctx_dev: int32 [n_ctx] rows of z that form the context (also their grid ids);
+ *   ids_tgt_dev: int32 [n_tgt] grid ids of the targets;
+ *   every target row starts as mask_tokens[mask_index mod n_mask_tokens];
+ *   positions are decoded from concat(ids_ctx, ids_tgt) on (gt, gh, gw);
+ *   out_dev: fp32 [n_tgt, Dout] = projection of the normed target rows.
+ * Errors: JEPA_ERR_SHAPE if n_ctx < 1, n_tgt < 1, n_ctx + n_tgt > max_rows or
+ * gt*gh*gw != n_enc. */
+int jepa_predict(jepa_predictor* pred, const float* z_dev, int n_enc,
+                 const int32_t* ids_ctx_dev, int n_ctx, const int32_t* ids_tgt_dev, int n_tgt,
+                 int mask_index, int gt, int gh, int gw, float* out_dev, void* stream);
+
+/* ------------------------------------------------------------------ stand-alone ops */
+
+/* 3-D RoPE ([Notes §4]; tiled [Notes §4.1], interleaved [Notes §4.2], interpolation
+ * [Notes §4.3]) on head vectors, out of place or in place (y_dev may equal x_dev):
+ *   element (b, n, e, j) of x/y is at [(b*N + n)*row_stride + e*head_dim + j],
+ *   dtype JEPA_F32 or JEPA_BF16, row_stride >= n_head*head_dim (in elements);
+ *   d = 2*((head_dim/3)/2) dims per axis: [0,d) follow t, [d,2d) h, [2d,3d) w, the
+ *   rest pass through; omega_k = theta^(-k/(d/2)); angles are formed in fp64 and
+ *   their cos/sin rounded to fp32.
+ *   ref_grid 0: integer positions; R > 1: h' = h(R-1)/(gh-1), w' = w(R-1)/(gw-1).
+ * head_dim must be even and >= 6. */
+int jepa_rope3d(const void* x_dev, void* y_dev, int dtype, int B, int N, int n_head,
+                int head_dim, int64_t row_stride, const int32_t* ids_dev, int gt, int gh,
+                int gw, int layout, float theta, int ref_grid, void* stream);
+
+/* LayerNorm over rows ([Notes §1] eps; centred variance as the CPU backend of
+ * [Parity "Parity on a GPU"]): x_dev fp32 [M, D]; weight/bias fp32 [D] (device);
+ * out_dev [M, D] in out_dtype (may alias x_dev when out_dtype is F32).
+ * D must be a multiple of 64 and at most 4096. */
+int jepa_layernorm(const float* x_dev, const float* weight_dev, const float* bias_dev,
+                   int M, int D, float eps, void* out_dev, int out_dtype, void* stream);
+
+/* Linear layer C = epilogue(A W^T + bias) ([Notes §2]: weights stored [out, in]):
+ *   A_dev [M, K] and W_dev [N, K] in dtype; bias_dev fp32 [N] or NULL; C_dev [M, N].
+ *   dtype JEPA_BF16: bf16 MFMA, fp32 accumulation; N a multiple of 128, K of 64.
+ *   dtype JEPA_F32: fp32 FMA; N and K multiples of 4. */
+int jepa_linear(const void* A_dev, const void* W_dev, const float* bias_dev, void* C_dev,
+                int M, int N, int K, int dtype, int epilogue, int out_dtype, void* stream);
+
+/* Multi-head softmax attention with the 3-D RoPE applied to q and k as they are loaded
+ * ([Notes §4]: RoPE on q and k, not v, before the 1/sqrt(head_dim) scaling; softmax
+ * over every key, no mask):
+ *   qkv_dev [B*N, 3*n_head*head_dim] in dtype: per row q | k | v, head e at columns
+ *   e*head_dim of each third ([Notes §2]: fused rows [q; k; v]);
+ *   out_dev [B*N, n_head*head_dim] in dtype, heads concatenated;
+ *   ids/grid/layout/theta/ref_grid as jepa_rope3d.  head_dim must be 64 or 32. */
+int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
+                   int head_dim, const int32_t* ids_dev, int gt, int gh, int gw, int layout,
+                   float theta, int ref_grid, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JEPA_H */

@@ -251,20 +251,26 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_head: int,
 
 
 def block(x: np.ndarray, W: Dict[str, np.ndarray], prefix: str, n_head: int, pos: np.ndarray,
-          layout: str, theta: float = 10000.0, eps: float = 1e-6) -> np.ndarray:
+          layout: str, theta: float = 10000.0, eps: float = 1e-6,
+          rows: Optional[np.ndarray] = None) -> np.ndarray:
     """One pre-norm transformer block ([Notes §2]: norm1 / fused q,k,v / proj / norm2 /
     fc1 / fc2; the residual form x += attn(ln1(x)); x += mlp(ln2(x)) is written out for
-    the attentive-pool blocks; [Notes §1]: no layer-scale, no CLS, no registers)."""
+    the attentive-pool blocks; [Notes §1]: no layer-scale, no CLS, no registers).
+
+    ``rows`` (default: all) selects the output rows.  Keys and values always come from
+    every row; everything after the attention is row-wise, so the selected rows equal
+    the same rows of the full result."""
     D = x.shape[1]
     h = layer_norm(x, W[f"{prefix}.ln1.weight"], W[f"{prefix}.ln1.bias"], eps)
     qkv = linear(h, W[f"{prefix}.attn_qkv.weight"], W[f"{prefix}.attn_qkv.bias"])
     # fused rows are [q; k; v] ([Notes §2], attn_qkv)
     q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
-    o = attention(q, k, v, n_head, pos, pos, layout, theta)
-    x = x + linear(o, W[f"{prefix}.attn_out.weight"], W[f"{prefix}.attn_out.bias"])
-    h2 = layer_norm(x, W[f"{prefix}.ln2.weight"], W[f"{prefix}.ln2.bias"], eps)
+    o = attention(q, k, v, n_head, pos, pos, layout, theta, rows=rows)
+    xr = x if rows is None else x[rows]
+    xr = xr + linear(o, W[f"{prefix}.attn_out.weight"], W[f"{prefix}.attn_out.bias"])
+    h2 = layer_norm(xr, W[f"{prefix}.ln2.weight"], W[f"{prefix}.ln2.bias"], eps)
     g = gelu_erf(linear(h2, W[f"{prefix}.ffn_up.weight"], W[f"{prefix}.ffn_up.bias"]))
-    return x + linear(g, W[f"{prefix}.ffn_down.weight"], W[f"{prefix}.ffn_down.bias"])
+    return xr + linear(g, W[f"{prefix}.ffn_down.weight"], W[f"{prefix}.ffn_down.bias"])
 
 
 def _f64(W: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
@@ -273,28 +279,36 @@ def _f64(W: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
 
 def encode_tokens(x: np.ndarray, W: Dict[str, np.ndarray], spec: EncoderSpec,
                   ids: np.ndarray, grid: Tuple[int, int, int],
-                  n_layer: Optional[int] = None) -> np.ndarray:
+                  n_layer: Optional[int] = None,
+                  last_rows: Optional[np.ndarray] = None) -> np.ndarray:
     """The encoder's blocks (and final norm when ``spec.final_norm``) on token
     activations x [N, D] whose grid ids are ``ids`` on ``grid`` = (gt, gh, gw).
-    Positions come from the ids ([Notes §4], [Notes §4.4])."""
+    Positions come from the ids ([Notes §4], [Notes §4.4]).  ``last_rows`` restricts
+    the last block (and the norm) to those output rows; earlier blocks run in full."""
     W = _f64(W)
     _, gh, gw = grid
     pos = rope_positions(ids, gh, gw, spec.ref_grid)
     x = np.asarray(x, dtype=np.float64)
     L = spec.n_layer if n_layer is None else n_layer
     for i in range(L):
-        x = block(x, W, f"enc.blk.{i}", spec.n_head, pos, spec.layout, spec.theta, spec.ln_eps)
+        rows = last_rows if i == L - 1 else None
+        x = block(x, W, f"enc.blk.{i}", spec.n_head, pos, spec.layout, spec.theta, spec.ln_eps,
+                  rows=rows)
+    if L == 0 and last_rows is not None:
+        x = x[last_rows]
     if spec.final_norm:
         x = layer_norm(x, W["enc.norm.weight"], W["enc.norm.bias"], spec.ln_eps)
     return x
 
 
-def encoder_forward(clip: np.ndarray, W: Dict[str, np.ndarray], spec: EncoderSpec) -> np.ndarray:
+def encoder_forward(clip: np.ndarray, W: Dict[str, np.ndarray], spec: EncoderSpec,
+                    last_rows: Optional[np.ndarray] = None) -> np.ndarray:
     """One clip, uint8 [T, H, W, 3] -> token map [N, D] float64.
 
     tokens = patchify(x) Wpe^T + bpe (+ mod_embed_video for V-JEPA 2.1) ([Notes §3
     "2.1 encoder forward"], [Notes §2] patch_embed), then the blocks with 3-D RoPE on the
-    clip's own grid, then the final norm ([Notes §3]: out = enc.norm(x)).
+    clip's own grid, then the final norm ([Notes §3]: out = enc.norm(x)).  ``last_rows``
+    as in ``encode_tokens``.
     """
     X = normalize_frames(clip)
     p = patchify(X, spec.tubelet, spec.patch)
@@ -305,7 +319,7 @@ def encoder_forward(clip: np.ndarray, W: Dict[str, np.ndarray], spec: EncoderSpe
     T, H, Wd_ = clip.shape[0], clip.shape[1], clip.shape[2]
     grid = (T // spec.tubelet, H // spec.patch, Wd_ // spec.patch)
     ids = np.arange(grid[0] * grid[1] * grid[2])
-    return encode_tokens(x, W, spec, ids, grid)
+    return encode_tokens(x, W, spec, ids, grid, last_rows=last_rows)
 
 
 def encoder_forward_batch(clips: np.ndarray, W, spec: EncoderSpec) -> np.ndarray:
@@ -315,7 +329,8 @@ def encoder_forward_batch(clips: np.ndarray, W, spec: EncoderSpec) -> np.ndarray
 
 def predictor_forward(z: np.ndarray, W: Dict[str, np.ndarray], spec: PredictorSpec,
                       ids_ctx: np.ndarray, ids_tgt: np.ndarray, mask_index: int,
-                      grid: Tuple[int, int, int]) -> np.ndarray:
+                      grid: Tuple[int, int, int],
+                      last_rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Masked predictor: encoder token map z [N, D_enc] -> predictions [len(ids_tgt), out].
 
     ctx = z[ids_ctx] Wemb^T + b; every target row is mask_tokens[mask_index mod n];
@@ -324,6 +339,8 @@ def predictor_forward(z: np.ndarray, W: Dict[str, np.ndarray], spec: PredictorSp
     projection on the target rows ([Notes §3 "2.1 predictor forward"] for the order of
     operations, [Notes §2] for the V-JEPA 2 tensors, [Notes §4.4] for the ids).  Tokens
     are not sorted by id: attention is permutation-equivariant ([Notes §3]).
+    ``last_rows`` (indices into the targets) restricts the last block, the norm and the
+    projection to those target rows.
     """
     W = _f64(W)
     ids_ctx = np.asarray(ids_ctx, dtype=np.int64)
@@ -334,7 +351,14 @@ def predictor_forward(z: np.ndarray, W: Dict[str, np.ndarray], spec: PredictorSp
     x = np.concatenate([ctx, tgt], axis=0)
     _, gh, gw = grid
     pos = rope_positions(np.concatenate([ids_ctx, ids_tgt]), gh, gw, 0)
-    for i in range(spec.n_layer):
-        x = block(x, W, f"pred.blk.{i}", spec.n_head, pos, spec.layout, spec.theta, spec.ln_eps)
+    n_ctx = len(ids_ctx)
+    tgt_rows = n_ctx + (np.arange(len(ids_tgt)) if last_rows is None else np.asarray(last_rows))
+    L = spec.n_layer
+    for i in range(L):
+        rows = tgt_rows if (i == L - 1 and last_rows is not None) else None
+        x = block(x, W, f"pred.blk.{i}", spec.n_head, pos, spec.layout, spec.theta, spec.ln_eps,
+                  rows=rows)
+    if not (L > 0 and last_rows is not None):
+        x = x[tgt_rows]
     x = layer_norm(x, W["pred.norm.weight"], W["pred.norm.bias"], spec.ln_eps)
-    return linear(x[len(ids_ctx):], W["pred.proj.weight"], W["pred.proj.bias"])
+    return linear(x, W["pred.proj.weight"], W["pred.proj.bias"])

@@ -1,0 +1,98 @@
+"""The C-ABI library loads and exports every function include/jepa.h declares; argument
+checks that return before any device work behave as documented.  CPU only: no call here
+reaches the GPU (each returns from its host-side validation first)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import video_vit_encoder_amd as J
+from video_vit_encoder_amd import _lib
+
+
+def test_library_exports_every_header_function():
+    lib = J.load()
+    names = J.header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert J.jepa_version() == 100
+    for st in range(0, -7, -1):
+        assert J.jepa_status_str(st) != "unknown status"
+    assert J.jepa_status_str(42) == "unknown status"
+
+
+def _enc_cfg(**kw):
+    c = dict(embed_dim=1024, n_layer=24, n_head=16, ffn_dim=4096, patch=16, tubelet=2,
+             in_chans=3, rope_layout=0, rope_ref_grid=0, has_mod_embed=0, final_norm=1,
+             compute=1, max_rows=8192, ln_eps=1e-6, rope_theta=10000.0)
+    c.update(kw)
+    return _lib.jepa_encoder_config(**c)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_head=0), dict(embed_dim=1000), dict(n_head=8),          # head dim 128
+    dict(n_head=32, embed_dim=1024, ffn_dim=4000),                 # F not a multiple of 128
+    dict(patch=14), dict(tubelet=1), dict(in_chans=1), dict(rope_layout=2),
+    dict(rope_ref_grid=1), dict(rope_ref_grid=-3), dict(max_rows=0), dict(compute=5),
+    dict(ln_eps=0.0), dict(rope_theta=1.0), dict(n_layer=-1),
+])
+def test_encoder_create_rejects_bad_config(bad):
+    lib = J.load()
+    h = ctypes.c_void_p()
+    cfg = _enc_cfg(**bad)
+    assert lib.jepa_encoder_create(ctypes.byref(cfg), ctypes.byref(h)) == _lib.JEPA_ERR_ARG
+    assert h.value is None
+
+
+def test_null_arguments_are_rejected():
+    lib = J.load()
+    assert lib.jepa_encoder_create(None, None) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_encode(None, None, 1, 2, 16, 16, None, None) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_encode_tokens(None, None, 1, 1, None, 1, 1, 1, None, None) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_predict(None, None, 1, None, 1, None, 1, 0, 1, 1, 1, None, None) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_encoder_set_tensor(None, b"x", None, 0, None, 0) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_predictor_set_tensor(None, b"x", None, 0, None, 0) == _lib.JEPA_ERR_ARG
+    lib.jepa_encoder_free(None)
+    lib.jepa_predictor_free(None)
+
+
+def test_standalone_ops_validate_before_launch():
+    lib = J.load()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+    # rope3d: odd head dim, stride below the row, bad layout, grid side 1 with interpolation
+    assert lib.jepa_rope3d(fake, fake, 0, 1, 4, 1, 63, 63, None, 1, 2, 2, 0, 1e4, 0, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_rope3d(fake, fake, 0, 1, 4, 2, 64, 64, None, 1, 2, 2, 0, 1e4, 0, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_rope3d(fake, fake, 0, 1, 4, 1, 64, 64, None, 1, 2, 2, 7, 1e4, 0, None) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_rope3d(fake, fake, 0, 1, 4, 1, 64, 64, None, 4, 1, 1, 0, 1e4, 16, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_rope3d(fake, fake, 0, 1, 5, 1, 64, 64, None, 1, 2, 2, 0, 1e4, 0, None) == _lib.JEPA_ERR_SHAPE
+    # empty inputs are no-ops that touch nothing
+    assert lib.jepa_rope3d(fake, fake, 0, 0, 4, 1, 64, 64, None, 1, 2, 2, 0, 1e4, 0, None) == _lib.JEPA_OK
+    assert lib.jepa_layernorm(fake, fake, fake, 0, 1024, 1e-6, fake, 0, None) == _lib.JEPA_OK
+    assert lib.jepa_linear(fake, fake, None, fake, 0, 128, 64, 1, 0, 1, None) == _lib.JEPA_OK
+    # layernorm: width not a multiple of 64 / above 4096 / not instantiated
+    assert lib.jepa_layernorm(fake, fake, fake, 4, 100, 1e-6, fake, 0, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_layernorm(fake, fake, fake, 4, 8192, 1e-6, fake, 0, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_layernorm(fake, fake, fake, 4, 64 * 7, 1e-6, fake, 0, None) == _lib.JEPA_ERR_SHAPE
+    # linear: bf16 tiles need N % 128 and K % 64; residual needs fp32 output
+    assert lib.jepa_linear(fake, fake, None, fake, 4, 100, 64, 1, 0, 1, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_linear(fake, fake, None, fake, 4, 128, 60, 1, 0, 1, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_linear(fake, fake, None, fake, 4, 128, 64, 1, 2, 1, None) == _lib.JEPA_ERR_ARG
+    # attention: head dim 48, grid side above the table limit
+    assert lib.jepa_attention(fake, fake, 1, 1, 8, 1, 48, None, 1, 2, 4, 0, 1e4, 0, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_attention(fake, fake, 1, 1, 65, 1, 64, None, 65, 1, 1, 0, 1e4, 0, None) == _lib.JEPA_ERR_SHAPE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libjepa.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -157,3 +157,27 @@ def test_vitl_tensor_and_parameter_counts():
     params = sum(int(np.prod(s)) for _, s, _ in enc + pred)
     assert round(params / 1e6) == g["params_millions_rounded"]
     assert params == 325_971_328
+
+
+@pytest.mark.parametrize("layout,ref_grid", [("tiled", 0), ("interleaved", 16)])
+def test_last_rows_restriction_equals_full_rows(layout, ref_grid):
+    # the sampled-row evaluation used by the full-size parity tests returns exactly the
+    # selected rows of the full forward (brute force anchors the full forward above)
+    clip = synth.clip_u8(4, 1, 4, 32, 48)[0]
+    W = tiny_weights(ref_grid > 0)
+    spec = tiny_spec(layout, ref_grid, ref_grid > 0)
+    full = oracle.encoder_forward(clip, W, spec)
+    rows = np.array([11, 0, 5, 7])
+    part = oracle.encoder_forward(clip, W, spec, last_rows=rows)
+    np.testing.assert_allclose(part, full[rows], rtol=1e-13, atol=1e-13)
+
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((18, 32))
+    ps = oracle.PredictorSpec(32, 16, 2, 1, 24, 3, 20)
+    Wp = synth.predictor_weights(synth.PredictorShape(32, 16, 2, 1, 24, 3, 20), seed=2,
+                                 dtype="f32", ln="random")
+    ids_ctx, ids_tgt = np.array([0, 4, 5, 9]), np.array([1, 2, 17, 8, 3])
+    fullp = oracle.predictor_forward(z, Wp, ps, ids_ctx, ids_tgt, 1, (2, 3, 3))
+    r = np.array([4, 1])
+    partp = oracle.predictor_forward(z, Wp, ps, ids_ctx, ids_tgt, 1, (2, 3, 3), last_rows=r)
+    np.testing.assert_allclose(partp, fullp[r], rtol=1e-13, atol=1e-13)

@@ -1,0 +1,112 @@
+"""video_vit_encoder_amd: the V-JEPA 2 / 2.1 video ViT encoder forward (and the V-JEPA 2
+masked predictor) as hand-written gfx950 HIP kernels behind the C ABI of include/jepa.h.
+
+The functions named ``jepa_*`` are the C entry points (see ``_lib``).  ``Encoder`` and
+``Predictor`` are small owners of a C handle: they upload a dict of host weights by name
+and call ``jepa_encode`` / ``jepa_encode_tokens`` / ``jepa_predict``.  Nothing here
+computes any part of the forward.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from ._lib import (  # noqa: F401
+    DTYPES, JEPA_BF16, JEPA_EPI_GELU, JEPA_EPI_RESIDUAL, JEPA_EPI_STORE, JEPA_F32, LAYOUTS,
+    JepaError, header_functions, jepa_attention, jepa_encode, jepa_encode_tokens,
+    jepa_encoder_config, jepa_encoder_create, jepa_encoder_free, jepa_encoder_set_tensor,
+    jepa_layernorm, jepa_linear, jepa_predict, jepa_predictor_config, jepa_predictor_create,
+    jepa_predictor_free, jepa_predictor_set_tensor, jepa_rope3d, jepa_status_str, jepa_version,
+    load,
+)
+
+
+class Encoder:
+    """Owner of a jepa_encoder handle."""
+
+    def __init__(self, embed_dim: int, n_layer: int, n_head: int, ffn_dim: int, *,
+                 layout: str = "tiled", ref_grid: int = 0, has_mod_embed: bool = False,
+                 final_norm: bool = True, dtype: str = "bf16", max_rows: int = 2048,
+                 ln_eps: float = 1e-6, theta: float = 10000.0):
+        cfg = jepa_encoder_config(
+            embed_dim=embed_dim, n_layer=n_layer, n_head=n_head, ffn_dim=ffn_dim, patch=16,
+            tubelet=2, in_chans=3, rope_layout=LAYOUTS[layout], rope_ref_grid=ref_grid,
+            has_mod_embed=int(has_mod_embed), final_norm=int(final_norm),
+            compute=DTYPES[dtype], max_rows=max_rows, ln_eps=ln_eps, rope_theta=theta)
+        self.cfg = cfg
+        self.embed_dim = embed_dim
+        self.handle = jepa_encoder_create(cfg)
+
+    def set_weights(self, weights: Dict[str, np.ndarray]) -> None:
+        for name, arr in weights.items():
+            jepa_encoder_set_tensor(self.handle, name, arr)
+
+    def encode(self, clip, out=None, stream=None):
+        """clip: uint8 device tensor [B, T, H, W, 3] -> fp32 [B, N, D]."""
+        import torch
+        B, T, H, W, _ = clip.shape
+        N = (T // 2) * (H // 16) * (W // 16)
+        if out is None:
+            out = torch.empty((B, N, self.embed_dim), dtype=torch.float32, device=clip.device)
+        jepa_encode(self.handle, clip, out, stream)
+        return out
+
+    def encode_tokens(self, x, grid: Sequence[int], ids=None, out=None, stream=None):
+        """x: fp32 device tensor [B, N, D] -> fp32 [B, N, D]."""
+        import torch
+        if out is None:
+            out = torch.empty_like(x)
+        jepa_encode_tokens(self.handle, x, ids, grid, out, stream)
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            jepa_encoder_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Predictor:
+    """Owner of a jepa_predictor handle."""
+
+    def __init__(self, enc_dim: int, embed_dim: int, n_layer: int, n_head: int, ffn_dim: int,
+                 n_mask_tokens: int, out_dim: int, *, layout: str = "tiled", dtype: str = "bf16",
+                 max_rows: int = 8192, ln_eps: float = 1e-6, theta: float = 10000.0):
+        cfg = jepa_predictor_config(
+            enc_dim=enc_dim, embed_dim=embed_dim, n_layer=n_layer, n_head=n_head,
+            ffn_dim=ffn_dim, n_mask_tokens=n_mask_tokens, out_dim=out_dim,
+            rope_layout=LAYOUTS[layout], compute=DTYPES[dtype], max_rows=max_rows,
+            ln_eps=ln_eps, rope_theta=theta)
+        self.cfg = cfg
+        self.out_dim = out_dim
+        self.handle = jepa_predictor_create(cfg)
+
+    def set_weights(self, weights: Dict[str, np.ndarray]) -> None:
+        for name, arr in weights.items():
+            jepa_predictor_set_tensor(self.handle, name, arr)
+
+    def predict(self, z, ids_ctx, ids_tgt, mask_index: int, grid: Sequence[int], out=None,
+                stream=None):
+        import torch
+        if out is None:
+            out = torch.empty((ids_tgt.numel(), self.out_dim), dtype=torch.float32,
+                              device=z.device)
+        jepa_predict(self.handle, z, ids_ctx, ids_tgt, mask_index, grid, out, stream)
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            jepa_predictor_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

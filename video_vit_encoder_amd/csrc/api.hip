@@ -1,0 +1,630 @@
+// C ABI of libjepa: handles, argument checks, weight upload and the kernel sequence of
+// the encoder and predictor forwards.  Declarations and conventions: include/jepa.h.
+//
+// Encoder forward ([Notes §3] "2.1 encoder forward"; block form [Notes §2]):
+//   x = patchify(normalise(clip)) Wpe^T + bpe (+ mod_embed_video)
+//   per block: x += attn(LN1(x)) Wout^T + bout ; x += GELU(LN2(x) Wup^T + bup) Wdown^T + bdown
+//   out = LN_final(x)
+// The residual stream x is fp32 and lives in the caller's output buffer; LayerNorm
+// outputs, q|k|v, the attention output and the FFN hidden activations are in the
+// compute dtype (bf16 on the MFMA path).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/jepa.h"
+#include "kernels.h"
+
+using namespace jepa;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+// ------------------------------------------------------------------ helpers
+
+uint16_t host_f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u) {  // inf / nan: keep, quiet the nan
+    uint16_t h = static_cast<uint16_t>(u >> 16);
+    if (u & 0x007FFFFFu) h |= 0x40;
+    return h;
+  }
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+float host_bf16_to_f32(uint16_t h) {
+  const uint32_t u = static_cast<uint32_t>(h) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+struct DevBuf {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+int dev_alloc(DevBuf& b, size_t bytes) {
+  if (b.p) return JEPA_OK;
+  if (bytes == 0) bytes = 16;
+  if (hipMalloc(&b.p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    b.p = nullptr;
+    return JEPA_ERR_OOM;
+  }
+  b.bytes = bytes;
+  return JEPA_OK;
+}
+
+void dev_free(DevBuf& b) {
+  if (b.p) (void)hipFree(b.p);
+  b.p = nullptr;
+  b.bytes = 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? JEPA_OK : JEPA_ERR_HIP; }
+
+#define JEPA_TRY(expr)                 \
+  do {                                 \
+    const int _st = (expr);            \
+    if (_st != JEPA_OK) return _st;    \
+  } while (0)
+
+#define JEPA_HIP(expr)                               \
+  do {                                               \
+    if ((expr) != hipSuccess) {                      \
+      (void)hipGetLastError();                       \
+      return JEPA_ERR_HIP;                           \
+    }                                                \
+  } while (0)
+
+// One weight tensor: expected shape, kind and device copy.
+struct Tensor {
+  std::string name;
+  std::vector<int64_t> shape;
+  bool matrix = false;   // stored in the compute dtype; vectors stay fp32
+  bool set = false;
+  bool required = true;
+  DevBuf dev;
+  std::vector<float> host;  // kept for vectors that are combined on the host
+  bool keep_host = false;
+
+  int64_t numel() const {
+    int64_t n = 1;
+    for (int64_t s : shape) n *= s;
+    return n;
+  }
+};
+
+struct TensorSet {
+  std::vector<Tensor> t;
+  int compute = JEPA_BF16;
+
+  int add(const std::string& name, std::vector<int64_t> shape, bool matrix, bool keep_host = false) {
+    Tensor x;
+    x.name = name;
+    x.shape = std::move(shape);
+    x.matrix = matrix;
+    x.keep_host = keep_host;
+    t.push_back(std::move(x));
+    return static_cast<int>(t.size()) - 1;
+  }
+
+  ~TensorSet() {
+    for (Tensor& x : t) dev_free(x.dev);
+  }
+
+  int find(const char* name) const {
+    for (size_t i = 0; i < t.size(); ++i)
+      if (t[i].name == name) return static_cast<int>(i);
+    return -1;
+  }
+
+  bool all_set() const {
+    for (const Tensor& x : t)
+      if (x.required && !x.set) return false;
+    return true;
+  }
+
+  // Upload `host` (numel values of src_dtype) into tensor i.
+  int upload(int i, const void* host, int src_dtype) {
+    Tensor& x = t[i];
+    const int64_t n = x.numel();
+    std::vector<float> f(static_cast<size_t>(n));
+    if (src_dtype == JEPA_F32) {
+      std::memcpy(f.data(), host, static_cast<size_t>(n) * 4);
+    } else {
+      const uint16_t* h = static_cast<const uint16_t*>(host);
+      for (int64_t k = 0; k < n; ++k) f[k] = host_bf16_to_f32(h[k]);
+    }
+    const bool as_bf16 = x.matrix && compute == JEPA_BF16;
+    const size_t bytes = static_cast<size_t>(n) * (as_bf16 ? 2 : 4);
+    JEPA_TRY(dev_alloc(x.dev, bytes));
+    if (as_bf16) {
+      std::vector<uint16_t> h(static_cast<size_t>(n));
+      if (src_dtype == JEPA_BF16)
+        std::memcpy(h.data(), host, static_cast<size_t>(n) * 2);
+      else
+        for (int64_t k = 0; k < n; ++k) h[k] = host_f32_to_bf16(f[k]);
+      JEPA_HIP(hipMemcpy(x.dev.p, h.data(), bytes, hipMemcpyHostToDevice));
+    } else {
+      JEPA_HIP(hipMemcpy(x.dev.p, f.data(), bytes, hipMemcpyHostToDevice));
+    }
+    if (x.keep_host) x.host = std::move(f);
+    x.set = true;
+    return JEPA_OK;
+  }
+
+  int set_tensor(const char* name, const void* host, int src_dtype, const int64_t* shape,
+                 int ndim) {
+    if (!name || !host || !shape) return JEPA_ERR_ARG;
+    if (src_dtype != JEPA_F32 && src_dtype != JEPA_BF16) return JEPA_ERR_ARG;
+    const int i = find(name);
+    if (i < 0) return JEPA_ERR_NAME;
+    const Tensor& x = t[i];
+    if (ndim != static_cast<int>(x.shape.size())) return JEPA_ERR_NAME;
+    for (int k = 0; k < ndim; ++k)
+      if (shape[k] != x.shape[k]) return JEPA_ERR_NAME;
+    return upload(i, host, src_dtype);
+  }
+
+  const void* dev(int i) const { return t[i].dev.p; }
+  const float* devf(int i) const { return static_cast<const float*>(t[i].dev.p); }
+};
+
+// Per-block tensor indices.
+struct BlockIdx {
+  int ln1w, ln1b, qkvw, qkvb, outw, outb, ln2w, ln2b, upw, upb, downw, downb;
+};
+
+BlockIdx add_block(TensorSet& ts, const std::string& p, int64_t d, int64_t f) {
+  BlockIdx b;
+  b.ln1w = ts.add(p + ".ln1.weight", {d}, false);
+  b.ln1b = ts.add(p + ".ln1.bias", {d}, false);
+  b.qkvw = ts.add(p + ".attn_qkv.weight", {3 * d, d}, true);
+  b.qkvb = ts.add(p + ".attn_qkv.bias", {3 * d}, false);
+  b.outw = ts.add(p + ".attn_out.weight", {d, d}, true);
+  b.outb = ts.add(p + ".attn_out.bias", {d}, false);
+  b.ln2w = ts.add(p + ".ln2.weight", {d}, false);
+  b.ln2b = ts.add(p + ".ln2.bias", {d}, false);
+  b.upw = ts.add(p + ".ffn_up.weight", {f, d}, true);
+  b.upb = ts.add(p + ".ffn_up.bias", {f}, false);
+  b.downw = ts.add(p + ".ffn_down.weight", {d, f}, true);
+  b.downb = ts.add(p + ".ffn_down.bias", {d}, false);
+  return b;
+}
+
+// Shape limits of the kernels, for a model width / FFN width / head dim.
+int check_widths(int compute, int D, int F, int n_head, int head_dim) {
+  if (compute != JEPA_F32 && compute != JEPA_BF16) return JEPA_ERR_ARG;
+  if (D <= 0 || F <= 0 || n_head <= 0) return JEPA_ERR_ARG;
+  if (head_dim * n_head != D) return JEPA_ERR_ARG;
+  if (head_dim != 64 && head_dim != 32) return JEPA_ERR_ARG;
+  if (D % 64 != 0 || D > 4096) return JEPA_ERR_ARG;  // LayerNorm kernel
+  if (compute == JEPA_BF16 && (D % 128 != 0 || F % 128 != 0)) return JEPA_ERR_ARG;  // GEMM tiles
+  if (compute == JEPA_F32 && (F % 4 != 0)) return JEPA_ERR_ARG;
+  return JEPA_OK;
+}
+
+int check_grid(int gt, int gh, int gw, int ref_grid) {
+  if (gt < 1 || gh < 1 || gw < 1) return JEPA_ERR_SHAPE;
+  if (gt > kMaxGridSide || gh > kMaxGridSide || gw > kMaxGridSide) return JEPA_ERR_SHAPE;
+  if (ref_grid < 0 || ref_grid == 1) return JEPA_ERR_ARG;
+  // [Notes §4.3]: the interpolation divides by (side - 1)
+  if (ref_grid > 1 && (gh < 2 || gw < 2)) return JEPA_ERR_SHAPE;
+  return JEPA_OK;
+}
+
+// Workspace of the block sequence for `rows` token rows.
+struct Workspace {
+  DevBuf h, qkv, o, g, a;
+  int rows = 0;
+  ~Workspace() {
+    dev_free(h);
+    dev_free(qkv);
+    dev_free(o);
+    dev_free(g);
+    dev_free(a);
+  }
+  int alloc(int max_rows, int D, int F, int a_cols, int compute) {
+    rows = max_rows;
+    const size_t es = compute == JEPA_BF16 ? 2 : 4;
+    const size_t m = static_cast<size_t>(max_rows);
+    JEPA_TRY(dev_alloc(h, m * D * es));
+    JEPA_TRY(dev_alloc(qkv, m * 3 * D * es));
+    JEPA_TRY(dev_alloc(o, m * D * es));
+    JEPA_TRY(dev_alloc(g, m * F * es));
+    if (a_cols > 0) JEPA_TRY(dev_alloc(a, m * a_cols * es));
+    return JEPA_OK;
+  }
+};
+
+// GEMM in the compute dtype.  out_f32 selects fp32 output for the STORE/GELU epilogues.
+hipError_t linear(int compute, const void* A, const void* W, const float* bias, void* C, int M,
+                  int N, int K, int epi, int out_f32, hipStream_t s) {
+  if (compute == JEPA_BF16)
+    return launch_gemm_bf16(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), bias,
+                            C, M, N, K, epi, out_f32, s);
+  return launch_gemm_f32(static_cast<const float*>(A), static_cast<const float*>(W), bias,
+                         static_cast<float*>(C), M, N, K, epi, s);
+}
+
+// The pre-norm blocks over x (fp32 [B*N, D], in place).
+int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_run, Workspace& ws,
+               float* x, int B, int N, int D, int F, int n_head, float eps, const int32_t* ids,
+               const RopeSpec& rs, hipStream_t s) {
+  const int compute = ts.compute;
+  const int bf = compute == JEPA_BF16 ? 1 : 0;
+  const int M = B * N;
+  const int hd = D / n_head;
+  for (int l = 0; l < n_run; ++l) {
+    const BlockIdx& b = blocks[l];
+    JEPA_HIP(launch_layernorm(x, ts.devf(b.ln1w), ts.devf(b.ln1b), M, D, eps, ws.h.p, bf, s));
+    JEPA_HIP(linear(compute, ws.h.p, ts.dev(b.qkvw), ts.devf(b.qkvb), ws.qkv.p, M, 3 * D, D,
+                    JEPA_EPI_STORE, !bf, s));
+    if (bf)
+      JEPA_HIP(launch_attention_bf16(static_cast<const uint16_t*>(ws.qkv.p),
+                                     static_cast<uint16_t*>(ws.o.p), B, N, n_head, hd, ids, rs, s));
+    else
+      JEPA_HIP(launch_attention_f32(static_cast<const float*>(ws.qkv.p),
+                                    static_cast<float*>(ws.o.p), B, N, n_head, hd, ids, rs, s));
+    JEPA_HIP(linear(compute, ws.o.p, ts.dev(b.outw), ts.devf(b.outb), x, M, D, D,
+                    JEPA_EPI_RESIDUAL, 1, s));
+    JEPA_HIP(launch_layernorm(x, ts.devf(b.ln2w), ts.devf(b.ln2b), M, D, eps, ws.h.p, bf, s));
+    JEPA_HIP(linear(compute, ws.h.p, ts.dev(b.upw), ts.devf(b.upb), ws.g.p, M, F, D,
+                    JEPA_EPI_GELU, !bf, s));
+    JEPA_HIP(linear(compute, ws.g.p, ts.dev(b.downw), ts.devf(b.downb), x, M, D, F,
+                    JEPA_EPI_RESIDUAL, 1, s));
+  }
+  return JEPA_OK;
+}
+
+}  // namespace
+
+// ==================================================================== encoder
+
+struct jepa_encoder {
+  jepa_encoder_config cfg;
+  TensorSet ts;
+  std::vector<BlockIdx> blocks;
+  int pe_w = -1, pe_b = -1, mod = -1, norm_w = -1, norm_b = -1;
+  DevBuf pe_bias_eff;  // bpe + mod_embed_video (when has_mod_embed), fp32 [D]
+  bool pe_bias_dirty = true;
+  Workspace ws;
+};
+
+extern "C" {
+
+int jepa_version(void) { return kVersion; }
+
+const char* jepa_status_str(int status) {
+  switch (status) {
+    case JEPA_OK: return "ok";
+    case JEPA_ERR_ARG: return "invalid argument";
+    case JEPA_ERR_SHAPE: return "unsupported shape";
+    case JEPA_ERR_STATE: return "handle not ready (a required tensor was never set)";
+    case JEPA_ERR_NAME: return "unknown tensor name or shape mismatch";
+    case JEPA_ERR_OOM: return "device allocation failed";
+    case JEPA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int jepa_encoder_create(const jepa_encoder_config* cfg, jepa_encoder** out) {
+  if (!cfg || !out) return JEPA_ERR_ARG;
+  *out = nullptr;
+  const jepa_encoder_config& c = *cfg;
+  if (c.n_head <= 0 || c.embed_dim <= 0) return JEPA_ERR_ARG;
+  const int hd = c.embed_dim / c.n_head;
+  JEPA_TRY(check_widths(c.compute, c.embed_dim, c.ffn_dim, c.n_head, hd));
+  if (c.n_layer < 0 || c.patch != 16 || c.tubelet != 2 || c.in_chans != 3) return JEPA_ERR_ARG;
+  if (c.rope_layout != JEPA_ROPE_TILED && c.rope_layout != JEPA_ROPE_INTERLEAVED) return JEPA_ERR_ARG;
+  if (c.rope_ref_grid < 0 || c.rope_ref_grid == 1) return JEPA_ERR_ARG;
+  if (c.max_rows <= 0) return JEPA_ERR_ARG;
+  if (!(c.ln_eps > 0.f) || !(c.rope_theta > 1.f)) return JEPA_ERR_ARG;
+
+  jepa_encoder* e = new (std::nothrow) jepa_encoder();
+  if (!e) return JEPA_ERR_OOM;
+  e->cfg = c;
+  e->ts.compute = c.compute;
+  const int64_t D = c.embed_dim, F = c.ffn_dim;
+  const int64_t feat = static_cast<int64_t>(c.in_chans) * c.tubelet * c.patch * c.patch;
+  e->pe_w = e->ts.add("enc.patch_embed.weight", {D, feat}, true);
+  e->pe_b = e->ts.add("enc.patch_embed.bias", {D}, false, true);
+  if (c.has_mod_embed) e->mod = e->ts.add("enc.mod_embed_video", {D}, false, true);
+  for (int i = 0; i < c.n_layer; ++i)
+    e->blocks.push_back(add_block(e->ts, "enc.blk." + std::to_string(i), D, F));
+  if (c.final_norm) {
+    e->norm_w = e->ts.add("enc.norm.weight", {D}, false);
+    e->norm_b = e->ts.add("enc.norm.bias", {D}, false);
+  }
+  int st = e->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, static_cast<int>(feat), c.compute);
+  if (st == JEPA_OK) st = dev_alloc(e->pe_bias_eff, static_cast<size_t>(D) * 4);
+  if (st != JEPA_OK) {
+    delete e;
+    return st;
+  }
+  *out = e;
+  return JEPA_OK;
+}
+
+void jepa_encoder_free(jepa_encoder* enc) {
+  if (!enc) return;
+  dev_free(enc->pe_bias_eff);
+  delete enc;
+}
+
+int jepa_encoder_set_tensor(jepa_encoder* enc, const char* name, const void* host,
+                            int src_dtype, const int64_t* shape, int ndim) {
+  if (!enc) return JEPA_ERR_ARG;
+  const int st = enc->ts.set_tensor(name, host, src_dtype, shape, ndim);
+  if (st == JEPA_OK) enc->pe_bias_dirty = true;
+  return st;
+}
+
+// Folds mod_embed_video into the patch-embedding bias on the host (fp32 sum of the two
+// fp32 vectors, the same value the GPU would form).
+static int refresh_pe_bias(jepa_encoder* e) {
+  if (!e->pe_bias_dirty) return JEPA_OK;
+  const Tensor& b = e->ts.t[e->pe_b];
+  std::vector<float> v(b.host);
+  if (e->mod >= 0) {
+    const Tensor& m = e->ts.t[e->mod];
+    for (size_t i = 0; i < v.size(); ++i) v[i] = v[i] + m.host[i];
+  }
+  JEPA_HIP(hipMemcpy(e->pe_bias_eff.p, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+  e->pe_bias_dirty = false;
+  return JEPA_OK;
+}
+
+int jepa_encode(jepa_encoder* enc, const uint8_t* clip_dev, int B, int T, int H, int W,
+                float* out_dev, void* stream) {
+  if (!enc || !clip_dev || !out_dev) return JEPA_ERR_ARG;
+  const jepa_encoder_config& c = enc->cfg;
+  if (B < 1 || T < 2 || T % 2 || H < 16 || W < 16 || H % 16 || W % 16) return JEPA_ERR_SHAPE;
+  const int gt = T / 2, gh = H / 16, gw = W / 16;
+  JEPA_TRY(check_grid(gt, gh, gw, c.rope_ref_grid));
+  const long long N = static_cast<long long>(gt) * gh * gw;
+  if (static_cast<long long>(B) * N > c.max_rows) return JEPA_ERR_SHAPE;
+  if (!enc->ts.all_set()) return JEPA_ERR_STATE;
+  JEPA_TRY(refresh_pe_bias(enc));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int M = static_cast<int>(B * N);
+  const int D = c.embed_dim, bf = c.compute == JEPA_BF16 ? 1 : 0;
+  const int feat = c.in_chans * c.tubelet * c.patch * c.patch;
+  JEPA_HIP(launch_patchify(clip_dev, B, T, H, W, enc->ws.a.p, bf, s));
+  JEPA_HIP(linear(c.compute, enc->ws.a.p, enc->ts.dev(enc->pe_w),
+                  static_cast<const float*>(enc->pe_bias_eff.p), out_dev, M, D, feat,
+                  JEPA_EPI_STORE, 1, s));
+  const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, c.rope_ref_grid};
+  JEPA_TRY(run_blocks(enc->ts, enc->blocks, c.n_layer, enc->ws, out_dev, B, static_cast<int>(N), D,
+                      c.ffn_dim, c.n_head, c.ln_eps, nullptr, rs, s));
+  if (c.final_norm)
+    JEPA_HIP(launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M, D,
+                              c.ln_eps, out_dev, 0, s));
+  return JEPA_OK;
+}
+
+int jepa_encode_tokens(jepa_encoder* enc, const float* x_dev, int B, int N,
+                       const int32_t* ids_dev, int gt, int gh, int gw, float* out_dev,
+                       void* stream) {
+  if (!enc || !x_dev || !out_dev) return JEPA_ERR_ARG;
+  const jepa_encoder_config& c = enc->cfg;
+  if (B < 1 || N < 1) return JEPA_ERR_SHAPE;
+  JEPA_TRY(check_grid(gt, gh, gw, c.rope_ref_grid));
+  if (!ids_dev && static_cast<long long>(N) > static_cast<long long>(gt) * gh * gw)
+    return JEPA_ERR_SHAPE;
+  if (static_cast<long long>(B) * N > c.max_rows) return JEPA_ERR_SHAPE;
+  if (!enc->ts.all_set()) return JEPA_ERR_STATE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int M = B * N, D = c.embed_dim;
+  if (out_dev != x_dev)
+    JEPA_HIP(hipMemcpyAsync(out_dev, x_dev, static_cast<size_t>(M) * D * 4,
+                            hipMemcpyDeviceToDevice, s));
+  const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, c.rope_ref_grid};
+  JEPA_TRY(run_blocks(enc->ts, enc->blocks, c.n_layer, enc->ws, out_dev, B, N, D, c.ffn_dim,
+                      c.n_head, c.ln_eps, ids_dev, rs, s));
+  if (c.final_norm)
+    JEPA_HIP(launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M, D,
+                              c.ln_eps, out_dev, 0, s));
+  return JEPA_OK;
+}
+
+}  // extern "C"
+
+// ==================================================================== predictor
+
+struct jepa_predictor {
+  jepa_predictor_config cfg;
+  TensorSet ts;
+  std::vector<BlockIdx> blocks;
+  int emb_w = -1, emb_b = -1, mask = -1, norm_w = -1, norm_b = -1, proj_w = -1, proj_b = -1;
+  Workspace ws;
+  DevBuf x;     // fp32 [max_rows, E] residual stream
+  DevBuf ids;   // int32 [max_rows] concat(ids_ctx, ids_tgt)
+};
+
+extern "C" {
+
+int jepa_predictor_create(const jepa_predictor_config* cfg, jepa_predictor** out) {
+  if (!cfg || !out) return JEPA_ERR_ARG;
+  *out = nullptr;
+  const jepa_predictor_config& c = *cfg;
+  if (c.n_head <= 0 || c.embed_dim <= 0) return JEPA_ERR_ARG;
+  const int hd = c.embed_dim / c.n_head;
+  JEPA_TRY(check_widths(c.compute, c.embed_dim, c.ffn_dim, c.n_head, hd));
+  if (c.enc_dim <= 0 || c.out_dim <= 0 || c.n_layer < 0 || c.n_mask_tokens < 1) return JEPA_ERR_ARG;
+  if (c.compute == JEPA_BF16 && (c.enc_dim % 64 != 0 || c.out_dim % 128 != 0)) return JEPA_ERR_ARG;
+  if (c.compute == JEPA_F32 && (c.out_dim % 4 != 0)) return JEPA_ERR_ARG;
+  if (c.rope_layout != JEPA_ROPE_TILED && c.rope_layout != JEPA_ROPE_INTERLEAVED) return JEPA_ERR_ARG;
+  if (c.max_rows <= 0) return JEPA_ERR_ARG;
+  if (!(c.ln_eps > 0.f) || !(c.rope_theta > 1.f)) return JEPA_ERR_ARG;
+
+  jepa_predictor* p = new (std::nothrow) jepa_predictor();
+  if (!p) return JEPA_ERR_OOM;
+  p->cfg = c;
+  p->ts.compute = c.compute;
+  const int64_t E = c.embed_dim, F = c.ffn_dim;
+  p->emb_w = p->ts.add("pred.embed.weight", {E, c.enc_dim}, true);
+  p->emb_b = p->ts.add("pred.embed.bias", {E}, false);
+  p->mask = p->ts.add("pred.mask_tokens", {c.n_mask_tokens, E}, false);
+  for (int i = 0; i < c.n_layer; ++i)
+    p->blocks.push_back(add_block(p->ts, "pred.blk." + std::to_string(i), E, F));
+  p->norm_w = p->ts.add("pred.norm.weight", {E}, false);
+  p->norm_b = p->ts.add("pred.norm.bias", {E}, false);
+  p->proj_w = p->ts.add("pred.proj.weight", {c.out_dim, E}, true);
+  p->proj_b = p->ts.add("pred.proj.bias", {c.out_dim}, false);
+  int st = p->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, c.enc_dim, c.compute);
+  if (st == JEPA_OK) st = dev_alloc(p->x, static_cast<size_t>(c.max_rows) * E * 4);
+  if (st == JEPA_OK) st = dev_alloc(p->ids, static_cast<size_t>(c.max_rows) * 4);
+  if (st != JEPA_OK) {
+    dev_free(p->x);
+    dev_free(p->ids);
+    delete p;
+    return st;
+  }
+  *out = p;
+  return JEPA_OK;
+}
+
+void jepa_predictor_free(jepa_predictor* pred) {
+  if (!pred) return;
+  dev_free(pred->x);
+  dev_free(pred->ids);
+  delete pred;
+}
+
+int jepa_predictor_set_tensor(jepa_predictor* pred, const char* name, const void* host,
+                              int src_dtype, const int64_t* shape, int ndim) {
+  if (!pred) return JEPA_ERR_ARG;
+  return pred->ts.set_tensor(name, host, src_dtype, shape, ndim);
+}
+
+int jepa_predict(jepa_predictor* pred, const float* z_dev, int n_enc,
+                 const int32_t* ids_ctx_dev, int n_ctx, const int32_t* ids_tgt_dev, int n_tgt,
+                 int mask_index, int gt, int gh, int gw, float* out_dev, void* stream) {
+  if (!pred || !z_dev || !ids_ctx_dev || !ids_tgt_dev || !out_dev) return JEPA_ERR_ARG;
+  const jepa_predictor_config& c = pred->cfg;
+  if (n_ctx < 1 || n_tgt < 1 || n_enc < 1) return JEPA_ERR_SHAPE;
+  if (static_cast<long long>(n_ctx) + n_tgt > c.max_rows) return JEPA_ERR_SHAPE;
+  JEPA_TRY(check_grid(gt, gh, gw, 0));
+  if (static_cast<long long>(gt) * gh * gw != n_enc) return JEPA_ERR_SHAPE;
+  if (!pred->ts.all_set()) return JEPA_ERR_STATE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = c.embed_dim, bf = c.compute == JEPA_BF16 ? 1 : 0;
+  const int M = n_ctx + n_tgt;
+  float* x = static_cast<float*>(pred->x.p);
+  int32_t* ids = static_cast<int32_t*>(pred->ids.p);
+  // [Notes §3] "2.1 predictor forward": embed the context rows, mask tokens at the
+  // targets, concatenate; positions from the concatenated ids ([Notes §4.4]).
+  JEPA_HIP(launch_gather_rows(z_dev, n_enc, c.enc_dim, ids_ctx_dev, n_ctx, pred->ws.a.p, bf, s));
+  JEPA_HIP(linear(c.compute, pred->ws.a.p, pred->ts.dev(pred->emb_w), pred->ts.devf(pred->emb_b),
+                  x, n_ctx, E, c.enc_dim, JEPA_EPI_STORE, 1, s));
+  int mi = mask_index % c.n_mask_tokens;
+  if (mi < 0) mi += c.n_mask_tokens;
+  JEPA_HIP(launch_fill_rows(x + static_cast<size_t>(n_ctx) * E,
+                            pred->ts.devf(pred->mask) + static_cast<size_t>(mi) * E, n_tgt, E, s));
+  JEPA_HIP(hipMemcpyAsync(ids, ids_ctx_dev, static_cast<size_t>(n_ctx) * 4,
+                          hipMemcpyDeviceToDevice, s));
+  JEPA_HIP(hipMemcpyAsync(ids + n_ctx, ids_tgt_dev, static_cast<size_t>(n_tgt) * 4,
+                          hipMemcpyDeviceToDevice, s));
+  const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, 0};
+  JEPA_TRY(run_blocks(pred->ts, pred->blocks, c.n_layer, pred->ws, x, 1, M, E, c.ffn_dim,
+                      c.n_head, c.ln_eps, ids, rs, s));
+  // final norm and output projection on the target rows only
+  float* xt = x + static_cast<size_t>(n_ctx) * E;
+  JEPA_HIP(launch_layernorm(xt, pred->ts.devf(pred->norm_w), pred->ts.devf(pred->norm_b), n_tgt, E,
+                            c.ln_eps, pred->ws.h.p, bf, s));
+  JEPA_HIP(linear(c.compute, pred->ws.h.p, pred->ts.dev(pred->proj_w), pred->ts.devf(pred->proj_b),
+                  out_dev, n_tgt, c.out_dim, E, JEPA_EPI_STORE, 1, s));
+  return JEPA_OK;
+}
+
+// ==================================================================== stand-alone ops
+
+int jepa_rope3d(const void* x_dev, void* y_dev, int dtype, int B, int N, int n_head,
+                int head_dim, int64_t row_stride, const int32_t* ids_dev, int gt, int gh,
+                int gw, int layout, float theta, int ref_grid, void* stream) {
+  if (!x_dev || !y_dev) return JEPA_ERR_ARG;
+  if (dtype != JEPA_F32 && dtype != JEPA_BF16) return JEPA_ERR_ARG;
+  if (layout != JEPA_ROPE_TILED && layout != JEPA_ROPE_INTERLEAVED) return JEPA_ERR_ARG;
+  if (!(theta > 1.f) || ref_grid < 0 || ref_grid == 1) return JEPA_ERR_ARG;
+  if (B < 0 || N < 0 || n_head < 1) return JEPA_ERR_SHAPE;
+  if (head_dim < 6 || head_dim > 96 || head_dim % 2) return JEPA_ERR_SHAPE;
+  if (row_stride < static_cast<int64_t>(n_head) * head_dim || row_stride % 2) return JEPA_ERR_SHAPE;
+  if (gt < 1 || gh < 1 || gw < 1) return JEPA_ERR_SHAPE;
+  if (ref_grid > 1 && (gh < 2 || gw < 2)) return JEPA_ERR_SHAPE;
+  if (!ids_dev && static_cast<long long>(N) > static_cast<long long>(gt) * gh * gw) return JEPA_ERR_SHAPE;
+  if (B == 0 || N == 0) return JEPA_OK;
+  const RopeSpec rs{gt, gh, gw, layout, theta, ref_grid};
+  return hip_status(launch_rope3d(x_dev, y_dev, dtype == JEPA_BF16, B, N, n_head, head_dim,
+                                  row_stride, ids_dev, rs, static_cast<hipStream_t>(stream)));
+}
+
+int jepa_layernorm(const float* x_dev, const float* weight_dev, const float* bias_dev, int M,
+                   int D, float eps, void* out_dev, int out_dtype, void* stream) {
+  if (!x_dev || !weight_dev || !bias_dev || !out_dev) return JEPA_ERR_ARG;
+  if (out_dtype != JEPA_F32 && out_dtype != JEPA_BF16) return JEPA_ERR_ARG;
+  if (!(eps > 0.f)) return JEPA_ERR_ARG;
+  if (M < 0 || D <= 0 || D % 64 || D > 4096) return JEPA_ERR_SHAPE;
+  const int vpt = D / 64;
+  // the kernel is instantiated for these row lengths
+  static const int ok_vpt[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 40, 48, 64};
+  bool ok = false;
+  for (int v : ok_vpt) ok = ok || v == vpt;
+  if (!ok) return JEPA_ERR_SHAPE;
+  if (M == 0) return JEPA_OK;
+  return hip_status(launch_layernorm(x_dev, weight_dev, bias_dev, M, D, eps, out_dev,
+                                     out_dtype == JEPA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+int jepa_linear(const void* A_dev, const void* W_dev, const float* bias_dev, void* C_dev, int M,
+                int N, int K, int dtype, int epilogue, int out_dtype, void* stream) {
+  if (!A_dev || !W_dev || !C_dev) return JEPA_ERR_ARG;
+  if (dtype != JEPA_F32 && dtype != JEPA_BF16) return JEPA_ERR_ARG;
+  if (out_dtype != JEPA_F32 && out_dtype != JEPA_BF16) return JEPA_ERR_ARG;
+  if (epilogue != JEPA_EPI_STORE && epilogue != JEPA_EPI_GELU && epilogue != JEPA_EPI_RESIDUAL)
+    return JEPA_ERR_ARG;
+  if (epilogue == JEPA_EPI_RESIDUAL && out_dtype != JEPA_F32) return JEPA_ERR_ARG;
+  if (dtype == JEPA_F32 && out_dtype != JEPA_F32) return JEPA_ERR_ARG;
+  if (M < 0 || N <= 0 || K <= 0) return JEPA_ERR_SHAPE;
+  if (dtype == JEPA_BF16 && (N % 128 || K % 64)) return JEPA_ERR_SHAPE;
+  if (dtype == JEPA_F32 && (N % 4 || K % 4)) return JEPA_ERR_SHAPE;
+  if (M == 0) return JEPA_OK;
+  return hip_status(linear(dtype, A_dev, W_dev, bias_dev, C_dev, M, N, K, epilogue,
+                           out_dtype == JEPA_F32, static_cast<hipStream_t>(stream)));
+}
+
+int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
+                   int head_dim, const int32_t* ids_dev, int gt, int gh, int gw, int layout,
+                   float theta, int ref_grid, void* stream) {
+  if (!qkv_dev || !out_dev) return JEPA_ERR_ARG;
+  if (dtype != JEPA_F32 && dtype != JEPA_BF16) return JEPA_ERR_ARG;
+  if (layout != JEPA_ROPE_TILED && layout != JEPA_ROPE_INTERLEAVED) return JEPA_ERR_ARG;
+  if (!(theta > 1.f)) return JEPA_ERR_ARG;
+  if (head_dim != 64 && head_dim != 32) return JEPA_ERR_SHAPE;
+  if (B < 0 || N < 0 || n_head < 1) return JEPA_ERR_SHAPE;
+  JEPA_TRY(check_grid(gt, gh, gw, ref_grid));
+  if (!ids_dev && static_cast<long long>(N) > static_cast<long long>(gt) * gh * gw) return JEPA_ERR_SHAPE;
+  if (B == 0 || N == 0) return JEPA_OK;
+  const RopeSpec rs{gt, gh, gw, layout, theta, ref_grid};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == JEPA_BF16)
+    return hip_status(launch_attention_bf16(static_cast<const uint16_t*>(qkv_dev),
+                                            static_cast<uint16_t*>(out_dev), B, N, n_head,
+                                            head_dim, ids_dev, rs, s));
+  return hip_status(launch_attention_f32(static_cast<const float*>(qkv_dev),
+                                         static_cast<float*>(out_dev), B, N, n_head, head_dim,
+                                         ids_dev, rs, s));
+}
+
+}  // extern "C"

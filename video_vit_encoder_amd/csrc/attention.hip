@@ -1,0 +1,396 @@
+// Multi-head softmax attention with the 3-D RoPE applied to q and k as they are loaded.
+//
+// What is computed ([Notes §4]): for each clip and head, softmax(R(q) R(k)^T / sqrt(hd)) v
+// over every token of the clip (no mask), with R the 3-D RoPE of the token's (t, h, w)
+// position: d = 2*((hd/3)/2) dims per axis, adjacent pairs rotated, tiled ([Notes §4.1])
+// or interleaved ([Notes §4.2]) frequency layout, optional interpolation ([Notes §4.3]).
+// RoPE acts on q and k only, before the 1/sqrt(hd) scaling.
+//
+// bf16 kernel (gfx950 MFMA, fp32 softmax and accumulation):
+//   * a workgroup owns 128 query rows of one (clip, head); each of its 4 wavefronts owns
+//     32 of them and keeps them, rotated and pre-scaled by log2(e)/sqrt(hd), as bf16
+//     MFMA operands in registers;
+//   * keys/values stream through LDS 64 at a time; K is rotated on its way from HBM to
+//     LDS (angles from per-axis cos/sin tables built in LDS at kernel start), V is
+//     written transposed so it can serve as the A operand of the second product;
+//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16): in the 32x32 accumulator a lane holds 16
+//     keys of one query, so the running max and sum are per lane plus one exchange with
+//     the lane 32 away;
+//   * O^T += V^T P^T: P^T leaves the first product already in the B-operand layout of
+//     the second (the key <-> register-slot map is the same on both sides), and O^T keeps
+//     one query per lane, so the online-softmax rescale is per lane too.
+// fp32 kernel: one query per thread, plain FMA, for the fp32 encoder path.
+#include "common.h"
+#include "kernels.h"
+
+namespace jepa {
+
+struct RopeFreq {
+  float w[16];
+};
+
+// cos/sin of every (axis, coordinate, frequency) the clip's grid can need, in LDS:
+// tab[(axis*kMaxGridSide + coord) * MF + k] = (cos, sin) of p_axis(coord) * omega_k.
+template <int MF>
+__device__ void build_rope_tables(float2* tab, const RopeSpec& r, const RopeFreq& fr) {
+  // stage the frequencies through LDS with constant indices (no private copy of `fr`)
+  __shared__ float om[16];
+#pragma unroll
+  for (int k = 0; k < MF; ++k)
+    if (threadIdx.x == k) om[k] = fr.w[k];
+  __syncthreads();
+  const int rows = r.gt + r.gh + r.gw;
+  for (int e = threadIdx.x; e < rows * MF; e += blockDim.x) {
+    const int row = e / MF, k = e - row * MF;
+    int axis, coord;
+    if (row < r.gt) {
+      axis = 0; coord = row;
+    } else if (row < r.gt + r.gh) {
+      axis = 1; coord = row - r.gt;
+    } else {
+      axis = 2; coord = row - r.gt - r.gh;
+    }
+    float p = static_cast<float>(coord);
+    if (axis > 0 && r.ref_grid > 0) {
+      const int side = axis == 1 ? r.gh : r.gw;
+      p = p * static_cast<float>(r.ref_grid - 1) / static_cast<float>(side - 1);
+    }
+    float sv, cv;
+    sincosf(p * om[k], &sv, &cv);
+    tab[(axis * kMaxGridSide + coord) * MF + k] = make_float2(cv, sv);
+  }
+}
+
+// Rotate the NE consecutive dims [j0, j0 + NE) (j0 even) of one head vector held in x.
+template <int HD, int NE>
+__device__ __forceinline__ void rope_chunk(float* x, int j0, const Thw& g, int layout,
+                                           const float2* tab) {
+  constexpr int D3 = 2 * ((HD / 3) / 2);
+  constexpr int MF = D3 / 2;
+#pragma unroll
+  for (int e = 0; e < NE; e += 2) {
+    const int j = j0 + e;
+    if (j < 3 * D3) {
+      const int a = j / D3, jl = j - a * D3;
+      const int coord = a == 0 ? g.t : (a == 1 ? g.h : g.w);
+      int i0, i1;
+      if (layout == 0) {
+        i0 = jl % MF;
+        i1 = (jl + 1) % MF;
+      } else {
+        i0 = i1 = jl >> 1;
+      }
+      const float2 cs0 = tab[(a * kMaxGridSide + coord) * MF + i0];
+      const float2 cs1 = tab[(a * kMaxGridSide + coord) * MF + i1];
+      const float x0 = x[e], x1 = x[e + 1];
+      x[e] = x0 * cs0.x - x1 * cs0.y;
+      x[e + 1] = x1 * cs1.x + x0 * cs1.y;
+    }
+  }
+}
+
+__device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
+  const int id = ids ? ids[n] : n;
+  return min(max(id, 0), ntot - 1);
+}
+
+// ---------------------------------------------------------------- bf16 / MFMA
+
+template <int HD>
+__global__ __launch_bounds__(256)
+void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, int N,
+                      int H, const int32_t* __restrict__ ids, RopeSpec r, RopeFreq fr,
+                      float qscale) {
+  constexpr int D3 = 2 * ((HD / 3) / 2);
+  constexpr int MF = D3 / 2;
+  constexpr int BQ = 128, BKV = 64;
+  constexpr int CH = HD / 8;        // 16-byte chunks per head row
+  constexpr int VT_LD = BKV + 4;    // padded row of the transposed V tile
+  constexpr int KS = HD / 16;       // MFMA k-steps over the head dim
+
+  __shared__ float2 tab[3 * kMaxGridSide * MF];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * VT_LD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int D = H * HD, ld = 3 * D;
+  const int ntot = r.gt * r.gh * r.gw;
+  const uint16_t* base = qkv + static_cast<size_t>(b) * N * ld + head * HD;
+
+  build_rope_tables<MF>(tab, r, fr);
+  __syncthreads();
+
+  // ---- this lane's query: rotate, scale, keep as B operands (dims kk*16 + hh*8 + [0,8))
+  const int q = blockIdx.x * BQ + wave * 32 + l32;
+  bf16x8 qf[KS];
+  {
+    const int qr = min(q, N - 1);
+    const Thw g = decode_id(token_id(ids, qr, ntot), r.gh, r.gw);
+    const uint16_t* src = base + static_cast<size_t>(qr) * ld;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int j0 = kk * 16 + hh * 8;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + j0);
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_to_f32(static_cast<uint16_t>(raw[e] & 0xFFFF));
+        x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(raw[e] >> 16));
+      }
+      rope_chunk<HD, 8>(x, j0, g, r.layout, tab);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = static_cast<__bf16>(x[e] * qscale);
+    }
+  }
+
+  f32x16 o[HD / 32];
+#pragma unroll
+  for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int kb = 0; kb < N; kb += BKV) {
+    __syncthreads();
+    // ---- K tile: rotate on load, store swizzled [key][chunk]
+#pragma unroll
+    for (int it = 0; it < (BKV * CH + 255) / 256; ++it) {
+      const int id = tid + it * 256;
+      if (id < BKV * CH) {
+        const int key = id / CH, c = id - key * CH;
+        const int kr = min(kb + key, N - 1);
+        const Thw g = decode_id(token_id(ids, kr, ntot), r.gh, r.gw);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(kr) * ld + D + c * 8);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf16_to_f32(static_cast<uint16_t>(raw[e] & 0xFFFF));
+          x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(raw[e] >> 16));
+        }
+        rope_chunk<HD, 8>(x, c * 8, g, r.layout, tab);
+        u32x4 p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+        const int sw = (HD == 64) ? (c ^ (key & 7)) : (c ^ ((key >> 1) & 3));
+        *reinterpret_cast<u32x4*>(Ks + key * HD + sw * 8) = p;
+      }
+    }
+    // ---- V tile: two keys x 8 dims per thread, written transposed Vt[dim][key]
+#pragma unroll
+    for (int it = 0; it < ((BKV / 2) * CH + 255) / 256; ++it) {
+      const int id = tid + it * 256;
+      if (id < (BKV / 2) * CH) {
+        const int kp = id / CH, c = id - kp * CH;
+        const int k0 = min(kb + 2 * kp, N - 1), k1 = min(kb + 2 * kp + 1, N - 1);
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(k0) * ld + 2 * D + c * 8);
+        const u32x4 v1 = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(k1) * ld + 2 * D + c * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = (v0[e] & 0xFFFFu) | (v1[e] << 16);
+          const uint32_t hi = (v0[e] >> 16) | (v1[e] & 0xFFFF0000u);
+          *reinterpret_cast<uint32_t*>(Vt + (c * 8 + 2 * e) * VT_LD + 2 * kp) = lo;
+          *reinterpret_cast<uint32_t*>(Vt + (c * 8 + 2 * e + 1) * VT_LD + 2 * kp) = hi;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for keys [kb, kb+64): two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[t2][i] = 0.f;
+      const int key = t2 * 32 + l32;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int c = kk * 2 + hh;
+        const int sw = (HD == 64) ? (c ^ (key & 7)) : (c ^ ((key >> 1) & 3));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + key * HD + sw * 8);
+        s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[t2], 0, 0, 0);
+      }
+    }
+    // element i of s[t2] is key kb + t2*32 + 8*(i/4) + 4*hh + (i%4) of query q
+    if (kb + BKV > N) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb + t2 * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= N) s[t2][i] = -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float ls = 0.f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2f(s[t2][i] - m_new);
+        ls += p;
+        pf[t2 * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+      }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+
+    // ---- O^T += V^T P^T; slot s of k-step ks is key ks*16 + 8*(s/4) + 4*hh + (s%4)
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) {
+      const uint16_t* vrow = Vt + (dt * 32 + l32) * VT_LD;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ks * 16 + 4 * hh);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ks * 16 + 8 + 4 * hh);
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks],
+                                                        o[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- normalise and store: element i of o[dt] is dim dt*32 + 8*(i/4) + 4*hh + (i%4)
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  if (q < N) {
+    uint16_t* dst = out + (static_cast<size_t>(b) * N + q) * D + head * HD;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv);
+        pk[1] = pack_bf16x2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g4 + 4 * hh) = pk;
+      }
+  }
+}
+
+static RopeFreq make_freq(int head_dim, float theta) {
+  RopeFreq f{};
+  const int m = (2 * ((head_dim / 3) / 2)) / 2;
+  for (int k = 0; k < m && k < 16; ++k)
+    f.w[k] = static_cast<float>(1.0 / pow(static_cast<double>(theta), static_cast<double>(k) / m));
+  return f;
+}
+
+hipError_t launch_attention_bf16(const uint16_t* qkv, uint16_t* out, int B, int N, int n_head,
+                                 int head_dim, const int32_t* ids, const RopeSpec& r,
+                                 hipStream_t s) {
+  if (B <= 0 || N <= 0) return hipSuccess;
+  const RopeFreq fr = make_freq(head_dim, r.theta);
+  const float qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
+  const dim3 grid((N + 127) / 128, n_head, B);
+  if (head_dim == 64)
+    attn_bf16_kernel<64><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale);
+  else if (head_dim == 32)
+    attn_bf16_kernel<32><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fp32 / FMA
+
+template <int HD>
+__global__ __launch_bounds__(64)
+void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out, int N, int H,
+                     const int32_t* __restrict__ ids, RopeSpec r, RopeFreq fr, float scale) {
+  constexpr int D3 = 2 * ((HD / 3) / 2);
+  constexpr int MF = D3 / 2;
+  constexpr int BKV = 64;
+  __shared__ float2 tab[3 * kMaxGridSide * MF];
+  __shared__ float Ks[BKV][HD];
+  __shared__ float Vs[BKV][HD];
+  const int tid = threadIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const int D = H * HD, ld = 3 * D;
+  const int ntot = r.gt * r.gh * r.gw;
+  const float* base = qkv + static_cast<size_t>(b) * N * ld + head * HD;
+  build_rope_tables<MF>(tab, r, fr);
+  __syncthreads();
+
+  const int q = blockIdx.x * 64 + tid;
+  const int qr = min(q, N - 1);
+  float qv[HD], ov[HD];
+  {
+    const Thw g = decode_id(token_id(ids, qr, ntot), r.gh, r.gw);
+#pragma unroll
+    for (int j = 0; j < HD; ++j) qv[j] = base[static_cast<size_t>(qr) * ld + j];
+    rope_chunk<HD, HD>(qv, 0, g, r.layout, tab);
+#pragma unroll
+    for (int j = 0; j < HD; ++j) {
+      qv[j] *= scale;
+      ov[j] = 0.f;
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int kb = 0; kb < N; kb += BKV) {
+    __syncthreads();
+    {
+      const int kr = min(kb + tid, N - 1);
+      const Thw g = decode_id(token_id(ids, kr, ntot), r.gh, r.gw);
+      float kv[HD];
+#pragma unroll
+      for (int j = 0; j < HD; ++j) kv[j] = base[static_cast<size_t>(kr) * ld + D + j];
+      rope_chunk<HD, HD>(kv, 0, g, r.layout, tab);
+#pragma unroll
+      for (int j = 0; j < HD; ++j) {
+        Ks[tid][j] = kv[j];
+        Vs[tid][j] = base[static_cast<size_t>(kr) * ld + 2 * D + j];
+      }
+    }
+    __syncthreads();
+    const int nk = min(BKV, N - kb);
+    for (int k = 0; k < nk; ++k) {
+      float sc = 0.f;
+#pragma unroll
+      for (int j = 0; j < HD; ++j) sc = fmaf(qv[j], Ks[k][j], sc);
+      if (sc > m_run) {
+        const float a = expf(m_run - sc);
+        l_run *= a;
+#pragma unroll
+        for (int j = 0; j < HD; ++j) ov[j] *= a;
+        m_run = sc;
+      }
+      const float p = expf(sc - m_run);
+      l_run += p;
+#pragma unroll
+      for (int j = 0; j < HD; ++j) ov[j] = fmaf(p, Vs[k][j], ov[j]);
+    }
+  }
+  if (q < N) {
+    const float inv = 1.0f / l_run;
+    float* dst = out + (static_cast<size_t>(b) * N + q) * D + head * HD;
+#pragma unroll
+    for (int j = 0; j < HD; ++j) dst[j] = ov[j] * inv;
+  }
+}
+
+hipError_t launch_attention_f32(const float* qkv, float* out, int B, int N, int n_head,
+                                int head_dim, const int32_t* ids, const RopeSpec& r,
+                                hipStream_t s) {
+  if (B <= 0 || N <= 0) return hipSuccess;
+  const RopeFreq fr = make_freq(head_dim, r.theta);
+  const float scale = static_cast<float>(1.0 / sqrt(static_cast<double>(head_dim)));
+  const dim3 grid((N + 63) / 64, n_head, B);
+  if (head_dim == 64)
+    attn_f32_kernel<64><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, r, fr, scale);
+  else if (head_dim == 32)
+    attn_f32_kernel<32><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, r, fr, scale);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace jepa
