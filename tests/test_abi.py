@@ -96,3 +96,15 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_one_hip_runtime_in_the_process():
+    # libjepa must bind to the HIP runtime torch loaded, not bring a second one
+    import subprocess, sys
+    code = ("import video_vit_encoder_amd as J; J.load();"
+            "m = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l};"
+            "print(len(m))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"

@@ -221,15 +221,17 @@ def test_encode_errors_leave_output_untouched():
     lib = J.load()
     stream = torch.cuda.current_stream().cuda_stream
 
-    def raw(clip_np):
+    def raw(clip_np, T=None):
         c = u8(clip_np)
-        B, T, H, W_, _ = clip_np.shape
-        return lib.jepa_encode(enc.handle, c.data_ptr(), B, T, H, W_, out.data_ptr(), stream)
+        B, T0, H, W_, _ = clip_np.shape
+        return lib.jepa_encode(enc.handle, c.data_ptr(), B, T0 if T is None else T, H, W_,
+                               out.data_ptr(), stream)
 
     assert raw(synth.clip_u8(0, 1, 3, 64, 64)) == -2      # odd T
     assert raw(synth.clip_u8(0, 1, 4, 72, 64)) == -2      # H not a multiple of 16
     assert raw(synth.clip_u8(0, 2, 4, 64, 64)) == -2      # B*N above max_rows
-    assert raw(synth.clip_u8(0, 1, 0, 64, 64)) == -2      # no frames
+    assert raw(synth.clip_u8(0, 1, 4, 64, 64), T=0) == -2  # no frames
+    assert lib.jepa_encode(enc.handle, None, 1, 4, 64, 64, out.data_ptr(), stream) == -1
     with pytest.raises(J.JepaError) as e:       # unknown tensor name
         J.jepa_encoder_set_tensor(enc.handle, "enc.blk.9.ln1.weight", np.ones(768, np.float32))
     assert e.value.status == -4

@@ -87,12 +87,17 @@ def _enc_dim(handle: int) -> int:
 
 
 def load() -> ctypes.CDLL:
-    """Load libjepa.so from the package directory (raises if it was never built)."""
+    """Load libjepa.so from the package directory (raises if it was never built).
+
+    torch is imported first: its HIP runtime (same soname as the system one) is then
+    already in the process, so libjepa binds to it and shares torch's device memory and
+    streams.  Loading libjepa first would bring a second, separate HIP runtime."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m video_vit_encoder_amd.build`")
+        import torch  # noqa: F401  (see above)
         lib = ctypes.CDLL(LIB_PATH)
         for name, (args, res) in _SIGS.items():
             f = getattr(lib, name)
