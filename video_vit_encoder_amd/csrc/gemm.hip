@@ -3,12 +3,25 @@
 // Weights are stored [out, in] row-major ([Notes §2] key map), so both operands are
 // contiguous along K and map straight onto the MFMA operand layout.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  A workgroup owns a BM x BN
-// output tile; its waves own WM x WN sub-tiles made of 32x32 MFMA blocks.  K advances
-// 64 at a time: the next K-slab is fetched global -> registers while the current one is
-// consumed from LDS.  LDS rows are 128 B (64 bf16); the 16-byte chunk c of row r lives
-// at chunk c ^ (r & 7), so the 8 lanes that read one chunk column of 8 consecutive rows
-// hit 8 different bank groups.
+// bf16 path (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
+//   * a workgroup of 8 wavefronts (2 per SIMD, so one wave's MFMAs cover the other's
+//     LDS reads) computes 256 (rows of A) x 128 (rows of W) output tiles; wave (wm, wn)
+//     owns 64 x 64 of a tile as 4 x 4 blocks of 16 x 16;
+//   * the kernel is persistent: one workgroup per CU walks its tiles, and the K-slabs of
+//     all its tiles form one stream through a 3-stage ring of LDS buffers.  Slabs are
+//     64 deep and are filled by global_load_lds_dwordx4 (HBM/L2 -> LDS, no register
+//     staging) two stages ahead of the MFMAs, so the next tile's first slabs load
+//     while the current tile's epilogue runs; one barrier per slab;
+//   * LDS rows are 128 B (64 bf16); the 16-byte chunk c of row r lives at chunk
+//     c ^ (r & 7).  A DMA instruction writes 64 consecutive 16-byte slots (8 rows), so
+//     lane p of it fetches the global chunk that belongs in slot p.  With the 16x16x32
+//     operand pattern (16 rows x 4 chunks per read) this layout keeps ds_read_b128 near
+//     the LDS peak on gfx950;
+//   * the MFMA takes the W fragment as its first operand, so each lane ends up holding 4
+//     consecutive output columns of one output row: the epilogue (bias, GELU, residual)
+//     reads and writes 8- or 16-byte vectors;
+//   * tiles are dealt so that the 32 workgroups of one XCD (work-groups go to the 8
+//     XCDs round-robin) work on neighbouring tiles at the same time.
 //
 // fp32 path: a plain 64x64-tile FMA kernel (no MFMA), used by the fp32 encoder.
 #include "common.h"
@@ -18,147 +31,245 @@ namespace jepa {
 
 enum { EPI_STORE = 0, EPI_GELU = 1, EPI_RESIDUAL = 2 };
 
-template <int BM, int BN, int WM, int WN, int EPI, bool OUT_F32>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+// HBM/L2 -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane p of the wave
+// writes LDS bytes [lds + 16p, lds + 16p + 16) from base + voff.  Issued through inline
+// asm so that the kernel, not the compiler, decides how many of these may still be in
+// flight at each barrier (s_waitcnt vmcnt).  lds must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p)));
+}
+
+// GELU with erf from Abramowitz & Stegun 7.1.26 (|error of erf| <= 1.5e-7, far below
+// the bf16 rounding of the output): erf(x) = 1 - t(a1 + t(a2 + ...)) exp(-x^2),
+// t = 1 / (1 + p|x|), odd in x.
+__device__ __forceinline__ float gelu_as(float z) {
+  const float x = fabsf(z) * 0.70710678118654752440f;
+  const float t = __frcp_rn(fmaf(0.3275911f, x, 1.0f));
+  float y = fmaf(1.061405429f, t, -1.453152027f);
+  y = fmaf(y, t, 1.421413741f);
+  y = fmaf(y, t, -0.284496736f);
+  y = fmaf(y, t, 0.254829592f);
+  const float e = 1.0f - y * t * __expf(-x * x);
+  return 0.5f * z * (1.0f + copysignf(e, z));
+}
+
+namespace gemm {
+constexpr int BM = 256, BN = 128, BK = 64, STAGES = 3;
+constexpr int NWAVES = 8, NT = NWAVES * 64;    // 2 waves per SIMD
+constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 48 KB
+constexpr int A_LOADS = A_BYTES / 16 / NT;      // 4 DMA instructions per thread
+constexpr int B_LOADS = B_BYTES / 16 / NT;      // 2
+constexpr int LOADS = A_LOADS + B_LOADS;
+constexpr int WM = 64, WN = 64;                 // wave tile
+constexpr int FI = WM / 16, FJ = WN / 16;       // 16x16 blocks per wave
+}  // namespace gemm
+
+template <int EPI, bool OUT_F32>
+__global__ __launch_bounds__(gemm::NT)
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                       const float* __restrict__ bias, void* __restrict__ Cv, int M, int N, int K) {
-  constexpr int NWN = BN / WN;
-  constexpr int NT = (BM / WM) * NWN * 64;
-  constexpr int BK = 64;
-  constexpr int TI = WM / 32, TJ = WN / 32;
-  constexpr int A_CH = BM * BK / 8 / NT;
-  constexpr int B_CH = BN * BK / 8 / NT;
-  static_assert(A_CH * NT * 8 == BM * BK && B_CH * NT * 8 == BN * BK, "tile/thread mismatch");
+  using namespace gemm;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * BK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA LDS bases
+  const int wm = wave >> 1, wn = wave & 1;                     // 4 x 2 waves of 64 x 64
+  const int q16 = lane >> 4, l16 = lane & 15;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / NWN, wn = wave % NWN;
   const int tiles_n = N / BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  u32x4 ra[A_CH], rb[B_CH];
-#define JEPA_GEMM_GLOAD(k0)                                                                    \
-  do {                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                         \
-      const int id = tid + i * NT, row = id >> 3, c = id & 7;                                  \
-      const int gm = min(m0 + row, M - 1);                                                     \
-      ra[i] = *reinterpret_cast<const u32x4*>(A + static_cast<size_t>(gm) * K + (k0) + c * 8); \
-    }                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                         \
-      const int id = tid + i * NT, row = id >> 3, c = id & 7;                                  \
-      rb[i] = *reinterpret_cast<const u32x4*>(W + static_cast<size_t>(n0 + row) * K + (k0) + c * 8); \
-    }                                                                                          \
-  } while (0)
-#define JEPA_GEMM_SSTORE()                                                                     \
-  do {                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                         \
-      const int id = tid + i * NT, row = id >> 3, c = id & 7;                                  \
-      *reinterpret_cast<u32x4*>(As + row * BK + ((c ^ (row & 7)) << 3)) = ra[i];               \
-    }                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                         \
-      const int id = tid + i * NT, row = id >> 3, c = id & 7;                                  \
-      *reinterpret_cast<u32x4*>(Bs + row * BK + ((c ^ (row & 7)) << 3)) = rb[i];               \
-    }                                                                                          \
-  } while (0)
-
-  f32x16 acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
+  const int tiles = ((M + BM - 1) / BM) * tiles_n;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int n_my = (tiles - b + G - 1) / G;   // tiles b, b + G, b + 2G, ...
   const int KT = K / BK;
-  JEPA_GEMM_GLOAD(0);
-  for (int kt = 0; kt < KT; ++kt) {
-    __syncthreads();
-    JEPA_GEMM_SSTORE();
-    __syncthreads();
-    if (kt + 1 < KT) JEPA_GEMM_GLOAD((kt + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = kk * 2 + (lane >> 5);
-      bf16x8 af[TI], bfr[TJ];
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8*>(As + row * BK + ((ch ^ (row & 7)) << 3));
-      }
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int row = wn * WN + j * 32 + (lane & 31);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + row * BK + ((ch ^ (row & 7)) << 3));
-      }
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  }
-#undef JEPA_GEMM_GLOAD
-#undef JEPA_GEMM_SSTORE
+  const int total = n_my * KT;
 
-  // Epilogue.  32x32 accumulator layout: lane l, element r holds
-  // row 8*(r/4) + 4*(l/32) + (r%4), column l%32 of the block.
+  // Tile of round i.  In full rounds the workgroups of XCD x = b % 8 take consecutive
+  // tiles (n fastest); the last, partial round keeps the plain order.
+  auto tile_of = [&](int i, int& m0, int& n0) {
+    int t = i * G + b;
+    if ((G & 7) == 0 && (i + 1) * G <= tiles) t = i * G + (b & 7) * (G >> 3) + (b >> 3);
+    const int tm = t / tiles_n;
+    m0 = tm * BM;
+    n0 = (t - tm * tiles_n) * BN;
+  };
+
+  // DMA mapping: instruction q of wave w fills rows [8g, 8g+8) of a tile, g = q*8 + w;
+  // lane p -> row 8g + p/8, slot p%8 holding logical chunk (p%8) ^ (p/8).
+  const int prow = lane >> 3, pchunk = (lane & 7) ^ prow;
+  const uint32_t smem_base = lds_addr(smem);
+
+  // Issue state: the next slab to load (tile it_iss, slab kt_iss) and the byte offsets
+  // of this lane's source rows in that tile, refreshed when the tile changes.
+  int it_iss = 0, kt_iss = 0, s_iss = 0;
+  uint32_t a_row[A_LOADS], b_row[B_LOADS];
+  auto set_rows = [&](int it) {
+    int m0, n0;
+    tile_of(it, m0, n0);
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int col = n0 + wn * WN + j * 32 + (lane & 31);
-    const float bv = bias ? bias[col] : 0.f;
+    for (int q = 0; q < A_LOADS; ++q) {
+      const int r = (q * NWAVES + wave) * 8 + prow;
+      a_row[q] = static_cast<uint32_t>(static_cast<size_t>(min(m0 + r, M - 1)) * K * 2) + pchunk * 16;
+    }
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
+    for (int q = 0; q < B_LOADS; ++q) {
+      const int r = (q * NWAVES + wave) * 8 + prow;
+      b_row[q] = static_cast<uint32_t>(static_cast<size_t>(n0 + r) * K * 2) + pchunk * 16;
+    }
+  };
+  auto issue_next = [&]() {
+    const uint32_t st = smem_base + (s_iss % STAGES) * STAGE_BYTES;
+    const uint32_t k0 = kt_iss * BK * 2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) {
-          float v = acc[i][j][r] + bv;
-          const size_t off = static_cast<size_t>(row) * N + col;
-          if (EPI == EPI_GELU) v = gelu_erf(v);
-          if (EPI == EPI_RESIDUAL) {
-            float* C = static_cast<float*>(Cv);
-            C[off] += v;
-          } else if (OUT_F32) {
-            static_cast<float*>(Cv)[off] = v;
-          } else {
-            static_cast<uint16_t*>(Cv)[off] = f32_to_bf16(v);
-          }
+    for (int q = 0; q < A_LOADS; ++q) dma16(A, a_row[q] + k0, st + (q * NWAVES + wave) * 1024);
+#pragma unroll
+    for (int q = 0; q < B_LOADS; ++q)
+      dma16(W, b_row[q] + k0, st + A_BYTES + (q * NWAVES + wave) * 1024);
+    ++s_iss;
+    if (++kt_iss == KT) {
+      kt_iss = 0;
+      if (++it_iss < n_my) set_rows(it_iss);
+    }
+  };
+
+  // fragment rows of this lane inside the A / W tiles (16x16x32 operand: row l%16,
+  // 8 consecutive k at chunk 4*step + l/16)
+  int arow[FI], brow[FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i) arow[i] = wm * WM + i * 16 + l16;
+#pragma unroll
+  for (int j = 0; j < FJ; ++j) brow[j] = wn * WN + j * 16 + l16;
+
+  if (total > 0) {
+    set_rows(0);
+    issue_next();
+  }
+  if (total > 1) issue_next();
+  int s = 0;  // position in this workgroup's slab stream
+  for (int it = 0; it < n_my; ++it) {
+    f32x4 acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kt = 0; kt < KT; ++kt, ++s) {
+      // slab s has landed once at most one later slab (LOADS DMAs) is still in flight
+      if (s + 1 < total)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(gemm::LOADS) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (s + 2 < total) issue_next();
+      const unsigned char* st = smem + (s % STAGES) * STAGE_BYTES;
+      const uint16_t* As = reinterpret_cast<const uint16_t*>(st);
+      const uint16_t* Bs = reinterpret_cast<const uint16_t*>(st + A_BYTES);
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        const int ch = ks * 4 + q16;
+        bf16x8 af[FI], bfr[FJ];
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(As + arow[i] * BK + ((ch ^ (arow[i] & 7)) << 3));
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + brow[j] * BK + ((ch ^ (brow[j] & 7)) << 3));
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+          for (int j = 0; j < FJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      }
+    }
+
+    // Epilogue of tile it.  acc[i][j] is the 16 (W rows) x 16 (A rows) block with lane
+    // l, element e at W row 4*(l/16) + e and A row l%16: four consecutive output
+    // columns per lane.
+    int m0, n0;
+    tile_of(it, m0, n0);
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int row = m0 + wm * WM + i * 16 + l16;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int col = n0 + wn * WN + j * 16 + 4 * q16;
+        const f32x4 bv = bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][e] + bv[e];
+          if (EPI == EPI_GELU) v[e] = OUT_F32 ? gelu_erf(v[e]) : gelu_as(v[e]);
+        }
+        const size_t off = static_cast<size_t>(row) * N + col;
+        if (EPI == EPI_RESIDUAL) {
+          f32x4* C = reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off);
+          f32x4 c = *C;
+          c[0] += v[0]; c[1] += v[1]; c[2] += v[2]; c[3] += v[3];
+          *C = c;
+        } else if (OUT_F32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+          u32x2 p;
+          p[0] = pack_bf16x2(v[0], v[1]);
+          p[1] = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cv) + off) = p;
         }
       }
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-static hipError_t dispatch_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C,
-                                int M, int N, int K, int epi, int out_f32, hipStream_t s) {
-  const dim3 grid(((M + BM - 1) / BM) * (N / BN));
-  const dim3 block((BM / WM) * (BN / WN) * 64);
-  if (epi == EPI_RESIDUAL) {
-    gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESIDUAL, true><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K);
-  } else if (epi == EPI_GELU) {
-    if (out_f32)
-      gemm_bf16_kernel<BM, BN, WM, WN, EPI_GELU, true><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K);
-    else
-      gemm_bf16_kernel<BM, BN, WM, WN, EPI_GELU, false><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K);
-  } else {
-    if (out_f32)
-      gemm_bf16_kernel<BM, BN, WM, WN, EPI_STORE, true><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K);
-    else
-      gemm_bf16_kernel<BM, BN, WM, WN, EPI_STORE, false><<<grid, block, 0, s>>>(A, W, bias, C, M, N, K);
+static int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    hipDeviceProp_t p;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess)
+      n = p.multiProcessorCount;
+    if (n <= 0) n = 256;
   }
+  return n;
+}
+
+template <int EPI, bool OUT_F32>
+static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float* bias, void* C,
+                              int M, int N, int K, hipStream_t s) {
+  using namespace gemm;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI, OUT_F32>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       STAGES * STAGE_BYTES);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int tiles = ((M + BM - 1) / BM) * (N / BN);
+  const dim3 grid(min(tiles, num_cus()));
+  gemm_bf16_kernel<EPI, OUT_F32><<<grid, NT, STAGES * STAGE_BYTES, s>>>(A, W, bias, C, M, N, K);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C,
                             int M, int N, int K, int epi, int out_f32, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  return dispatch_bf16<256, 128, 128, 64>(A, W, bias, C, M, N, K, epi, out_f32, s);
+  if (N % gemm::BN || K % gemm::BK) return hipErrorInvalidValue;
+  // the DMA addressing uses 32-bit byte offsets
+  if (static_cast<size_t>(M) * K * 2 >= (size_t(1) << 31) ||
+      static_cast<size_t>(N) * K * 2 >= (size_t(1) << 31))
+    return hipErrorInvalidValue;
+  if (epi == EPI_RESIDUAL) return gemm_launch<EPI_RESIDUAL, true>(A, W, bias, C, M, N, K, s);
+  if (epi == EPI_GELU)
+    return out_f32 ? gemm_launch<EPI_GELU, true>(A, W, bias, C, M, N, K, s)
+                   : gemm_launch<EPI_GELU, false>(A, W, bias, C, M, N, K, s);
+  return out_f32 ? gemm_launch<EPI_STORE, true>(A, W, bias, C, M, N, K, s)
+                 : gemm_launch<EPI_STORE, false>(A, W, bias, C, M, N, K, s);
 }
 
 // ---------------------------------------------------------------- fp32 path
