@@ -96,21 +96,95 @@ __device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
 
 // ---------------------------------------------------------------- bf16 / MFMA
 
+// Unsigned division by a runtime constant d >= 1 for n < 2^31 (round-up multiplier:
+// q = (umulhi(n, mul) + n) >> sh with sh = ceil(log2 d), mul = floor(2^32 (2^sh - d) / d) + 1).
+struct FastDiv {
+  uint32_t d, mul, sh;
+};
+
+static FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f{d, 0, 0};
+  while ((1ull << f.sh) < d) ++f.sh;
+  f.mul = static_cast<uint32_t>(((1ull << 32) * ((1ull << f.sh) - d)) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.mul) + n) >> f.sh;
+}
+
+// Grid coordinates of a (clamped) token id.
+__device__ __forceinline__ Thw decode_fast(int id, const FastDiv& dhw, const FastDiv& dw) {
+  Thw g;
+  g.t = static_cast<int>(fdiv(static_cast<uint32_t>(id), dhw));
+  const int rem = id - g.t * static_cast<int>(dhw.d);
+  g.h = static_cast<int>(fdiv(static_cast<uint32_t>(rem), dw));
+  g.w = rem - g.h * static_cast<int>(dw.d);
+  return g;
+}
+
+// Table code of head dim j: (axis << 24) | (axis*kMaxGridSide*MF + frequency index), or
+// -1 for a pass-through dim.  tiled: frequency j mod d/2 within the axis ([Notes §4.1]);
+// interleaved: frequency (j within the axis) / 2 ([Notes §4.2]).
 template <int HD>
-__global__ __launch_bounds__(256)
-void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, int N,
-                      int H, const int32_t* __restrict__ ids, RopeSpec r, RopeFreq fr,
-                      float qscale) {
+__device__ __forceinline__ int rope_code(int j, int layout) {
   constexpr int D3 = 2 * ((HD / 3) / 2);
   constexpr int MF = D3 / 2;
-  constexpr int BQ = 128, BKV = 64;
-  constexpr int CH = HD / 8;        // 16-byte chunks per head row
-  constexpr int VT_LD = BKV + 4;    // padded row of the transposed V tile
-  constexpr int KS = HD / 16;       // MFMA k-steps over the head dim
+  if (j >= 3 * D3) return -1;
+  const int a = j / D3, jl = j - a * D3;
+  return (a << 24) | (a * kMaxGridSide * MF + (layout == 0 ? jl % MF : jl >> 1));
+}
+
+// Rotation of one 8-dim chunk of a head vector held in x[8]; code[e] from rope_code.
+// Both dims of a pair always share the axis (d is even).
+template <int MF>
+__device__ __forceinline__ void rope8(float* x, const int* code, const Thw& g, const float2* tab) {
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    if (code[e] < 0) continue;
+    const int ax = code[e] >> 24;
+    const int c = ax == 0 ? g.t : (ax == 1 ? g.h : g.w);
+    const float2 cs0 = tab[(code[e] & 0xFFFFFF) + c * MF];
+    const float2 cs1 = tab[(code[e + 1] & 0xFFFFFF) + c * MF];
+    const float x0 = x[e], x1 = x[e + 1];
+    x[e] = x0 * cs0.x - x1 * cs0.y;
+    x[e + 1] = x1 * cs1.x + x0 * cs1.y;
+  }
+}
+
+// Flash attention, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 softmax and accumulators.
+//   * a workgroup of 4 wavefronts owns 256 queries of one (clip, head); each wave keeps
+//     two groups of 32, rotated once and pre-scaled by log2(e)/sqrt(hd), as bf16 MFMA B
+//     operands in registers.  256 queries share every key tile, so rotating K on its way
+//     into LDS costs little next to the MFMAs;
+//   * keys and values stream through LDS 64 at a time, double-buffered: the next tile is
+//     fetched into registers while the current one is consumed, then rotated (K) or
+//     transposed (V) into the other buffer; one barrier per tile;
+//   * S^T = K Q^T puts 16 keys of one query in each lane, so the online max and sum are
+//     per lane plus one exchange with the lane 32 away;
+//   * P^T leaves that MFMA already in the B-operand layout of O^T += V^T P^T, whose slot
+//     s of k-step ks is key 16ks + 8(s/4) + 4(l/32) + s%4.  V^T is stored in LDS with the
+//     keys of each 16-group in that order (quads 1 and 2 swapped), so every A operand is
+//     one 16-byte LDS read.
+template <int HD>
+__global__ __launch_bounds__(256, 2)
+void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, int N,
+                      int H, const int32_t* __restrict__ ids, RopeSpec r, RopeFreq fr,
+                      float qscale, FastDiv dhw, FastDiv dw) {
+  constexpr int D3 = 2 * ((HD / 3) / 2);
+  constexpr int MF = D3 / 2;
+  constexpr int BQ = 256, BKV = 64, NT = 256;
+  constexpr int CH = HD / 8;                 // 16-byte chunks per head row
+  constexpr int KS = HD / 16;                // MFMA k-steps over the head dim
+  constexpr int DT = HD / 32;                // 32-dim blocks of the output
+  constexpr int KCH = BKV * CH / NT;         // K chunks per thread per tile (2 or 1)
+  constexpr int VCH = (BKV / 2) * CH;        // V (2 keys x 8 dims) units per tile
+  constexpr int VP = BKV + 8;                // padded V^T row (keys), 144 B for 64 keys
+  static_assert(BKV * CH % NT == 0, "K tile mapping");
 
   __shared__ float2 tab[3 * kMaxGridSide * MF];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * VT_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -120,160 +194,194 @@ void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o
   const uint16_t* base = qkv + static_cast<size_t>(b) * N * ld + head * HD;
 
   build_rope_tables<MF>(tab, r, fr);
+
+  // per-thread constants of the K chunks this thread rotates: chunk c = tid % CH
+  const int kc = tid % CH;
+  int kcode[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kcode[e] = rope_code<HD>(kc * 8 + e, r.layout);
   __syncthreads();
 
-  // ---- this lane's query: rotate, scale, keep as B operands (dims kk*16 + hh*8 + [0,8))
-  const int q = blockIdx.x * BQ + wave * 32 + l32;
-  bf16x8 qf[KS];
-  {
+  // ---- queries: two groups of 32 per wave, rotated, scaled, bf16 B operands
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int q = blockIdx.x * BQ + wave * 64 + g * 32 + l32;
     const int qr = min(q, N - 1);
-    const Thw g = decode_id(token_id(ids, qr, ntot), r.gh, r.gw);
+    int id = ids ? ids[qr] : qr;
+    id = min(max(id, 0), ntot - 1);
+    const Thw gq = decode_fast(id, dhw, dw);
     const uint16_t* src = base + static_cast<size_t>(qr) * ld;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const int j0 = kk * 16 + hh * 8;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + j0);
+      const int c = kk * 2 + hh;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + c * 8);
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x[2 * e] = bf16_to_f32(static_cast<uint16_t>(raw[e] & 0xFFFF));
         x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(raw[e] >> 16));
       }
-      rope_chunk<HD, 8>(x, j0, g, r.layout, tab);
+      int qcode[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[kk][e] = static_cast<__bf16>(x[e] * qscale);
+      for (int e = 0; e < 8; ++e) qcode[e] = rope_code<HD>(c * 8 + e, r.layout);
+      rope8<MF>(x, qcode, gq, tab);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[g][kk][e] = static_cast<__bf16>(x[e] * qscale);
     }
   }
 
-  f32x16 o[HD / 32];
+  // ---- tile staging: global -> registers -> (rotate / transpose) -> LDS
+  u32x4 kraw[KCH];
+  int kid[KCH];
+  u32x4 vraw0, vraw1;
+  const int vkp = tid % (BKV / 2), vc = tid / (BKV / 2);   // V: key pair, dim chunk
+  auto fetch = [&](int kb) {
 #pragma unroll
-  for (int dt = 0; dt < HD / 32; ++dt)
+    for (int i = 0; i < KCH; ++i) {
+      const int key = (tid + i * NT) / CH;
+      const int kr = min(kb + key, N - 1);
+      int id = ids ? ids[kr] : kr;
+      kid[i] = min(max(id, 0), ntot - 1);
+      kraw[i] = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(kr) * ld + D + kc * 8);
+    }
+    if (tid < VCH) {
+      const int k0 = min(kb + 2 * vkp, N - 1), k1 = min(kb + 2 * vkp + 1, N - 1);
+      vraw0 = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(k0) * ld + 2 * D + vc * 8);
+      vraw1 = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(k1) * ld + 2 * D + vc * 8);
+    }
+  };
+  auto stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int i = 0; i < KCH; ++i) {
+      const int key = (tid + i * NT) / CH;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_to_f32(static_cast<uint16_t>(kraw[i][e] & 0xFFFF));
+        x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(kraw[i][e] >> 16));
+      }
+      rope8<MF>(x, kcode, decode_fast(kid[i], dhw, dw), tab);
+      u32x4 p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+      const int sw = (HD == 64) ? (kc ^ (key & 7)) : (kc ^ ((key >> 1) & 3));
+      *reinterpret_cast<u32x4*>(&Ks[buf][key * HD + sw * 8]) = p;
+    }
+    if (tid < VCH) {
+      // keys 2vkp, 2vkp+1 go to the pair slot of the quad-swapped order
+      const int k2 = 2 * vkp;
+      const int quad = (k2 >> 2) & 3;
+      const int pos = (k2 & ~15) | (((quad == 1) ? 2 : (quad == 2) ? 1 : quad) << 2) | (k2 & 3);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (vraw0[e] & 0xFFFFu) | (vraw1[e] << 16);
+        const uint32_t hi = (vraw0[e] >> 16) | (vraw1[e] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(&Vt[buf][(vc * 8 + 2 * e) * VP + pos]) = lo;
+        *reinterpret_cast<uint32_t*>(&Vt[buf][(vc * 8 + 2 * e + 1) * VP + pos]) = hi;
+      }
+    }
+  };
 
-  for (int kb = 0; kb < N; kb += BKV) {
-    __syncthreads();
-    // ---- K tile: rotate on load, store swizzled [key][chunk]
+  f32x16 o[2][DT];
 #pragma unroll
-    for (int it = 0; it < (BKV * CH + 255) / 256; ++it) {
-      const int id = tid + it * 256;
-      if (id < BKV * CH) {
-        const int key = id / CH, c = id - key * CH;
-        const int kr = min(kb + key, N - 1);
-        const Thw g = decode_id(token_id(ids, kr, ntot), r.gh, r.gw);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(kr) * ld + D + c * 8);
-        float x[8];
+  for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = bf16_to_f32(static_cast<uint16_t>(raw[e] & 0xFFFF));
-          x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(raw[e] >> 16));
-        }
-        rope_chunk<HD, 8>(x, c * 8, g, r.layout, tab);
-        u32x4 p;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-        const int sw = (HD == 64) ? (c ^ (key & 7)) : (c ^ ((key >> 1) & 3));
-        *reinterpret_cast<u32x4*>(Ks + key * HD + sw * 8) = p;
-      }
-    }
-    // ---- V tile: two keys x 8 dims per thread, written transposed Vt[dim][key]
-#pragma unroll
-    for (int it = 0; it < ((BKV / 2) * CH + 255) / 256; ++it) {
-      const int id = tid + it * 256;
-      if (id < (BKV / 2) * CH) {
-        const int kp = id / CH, c = id - kp * CH;
-        const int k0 = min(kb + 2 * kp, N - 1), k1 = min(kb + 2 * kp + 1, N - 1);
-        const u32x4 v0 = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(k0) * ld + 2 * D + c * 8);
-        const u32x4 v1 = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(k1) * ld + 2 * D + c * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (v0[e] & 0xFFFFu) | (v1[e] << 16);
-          const uint32_t hi = (v0[e] >> 16) | (v1[e] & 0xFFFF0000u);
-          *reinterpret_cast<uint32_t*>(Vt + (c * 8 + 2 * e) * VT_LD + 2 * kp) = lo;
-          *reinterpret_cast<uint32_t*>(Vt + (c * 8 + 2 * e + 1) * VT_LD + 2 * kp) = hi;
-        }
-      }
-    }
-    __syncthreads();
+      for (int i = 0; i < 16; ++i) o[g][dt][i] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-    // ---- S^T = K Q^T for keys [kb, kb+64): two 32-key blocks
-    f32x16 s[2];
+  const int ntiles = (N + BKV - 1) / BKV;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int kb = t * BKV, buf = t & 1;
+    if (t + 1 < ntiles) fetch(kb + BKV);
+    const uint16_t* Kb = Ks[buf];
+    const uint16_t* Vb = Vt[buf];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
+    for (int g = 0; g < 2; ++g) {
+      // S^T = K Q^T for keys [kb, kb + 64): two 32-key blocks
+      f32x16 sc[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[t2][i] = 0.f;
-      const int key = t2 * 32 + l32;
+      for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const int c = kk * 2 + hh;
-        const int sw = (HD == 64) ? (c ^ (key & 7)) : (c ^ ((key >> 1) & 3));
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + key * HD + sw * 8);
-        s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[t2], 0, 0, 0);
+        for (int i = 0; i < 16; ++i) sc[t2][i] = 0.f;
+        const int key = t2 * 32 + l32;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const int c = kk * 2 + hh;
+          const int sw = (HD == 64) ? (c ^ (key & 7)) : (c ^ ((key >> 1) & 3));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + key * HD + sw * 8);
+          sc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][kk], sc[t2], 0, 0, 0);
+        }
       }
-    }
-    // element i of s[t2] is key kb + t2*32 + 8*(i/4) + 4*hh + (i%4) of query q
-    if (kb + BKV > N) {
+      // element i of sc[t2] is key kb + 32 t2 + 8(i/4) + 4 hh + i%4 of this lane's query
+      if (kb + BKV > N) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kb + t2 * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= N) sc[t2][i] = -INFINITY;
+      }
+      float mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sc[0][i], sc[1][i]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[g], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+      m_run[g] = m_new;
+      float ls = 0.f;
+      bf16x8 pf[4];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb + t2 * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= N) s[t2][i] = -INFINITY;
-    }
-    float mx = s[0][0];
+        for (int i = 0; i < 16; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(sc[t2][i] - m_new);
+          ls += pv;
+          pf[t2 * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(pv);
+        }
+      l_run[g] = l_run[g] * alpha + ls;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float ls = 0.f;
-    bf16x8 pf[4];
+        for (int i = 0; i < 16; ++i) o[g][dt][i] *= alpha;
+      // O^T += V^T P^T
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+      for (int dt = 0; dt < DT; ++dt) {
+        const int dim = dt * 32 + l32;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(s[t2][i] - m_new);
-        ls += p;
-        pf[t2 * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(p);
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vb + dim * VP + ks * 16 + hh * 8);
+          o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[g][dt], 0, 0, 0);
+        }
       }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-
-    // ---- O^T += V^T P^T; slot s of k-step ks is key ks*16 + 8*(s/4) + 4*hh + (s%4)
-#pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt) {
-      const uint16_t* vrow = Vt + (dt * 32 + l32) * VT_LD;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ks * 16 + 4 * hh);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ks * 16 + 8 + 4 * hh);
-        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks],
-                                                        o[dt], 0, 0, 0);
-      }
+      // keep the two query groups apart: their score blocks are never live together
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (t + 1 < ntiles) stage(buf ^ 1);
+    __syncthreads();
   }
 
-  // ---- normalise and store: element i of o[dt] is dim dt*32 + 8*(i/4) + 4*hh + (i%4)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  if (q < N) {
-    uint16_t* dst = out + (static_cast<size_t>(b) * N + q) * D + head * HD;
+  // ---- normalise and store: element i of o[g][dt] is dim 32 dt + 8(i/4) + 4 hh + i%4
 #pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt)
+  for (int g = 0; g < 2; ++g) {
+    const int q = blockIdx.x * BQ + wave * 64 + g * 32 + l32;
+    const float inv = 1.0f / (l_run[g] + __shfl_xor(l_run[g], 32));
+    if (q < N) {
+      uint16_t* dst = out + (static_cast<size_t>(b) * N + q) * D + head * HD;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv);
-        pk[1] = pack_bf16x2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g4 + 4 * hh) = pk;
-      }
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[g][dt][4 * g4] * inv, o[g][dt][4 * g4 + 1] * inv);
+          pk[1] = pack_bf16x2(o[g][dt][4 * g4 + 2] * inv, o[g][dt][4 * g4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g4 + 4 * hh) = pk;
+        }
+    }
   }
 }
 
@@ -291,11 +399,13 @@ hipError_t launch_attention_bf16(const uint16_t* qkv, uint16_t* out, int B, int 
   if (B <= 0 || N <= 0) return hipSuccess;
   const RopeFreq fr = make_freq(head_dim, r.theta);
   const float qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
-  const dim3 grid((N + 127) / 128, n_head, B);
+  const FastDiv dhw = make_fastdiv(static_cast<uint32_t>(r.gh * r.gw));
+  const FastDiv dw = make_fastdiv(static_cast<uint32_t>(r.gw));
+  const dim3 grid((N + 255) / 256, n_head, B);
   if (head_dim == 64)
-    attn_bf16_kernel<64><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale);
+    attn_bf16_kernel<64><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale, dhw, dw);
   else if (head_dim == 32)
-    attn_bf16_kernel<32><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale);
+    attn_bf16_kernel<32><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale, dhw, dw);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
