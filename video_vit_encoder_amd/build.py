@@ -37,9 +37,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libjepa)")
 
 
+# per-source extra flags
+EXTRA = {}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature: harmless
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

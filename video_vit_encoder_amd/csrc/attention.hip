@@ -170,7 +170,7 @@ template <int HD>
 __global__ __launch_bounds__(256, 2)
 void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, int N,
                       int H, const int32_t* __restrict__ ids, RopeSpec r, RopeFreq fr,
-                      float qscale, FastDiv dhw, FastDiv dw) {
+                      float qscale, FastDiv dhw, FastDiv dw, int nqb) {
   constexpr int D3 = 2 * ((HD / 3) / 2);
   constexpr int MF = D3 / 2;
   constexpr int BQ = 256, BKV = 64, NT = 256;
@@ -188,7 +188,12 @@ void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
-  const int head = blockIdx.y, b = blockIdx.z;
+  // Work-groups are dealt to the 8 XCDs round-robin; renumber them so that the query
+  // blocks of one (clip, head), which read the same keys and values, share an XCD's L2.
+  int wg = blockIdx.x;
+  if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
+  const int qblk = wg % nqb, bh = wg / nqb;
+  const int head = bh % H, b = bh / H;
   const int D = H * HD, ld = 3 * D;
   const int ntot = r.gt * r.gh * r.gw;
   const uint16_t* base = qkv + static_cast<size_t>(b) * N * ld + head * HD;
@@ -206,7 +211,7 @@ void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o
   bf16x8 qf[2][KS];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int q = blockIdx.x * BQ + wave * 64 + g * 32 + l32;
+    const int q = qblk * BQ + wave * 64 + g * 32 + l32;
     const int qr = min(q, N - 1);
     int id = ids ? ids[qr] : qr;
     id = min(max(id, 0), ntot - 1);
@@ -368,7 +373,7 @@ void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o
   // ---- normalise and store: element i of o[g][dt] is dim 32 dt + 8(i/4) + 4 hh + i%4
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int q = blockIdx.x * BQ + wave * 64 + g * 32 + l32;
+    const int q = qblk * BQ + wave * 64 + g * 32 + l32;
     const float inv = 1.0f / (l_run[g] + __shfl_xor(l_run[g], 32));
     if (q < N) {
       uint16_t* dst = out + (static_cast<size_t>(b) * N + q) * D + head * HD;
@@ -401,11 +406,12 @@ hipError_t launch_attention_bf16(const uint16_t* qkv, uint16_t* out, int B, int 
   const float qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
   const FastDiv dhw = make_fastdiv(static_cast<uint32_t>(r.gh * r.gw));
   const FastDiv dw = make_fastdiv(static_cast<uint32_t>(r.gw));
-  const dim3 grid((N + 255) / 256, n_head, B);
+  const int nqb = (N + 255) / 256;
+  const dim3 grid(nqb * n_head * B);
   if (head_dim == 64)
-    attn_bf16_kernel<64><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale, dhw, dw);
+    attn_bf16_kernel<64><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale, dhw, dw, nqb);
   else if (head_dim == 32)
-    attn_bf16_kernel<32><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale, dhw, dw);
+    attn_bf16_kernel<32><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale, dhw, dw, nqb);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

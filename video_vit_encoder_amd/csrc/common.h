@@ -8,8 +8,10 @@ namespace jepa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -41,6 +43,27 @@ __device__ __forceinline__ Thw decode_id(int id, int gh, int gw) {
   r.h = rem / gw;
   r.w = rem - r.h * gw;
   return r;
+}
+
+// HBM/L2 -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane p of the wave
+// writes LDS bytes [lds + 16p, lds + 16p + 16) from base + voff.  Issued through inline
+// asm so that the kernel, not the compiler, decides how many of these may still be in
+// flight at each barrier (s_waitcnt vmcnt).  lds must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  // both operands live in SGPRs: make their uniformity explicit
+  // (readfirstlane returns int: widen through uint32_t, never by sign extension)
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b & 0xFFFFFFFFu)));
+  const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(reinterpret_cast<const void*>(bs))
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p)));
 }
 
 }  // namespace jepa

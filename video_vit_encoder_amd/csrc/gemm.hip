@@ -31,20 +31,6 @@ namespace jepa {
 
 enum { EPI_STORE = 0, EPI_GELU = 1, EPI_RESIDUAL = 2 };
 
-// HBM/L2 -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane p of the wave
-// writes LDS bytes [lds + 16p, lds + 16p + 16) from base + voff.  Issued through inline
-// asm so that the kernel, not the compiler, decides how many of these may still be in
-// flight at each barrier (s_waitcnt vmcnt).  lds must be wave-uniform.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
-               : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p)));
-}
-
 // GELU with erf from Abramowitz & Stegun 7.1.26 (|error of erf| <= 1.5e-7, far below
 // the bf16 rounding of the output): erf(x) = 1 - t(a1 + t(a2 + ...)) exp(-x^2),
 // t = 1 / (1 + p|x|), odd in x.
