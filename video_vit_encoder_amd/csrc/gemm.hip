@@ -5,15 +5,16 @@
 //
 // bf16 path (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
 //   * a workgroup of 8 wavefronts (2 per SIMD, so one wave's MFMAs cover the other's
-//     LDS reads) computes 256 (rows of A) x 128 (rows of W) output tiles; wave (wm, wn)
-//     owns 64 x 64 of a tile as 4 x 4 blocks of 16 x 16;
+//     LDS reads) computes 256 (rows of A) x 128 or x 256 (rows of W) output tiles, the
+//     wider tile wherever it fills whole rounds of the CUs (it halves the LDS reads per
+//     MFMA); each wave owns 64 x 64 or 128 x 64 of a tile as blocks of 16 x 16;
 //   * the kernel is persistent: one workgroup per CU walks its tiles, and the K-slabs of
-//     all its tiles form one stream through a 3-stage ring of LDS buffers.  Slabs are
-//     64 deep and are filled by global_load_lds_dwordx4 (HBM/L2 -> LDS, no register
-//     staging) two stages ahead of the MFMAs, so the next tile's first slabs load
+//     all its tiles form one stream through a ring of 3 (64-deep slabs) or 4 (32-deep)
+//     LDS buffers, filled by global_load_lds_dwordx4 (HBM/L2 -> LDS, no register
+//     staging) STAGES - 1 slabs ahead of the MFMAs, so the next tile's first slabs load
 //     while the current tile's epilogue runs; one barrier per slab;
-//   * LDS rows are 128 B (64 bf16); the 16-byte chunk c of row r lives at chunk
-//     c ^ (r & 7).  A DMA instruction writes 64 consecutive 16-byte slots (8 rows), so
+//   * LDS rows are 128 B (64-deep slabs) or 64 B (32-deep); the 16-byte chunk c of row r
+//     lives at chunk c ^ (r & 7), resp. c ^ ((r >> 2) & 3).  A DMA instruction writes 64 consecutive 16-byte slots (8 rows), so
 //     lane p of it fetches the global chunk that belongs in slot p.  With the 16x16x32
 //     operand pattern (16 rows x 4 chunks per read) this layout keeps ds_read_b128 near
 //     the LDS peak on gfx950;
@@ -45,28 +46,45 @@ __device__ __forceinline__ float gelu_as(float z) {
   return 0.5f * z * (1.0f + copysignf(e, z));
 }
 
-namespace gemm {
-constexpr int BM = 256, BN = 128, BK = 64, STAGES = 3;
-constexpr int NWAVES = 8, NT = NWAVES * 64;    // 2 waves per SIMD
-constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 48 KB
-constexpr int A_LOADS = A_BYTES / 16 / NT;      // 4 DMA instructions per thread
-constexpr int B_LOADS = B_BYTES / 16 / NT;      // 2
-constexpr int LOADS = A_LOADS + B_LOADS;
-constexpr int WM = 64, WN = 64;                 // wave tile
-constexpr int FI = WM / 16, FJ = WN / 16;       // 16x16 blocks per wave
-}  // namespace gemm
+// One tile configuration: BM x BN output tiles, K slabs of BK through STAGES LDS
+// buffers, WGM x WGN waves (2 per SIMD) of WM x WN.
+template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_, int WG_PER_CU_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int WG_PER_CU = WG_PER_CU_;
+  static constexpr int WGM = WGM_, WGN = WGN_, NWAVES = WGM * WGN, NT = NWAVES * 64;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int FI = WM / 16, FJ = WN / 16;        // 16x16 blocks per wave
+  static constexpr int ROWB = BK * 2;                     // LDS bytes per tile row
+  static constexpr int RPI = 1024 / ROWB;                 // rows per 1 KB DMA instruction
+  static constexpr int CPR = ROWB / 16;                   // 16-byte chunks per row
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // DMA instructions per thread
+  static constexpr int B_LOADS = B_BYTES / 1024 / NWAVES;
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static constexpr int LDS = STAGES * STAGE_BYTES;
+  static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && B_LOADS * NWAVES * 1024 == B_BYTES, "DMA split");
+  static_assert(BK == 64 || BK == 32, "row swizzle");
+  // swizzle key of tile row r: the 16-byte chunk c of row r sits at chunk c ^ key(r)
+  __device__ static int key(int r) { return BK == 64 ? (r & 7) : ((r >> 2) & 3); }
+};
+// 256 x 128, BK 64, 3 stages (144 KB), 4 x 2 waves of 64 x 64, one workgroup per CU
+using CfgBig = GemmCfg<256, 128, 64, 3, 4, 2, 1>;
 
-template <int EPI, bool OUT_F32>
-__global__ __launch_bounds__(gemm::NT)
+template <class C, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(C::NT)
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                       const float* __restrict__ bias, void* __restrict__ Cv, int M, int N, int K) {
-  using namespace gemm;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STAGES = C::STAGES, NWAVES = C::NWAVES;
+  constexpr int FI = C::FI, FJ = C::FJ, WM = C::WM, WN = C::WN;
+  constexpr int A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS;
+  constexpr int STAGE_BYTES = C::STAGE_BYTES, A_BYTES = C::A_BYTES, ROWB = C::ROWB;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA LDS bases
-  const int wm = wave >> 1, wn = wave & 1;                     // 4 x 2 waves of 64 x 64
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int q16 = lane >> 4, l16 = lane & 15;
 
   const int tiles_n = N / BN;
@@ -76,19 +94,41 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   const int KT = K / BK;
   const int total = n_my * KT;
 
-  // Tile of round i.  In full rounds the workgroups of XCD x = b % 8 take consecutive
-  // tiles (n fastest); the last, partial round keeps the plain order.
+  // Tile of round i.  Work-groups are dealt to the 8 XCDs round-robin (b % 8).  When the
+  // grid fills every CU and the tile grid splits evenly, the SPX = G/8 workgroups of XCD x
+  // work, round by round, on a block of SPX/8 row tiles x 8 column tiles of its share:
+  // they share those rows of A and columns of W in the XCD's L2, and the rows stay
+  // resident while the rounds walk the columns.  Otherwise: consecutive tiles per XCD
+  // in full rounds, plain order in the last, partial round.
+  const int tiles_m = (M + BM - 1) / BM;
+  const int spx = G >> 3, btm = spx >> 3;           // workgroups per XCD, block rows
+  const bool blocked = (G & 63) == 0 && btm > 0 && tiles_m % (8 * btm) == 0 && tiles_n % 8 == 0;
   auto tile_of = [&](int i, int& m0, int& n0) {
-    int t = i * G + b;
-    if ((G & 7) == 0 && (i + 1) * G <= tiles) t = i * G + (b & 7) * (G >> 3) + (b >> 3);
-    const int tm = t / tiles_n;
+    int tm, tn;
+    if (blocked) {
+      const int x = b & 7, j = b >> 3;              // XCD, slot in it
+      const int k = i * spx + j;                    // position in the XCD's sequence
+      const int rows = tiles_m / 8;                 // row tiles per XCD
+      const int nb = k / spx, w = k % spx;          // column block, slot in it
+      const int grp = nb / (tiles_n / 8);           // which group of btm row tiles
+      tm = x * rows + grp * btm + w / 8;
+      tn = (nb % (tiles_n / 8)) * 8 + (w % 8);
+    } else {
+      int t = i * G + b;
+      if ((G & 7) == 0 && (i + 1) * G <= tiles) t = i * G + (b & 7) * (G >> 3) + (b >> 3);
+      tm = t / tiles_n;
+      tn = t - tm * tiles_n;
+    }
     m0 = tm * BM;
-    n0 = (t - tm * tiles_n) * BN;
+    n0 = tn * BN;
   };
 
-  // DMA mapping: instruction q of wave w fills rows [8g, 8g+8) of a tile, g = q*8 + w;
-  // lane p -> row 8g + p/8, slot p%8 holding logical chunk (p%8) ^ (p/8).
-  const int prow = lane >> 3, pchunk = (lane & 7) ^ prow;
+  // DMA mapping: instruction q of wave w fills rows [RPI g, RPI (g+1)) of a tile,
+  // g = q*NWAVES + w; lane p -> row RPI g + p/CPR, slot p%CPR holding logical chunk
+  // (p%CPR) ^ key(row) (the key of the row depends on p/CPR only, RPI being a multiple
+  // of its period).
+  const int prow = lane / C::CPR;
+  const int pchunk = (lane % C::CPR) ^ C::key(prow);
   const uint32_t smem_base = lds_addr(smem);
 
   // Issue state: the next slab to load (tile it_iss, slab kt_iss) and the byte offsets
@@ -100,12 +140,12 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     tile_of(it, m0, n0);
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) {
-      const int r = (q * NWAVES + wave) * 8 + prow;
+      const int r = (q * NWAVES + wave) * C::RPI + prow;
       a_row[q] = static_cast<uint32_t>(static_cast<size_t>(min(m0 + r, M - 1)) * K * 2) + pchunk * 16;
     }
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q) {
-      const int r = (q * NWAVES + wave) * 8 + prow;
+      const int r = (q * NWAVES + wave) * C::RPI + prow;
       b_row[q] = static_cast<uint32_t>(static_cast<size_t>(n0 + r) * K * 2) + pchunk * 16;
     }
   };
@@ -132,11 +172,49 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
 #pragma unroll
   for (int j = 0; j < FJ; ++j) brow[j] = wn * WN + j * 16 + l16;
 
-  if (total > 0) {
-    set_rows(0);
-    issue_next();
+  // Operand fragments of slab s, k-step ks, from LDS.
+  auto load_frags = [&](int s_, int ks, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
+    const unsigned char* st = smem + (s_ % STAGES) * STAGE_BYTES;
+    const int ch = ks * 4 + q16;
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(st + arow[i] * ROWB + ((ch ^ C::key(arow[i])) << 4));
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(st + A_BYTES + brow[j] * ROWB + ((ch ^ C::key(brow[j])) << 4));
+  };
+  // Wait until slab s_ has landed in LDS for every lane of the workgroup: at most
+  // min(total - 1, s_ + STAGES - 3) - s_ later slabs may still be in flight.
+  auto wait_slab = [&](int s_) __attribute__((always_inline)) {
+    const int ahead = min(total - 1 - s_, STAGES - 3);
+    if (ahead >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS) : "memory");
+    else if (ahead == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  // Prologue: STAGES - 2 slabs in flight, slab 0 landed, its first fragments loaded.
+  // In the loop, slab s + 1's barrier and first fragment loads come before slab s's last
+  // k-step of MFMAs, so LDS latency hides behind MFMAs; the DMA issued after that barrier
+  // (slab s + STAGES - 2) reuses the buffer of slab s - 2, whose reads all completed
+  // before the barrier.
+  constexpr int KSTEPS = BK / 32;
+#pragma unroll
+  for (int p = 0; p < STAGES - 2; ++p) {
+    if (p < total) {
+      if (p == 0) set_rows(0);
+      issue_next();
+    }
   }
-  if (total > 1) issue_next();
+  bf16x8 af[2][FI], bfr[2][FJ];
+  if (total > 0) {
+    wait_slab(0);
+    if (STAGES - 2 < total) issue_next();
+    load_frags(0, 0, af[0], bfr[0]);
+  }
   int s = 0;  // position in this workgroup's slab stream
   for (int it = 0; it < n_my; ++it) {
     f32x4 acc[FI][FJ];
@@ -146,31 +224,28 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
       for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int kt = 0; kt < KT; ++kt, ++s) {
-      // slab s has landed once at most one later slab (LOADS DMAs) is still in flight
-      if (s + 1 < total)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(gemm::LOADS) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (s + 2 < total) issue_next();
-      const unsigned char* st = smem + (s % STAGES) * STAGE_BYTES;
-      const uint16_t* As = reinterpret_cast<const uint16_t*>(st);
-      const uint16_t* Bs = reinterpret_cast<const uint16_t*>(st + A_BYTES);
 #pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) {
-        const int ch = ks * 4 + q16;
-        bf16x8 af[FI], bfr[FJ];
-#pragma unroll
-        for (int i = 0; i < FI; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(As + arow[i] * BK + ((ch ^ (arow[i] & 7)) << 3));
-#pragma unroll
-        for (int j = 0; j < FJ; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + brow[j] * BK + ((ch ^ (brow[j] & 7)) << 3));
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        if (ks + 1 < KSTEPS) {
+          load_frags(s, ks + 1, af[nxt], bfr[nxt]);
+        } else if (s + 1 < total) {
+          wait_slab(s + 1);
+          if (s + STAGES - 1 < total) issue_next();
+          load_frags(s + 1, 0, af[nxt], bfr[nxt]);
+        }
 #pragma unroll
         for (int i = 0; i < FI; ++i)
 #pragma unroll
           for (int j = 0; j < FJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+        if (KSTEPS == 1 || ks + 1 == KSTEPS) {
+          // the fragments loaded above for slab s + 1 move into slot 0
+#pragma unroll
+          for (int i = 0; i < FI; ++i) af[0][i] = af[nxt][i];
+#pragma unroll
+          for (int j = 0; j < FJ; ++j) bfr[0][j] = bfr[nxt][j];
+        }
       }
     }
 
@@ -195,17 +270,17 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
         }
         const size_t off = static_cast<size_t>(row) * N + col;
         if (EPI == EPI_RESIDUAL) {
-          f32x4* C = reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off);
-          f32x4 c = *C;
+          f32x4* Cp = reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off);
+          f32x4 c = *Cp;
           c[0] += v[0]; c[1] += v[1]; c[2] += v[2]; c[3] += v[3];
-          *C = c;
+          *Cp = c;
         } else if (OUT_F32) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off) = f32x4{v[0], v[1], v[2], v[3]};
         } else {
-          u32x2 p;
-          p[0] = pack_bf16x2(v[0], v[1]);
-          p[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cv) + off) = p;
+          u32x2 pk;
+          pk[0] = pack_bf16x2(v[0], v[1]);
+          pk[1] = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cv) + off) = pk;
         }
       }
     }
@@ -224,38 +299,42 @@ static int num_cus() {
   return n;
 }
 
-template <int EPI, bool OUT_F32>
-static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float* bias, void* C,
+template <class C, int EPI, bool OUT_F32>
+static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float* bias, void* Cp,
                               int M, int N, int K, hipStream_t s) {
-  using namespace gemm;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI, OUT_F32>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       STAGES * STAGE_BYTES);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI, OUT_F32>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  const dim3 grid(min(tiles, num_cus()));
-  gemm_bf16_kernel<EPI, OUT_F32><<<grid, NT, STAGES * STAGE_BYTES, s>>>(A, W, bias, C, M, N, K);
+  const int tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
+  const dim3 grid(min(tiles, C::WG_PER_CU * num_cus()));
+  gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, C::LDS, s>>>(A, W, bias, Cp, M, N, K);
   return hipGetLastError();
+}
+
+template <class C>
+static hipError_t gemm_dispatch(const uint16_t* A, const uint16_t* W, const float* bias, void* Cp,
+                                int M, int N, int K, int epi, int out_f32, hipStream_t s) {
+  if (epi == EPI_RESIDUAL) return gemm_launch<C, EPI_RESIDUAL, true>(A, W, bias, Cp, M, N, K, s);
+  if (epi == EPI_GELU)
+    return out_f32 ? gemm_launch<C, EPI_GELU, true>(A, W, bias, Cp, M, N, K, s)
+                   : gemm_launch<C, EPI_GELU, false>(A, W, bias, Cp, M, N, K, s);
+  return out_f32 ? gemm_launch<C, EPI_STORE, true>(A, W, bias, Cp, M, N, K, s)
+                 : gemm_launch<C, EPI_STORE, false>(A, W, bias, Cp, M, N, K, s);
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C,
                             int M, int N, int K, int epi, int out_f32, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (N % gemm::BN || K % gemm::BK) return hipErrorInvalidValue;
+  if (N % 128 || K % 64) return hipErrorInvalidValue;
   // the DMA addressing uses 32-bit byte offsets
   if (static_cast<size_t>(M) * K * 2 >= (size_t(1) << 31) ||
       static_cast<size_t>(N) * K * 2 >= (size_t(1) << 31))
     return hipErrorInvalidValue;
-  if (epi == EPI_RESIDUAL) return gemm_launch<EPI_RESIDUAL, true>(A, W, bias, C, M, N, K, s);
-  if (epi == EPI_GELU)
-    return out_f32 ? gemm_launch<EPI_GELU, true>(A, W, bias, C, M, N, K, s)
-                   : gemm_launch<EPI_GELU, false>(A, W, bias, C, M, N, K, s);
-  return out_f32 ? gemm_launch<EPI_STORE, true>(A, W, bias, C, M, N, K, s)
-                 : gemm_launch<EPI_STORE, false>(A, W, bias, C, M, N, K, s);
+  return gemm_dispatch<CfgBig>(A, W, bias, C, M, N, K, epi, out_f32, s);
 }
 
 // ---------------------------------------------------------------- fp32 path
