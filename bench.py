@@ -10,10 +10,11 @@ N(0, 0.01), LayerNorm 1/0; the clips are uniform uint8 (no dataset, no checkpoin
 
 Prints one JSON line.  ``value`` is encoder tokens/s over the K timed steps (HIP events
 on the stream the library launches on, bracketed by device synchronisation).  Beside it:
-  * ``roofline``: the dominant kernel (the largest share of a step's time, its launch
-    durations measured here with HIP events through the library's stand-alone entry
-    points at the step's shapes), its algorithmic TFLOP/s or GB/s against the MI355X
-    peak (bf16 dense MFMA 2500 TFLOP/s, HBM 8000 GB/s);
+  * ``roofline``: the dominant kernel (the largest share of a step's time), its
+    algorithmic TFLOP/s or GB/s per launch against the MI355X peak (bf16 dense MFMA
+    2500 TFLOP/s, HBM 8000 GB/s).  Launch durations come from a second pass of K
+    forwards in which the library records a HIP event pair around every launch on the
+    stream it launches on (jepa_timing_begin / jepa_timing_end);
   * ``kernels``: the same figures for every kernel class of the step;
   * ``cpu_baseline``: the float64 oracle timed on the host on one clip through a few
     layers, scaled to the 24-layer forward (a reported baseline, not a target).
@@ -49,75 +50,77 @@ def forward_flops(B, N, D, F, L, feat=1536):
     return 2 * B * N * feat * D + L * (gemm + attn)
 
 
-def time_launches(fn, reps, warm=3):
-    """Average duration (ms) of fn() over reps launches, HIP events on the current stream."""
-    import torch
-    for _ in range(warm):
-        fn()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
-        fn()
-    e.record()
-    e.synchronize()
-    return s.elapsed_time(e) / reps
-
-
-def kernel_breakdown(w, B, N, D, F, H, hd, L):
-    """Per-kernel launch durations at the step's shapes, through the C ABI."""
-    import torch
-    import video_vit_encoder_amd as J
-    dev = torch.device("cuda:0")
+def kernel_work(B, N, D, F, L, feat=1536):
+    """Algorithmic work per step of each kernel class: (bound, FLOPs or bytes per step)."""
     M = B * N
-    g = torch.Generator(device=dev).manual_seed(0)
+    ln_bytes = 2 * L * (M * D * (4 + 2) + 2 * D * 4) + (M * D * (4 + 4) + 2 * D * 4)
+    return {
+        "patchify": ("hbm", M * feat * (1 + 2)),          # u8 pixels in, bf16 rows out
+        "gemm_embed": ("mfma", 2 * M * feat * D),
+        "layernorm": ("hbm", ln_bytes),                  # 2L of fp32 -> bf16, final fp32 -> fp32
+        "gemm_qkv": ("mfma", L * 2 * M * D * 3 * D),
+        "attention": ("mfma", L * 4 * B * N * N * D),
+        "gemm_out": ("mfma", L * 2 * M * D * D),
+        "gemm_up": ("mfma", L * 2 * M * D * F),
+        "gemm_down": ("mfma", L * 2 * M * F * D),
+    }
 
-    def rn(*shape, scale=1.0, dtype=torch.bfloat16):
-        return (torch.randn(*shape, generator=g, device=dev) * scale).to(dtype)
 
-    x = rn(M, D, dtype=torch.float32)
-    h = rn(M, D)
-    lw, lb = torch.ones(D, device=dev), torch.zeros(D, device=dev)
-    Wqkv, bqkv = rn(3 * D, D, scale=0.02), rn(3 * D, scale=0.01, dtype=torch.float32)
-    Wo, bo = rn(D, D, scale=0.02), rn(D, scale=0.01, dtype=torch.float32)
-    Wu, bu = rn(F, D, scale=0.02), rn(F, scale=0.01, dtype=torch.float32)
-    Wd, bd = rn(D, F, scale=0.02), rn(D, scale=0.01, dtype=torch.float32)
-    qkv = torch.empty(M, 3 * D, device=dev, dtype=torch.bfloat16)
-    o = rn(M, D)
-    gg = torch.empty(M, F, device=dev, dtype=torch.bfloat16)
-    grid = w["grid"]
-    J.jepa_linear(h, Wqkv, bqkv, qkv, J.JEPA_EPI_STORE)
-    J.jepa_linear(h, Wu, bu, gg, J.JEPA_EPI_GELU)
-    reps = 20
-    ks = {}
-    ks["layernorm"] = dict(
-        ms=time_launches(lambda: J.jepa_layernorm(x, lw, lb, 1e-6, h), reps), per_step=2 * L + 1,
-        bound="hbm", bytes=M * D * (4 + 2) + 2 * D * 4)
-    ks["gemm_qkv"] = dict(
-        ms=time_launches(lambda: J.jepa_linear(h, Wqkv, bqkv, qkv, J.JEPA_EPI_STORE), reps),
-        per_step=L, bound="mfma", flops=2 * M * D * 3 * D)
-    ks["attention"] = dict(
-        ms=time_launches(lambda: J.jepa_attention(qkv, o, B, N, H, hd, None, grid, "tiled"), reps),
-        per_step=L, bound="mfma", flops=4 * B * N * N * D)
-    ks["gemm_out_residual"] = dict(
-        ms=time_launches(lambda: J.jepa_linear(o, Wo, bo, x, J.JEPA_EPI_RESIDUAL), reps),
-        per_step=L, bound="mfma", flops=2 * M * D * D)
-    ks["gemm_ffn_up_gelu"] = dict(
-        ms=time_launches(lambda: J.jepa_linear(h, Wu, bu, gg, J.JEPA_EPI_GELU), reps),
-        per_step=L, bound="mfma", flops=2 * M * D * F)
-    ks["gemm_ffn_down_residual"] = dict(
-        ms=time_launches(lambda: J.jepa_linear(gg, Wd, bd, x, J.JEPA_EPI_RESIDUAL), reps),
-        per_step=L, bound="mfma", flops=2 * M * F * D)
-    for k, v in ks.items():
-        if v["bound"] == "mfma":
-            v["tflops"] = v["flops"] / (v["ms"] * 1e-3) / 1e12
-            v["frac"] = v["tflops"] / PEAK_BF16_TFLOPS
-        else:
-            v["gbs"] = v["bytes"] / (v["ms"] * 1e-3) / 1e9
-            v["frac"] = v["gbs"] / PEAK_HBM_GBS
-        v["ms_per_step"] = v["ms"] * v["per_step"]
+def kernel_timing(J, run_step, steps, work):
+    """Per-class launch durations over `steps` forwards, from HIP event pairs the library
+    records around each launch on the stream it launches on."""
+    import torch
     torch.cuda.synchronize()
-    return ks
+    J.jepa_timing_begin(64 * steps)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run_step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    rec = J.jepa_timing_end()
+    ks = {}
+    for name, (bound, per_step) in work.items():
+        ms, n = rec[name]
+        if n == 0:
+            continue
+        per_launch = per_step * steps / n
+        avg = ms / n
+        k = {"bound": bound, "launches_per_step": n // steps, "avg_ms": round(avg, 5),
+             "ms_per_step": round(ms / steps, 4)}
+        if bound == "mfma":
+            k["flops_per_launch"] = int(per_launch)
+            k["tflops"] = round(per_launch / (avg * 1e-3) / 1e12, 2)
+            k["frac"] = round(k["tflops"] / PEAK_BF16_TFLOPS, 4)
+        else:
+            k["bytes_per_launch"] = int(per_launch)
+            k["gbs"] = round(per_launch / (avg * 1e-3) / 1e9, 1)
+            k["frac"] = round(k["gbs"] / PEAK_HBM_GBS, 4)
+        ks[name] = k
+    return ks, wall * 1e3
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch of kernel class `kind` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (profiles/hbm_traffic.json), or None when there is no entry or the
+    kernel's sources changed since the counters were taken (source hash differs)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        tab = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kind)
+    if not isinstance(ent, dict):
+        return None
+    h = hashlib.sha256()
+    for fn in ent["sources"]:
+        try:
+            h.update(open(os.path.join(ROOT, "video_vit_encoder_amd", "csrc", fn), "rb").read())
+        except OSError:
+            return None
+    if h.hexdigest() != ent["source_sha256"]:
+        return None
+    return ent["read_bytes"] + ent["write_bytes"]
 
 
 def cpu_baseline(w, W, clips, budget_layers=12):
@@ -157,6 +160,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a plain 256 MiB device-to-device copy 3 times, the "
+                         "reference for scaling HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -181,6 +187,13 @@ def main():
     enc.set_weights(W)
     clip_d = torch.from_numpy(clips).to(dev)
     out = torch.empty((B, N, D), dtype=torch.float32, device=dev)
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log("warmup")
     for _ in range(args.warmup):
         enc.encode(clip_d, out=out)
@@ -206,22 +219,23 @@ def main():
 
     roof, kernels = None, None
     if not args.no_kernels:
-        log("per-kernel launch timing")
-        kernels = kernel_breakdown(w, B, N, D, F, H, D // H, L)
+        log(f"per-kernel launch timing over {args.steps} more steps (HIP events in the library)")
+        kernels, prof_ms = kernel_timing(J, lambda: enc.encode(clip_d, out=out), args.steps,
+                                         kernel_work(B, N, D, F, L))
         dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
         k = kernels[dom]
         if k["bound"] == "mfma":
-            roof = {"kernel": dom, "bound": "mfma", "achieved": round(k["tflops"], 2),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(k["frac"], 4),
-                    "traffic": None, "launch_ms": round(k["ms"], 4),
-                    "flops_per_launch": k["flops"]}
+            roof = {"kernel": dom, "bound": "mfma", "achieved": k["tflops"],
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": k["frac"],
+                    "traffic": measured_traffic(dom), "launch_ms": k["avg_ms"],
+                    "flops_per_launch": k["flops_per_launch"]}
         else:
-            roof = {"kernel": dom, "bound": "hbm", "achieved": round(k["gbs"], 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(k["frac"], 4),
-                    "traffic": None, "launch_ms": round(k["ms"], 4),
-                    "bytes_per_launch": k["bytes"]}
-        kernels = {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                   for n, v in kernels.items()}
+            roof = {"kernel": dom, "bound": "hbm", "achieved": k["gbs"],
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": k["frac"],
+                    "traffic": measured_traffic(dom), "launch_ms": k["avg_ms"],
+                    "bytes_per_launch": k["bytes_per_launch"]}
+        log(f"dominant kernel {dom}: {k['avg_ms'] * 1e3:.1f} us/launch, frac {k['frac']:.3f}; "
+            f"timed pass {prof_ms:.3f} ms/step (wall)")
 
     cpu = None
     if not args.no_cpu_baseline:

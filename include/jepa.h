@@ -224,6 +224,36 @@ int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, 
                    int head_dim, const int32_t* ids_dev, int gt, int gh, int gw, int layout,
                    float theta, int ref_grid, void* stream);
 
+/* ------------------------------------------------------------------ kernel timing */
+
+/* Kernel classes of the forwards, for jepa_timing_end. */
+enum jepa_kernel_class {
+  JEPA_KC_PATCHIFY = 0,   /* u8 clip -> normalised tubelet rows                     */
+  JEPA_KC_GEMM_EMBED = 1, /* patch / predictor embedding and predictor output GEMMs  */
+  JEPA_KC_LAYERNORM = 2,  /* LN1, LN2 and the final norm                            */
+  JEPA_KC_GEMM_QKV = 3,   /* fused QKV projection                                   */
+  JEPA_KC_ATTENTION = 4,  /* RoPE-on-load flash attention                           */
+  JEPA_KC_GEMM_OUT = 5,   /* attention output projection + residual                 */
+  JEPA_KC_GEMM_UP = 6,    /* FFN up-projection + GELU                               */
+  JEPA_KC_GEMM_DOWN = 7,  /* FFN down-projection + residual                         */
+  JEPA_KC_OTHER = 8,      /* row gathers, fills and device copies                   */
+  JEPA_KC_COUNT = 9
+};
+
+/* Per-launch timing of the forwards, for measurement harnesses.  After
+ * jepa_timing_begin(cap), every jepa_encode, jepa_encode_tokens and jepa_predict
+ * records a HIP event pair on its own stream around each kernel launch, for at most
+ * `cap` launches per class (later launches are not recorded).  Process-wide state, not
+ * thread-safe; the events add a small gap between launches, so time throughput with
+ * timing off.  Errors: JEPA_ERR_ARG (cap < 1, or timing already on), JEPA_ERR_HIP. */
+int jepa_timing_begin(int cap);
+
+/* Wait for every recorded event, write per class the summed launch duration in ms
+ * (ms[JEPA_KC_COUNT]) and the number of recorded launches (launches[JEPA_KC_COUNT]),
+ * release the events and turn timing off.  Either pointer may be NULL.
+ * Errors: JEPA_ERR_STATE (timing is off), JEPA_ERR_HIP. */
+int jepa_timing_end(double* ms, int* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -108,3 +108,11 @@ def test_one_hip_runtime_in_the_process():
                          cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_timing_state_errors():
+    lib = J.load()
+    # neither call reaches the GPU: begin rejects cap < 1 before creating events, end
+    # rejects a timing session that was never begun
+    assert lib.jepa_timing_begin(0) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_timing_end(None, None) == _lib.JEPA_ERR_STATE

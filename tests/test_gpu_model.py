@@ -239,3 +239,30 @@ def test_encode_errors_leave_output_untouched():
         J.jepa_encoder_set_tensor(enc.handle, "enc.norm.weight", np.ones(767, np.float32))
     assert e.value.status == -4
     assert bool(torch.all(out == 7.0))
+
+
+def test_kernel_timing_counts_every_launch():
+    import torch
+    w = synth.workload("tiny_fp32")
+    banner("kernel timing counts, tiny fp32 encoder x 2 forwards")
+    enc = J.Encoder(768, 2, 12, 3072, dtype="f32", max_rows=32)
+    enc.set_weights(synth.encoder_weights(w["enc"], seed=0, dtype="f32"))
+    clip = u8(synth.clip_u8(0, 1, 4, 64, 64))
+    ref = host(enc.encode(clip))
+    J.jepa_timing_begin(8)
+    try:
+        got = [host(enc.encode(clip)) for _ in range(2)]
+    finally:
+        rec = J.jepa_timing_end()
+    # timing changes no result
+    for g in got:
+        assert np.array_equal(g, ref)
+    per_fwd = {"patchify": 1, "gemm_embed": 1, "layernorm": 2 * 2 + 1, "gemm_qkv": 2,
+               "attention": 2, "gemm_out": 2, "gemm_up": 2, "gemm_down": 2, "other": 0}
+    for k, n in per_fwd.items():
+        ms, cnt = rec[k]
+        assert cnt == min(2 * n, 8), (k, cnt)
+        assert (ms > 0) == (cnt > 0), (k, ms)
+    with pytest.raises(J.JepaError):
+        J.jepa_timing_end()
+    enc.close()

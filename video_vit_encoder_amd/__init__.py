@@ -14,11 +14,11 @@ import numpy as np
 
 from ._lib import (  # noqa: F401
     DTYPES, JEPA_BF16, JEPA_EPI_GELU, JEPA_EPI_RESIDUAL, JEPA_EPI_STORE, JEPA_F32, LAYOUTS,
-    JepaError, header_functions, jepa_attention, jepa_encode, jepa_encode_tokens,
+    KERNEL_CLASSES, JepaError, header_functions, jepa_attention, jepa_encode, jepa_encode_tokens,
     jepa_encoder_config, jepa_encoder_create, jepa_encoder_free, jepa_encoder_set_tensor,
     jepa_layernorm, jepa_linear, jepa_predict, jepa_predictor_config, jepa_predictor_create,
-    jepa_predictor_free, jepa_predictor_set_tensor, jepa_rope3d, jepa_status_str, jepa_version,
-    load,
+    jepa_predictor_free, jepa_predictor_set_tensor, jepa_rope3d, jepa_status_str,
+    jepa_timing_begin, jepa_timing_end, jepa_version, load,
 )
 
 

@@ -24,6 +24,8 @@ JEPA_ERR_NAME, JEPA_ERR_OOM, JEPA_ERR_HIP = -4, -5, -6
 JEPA_ROPE_TILED, JEPA_ROPE_INTERLEAVED = 0, 1
 JEPA_F32, JEPA_BF16 = 0, 1
 JEPA_EPI_STORE, JEPA_EPI_GELU, JEPA_EPI_RESIDUAL = 0, 1, 2
+KERNEL_CLASSES = ("patchify", "gemm_embed", "layernorm", "gemm_qkv", "attention", "gemm_out",
+                  "gemm_up", "gemm_down", "other")
 
 LAYOUTS = {"tiled": JEPA_ROPE_TILED, "interleaved": JEPA_ROPE_INTERLEAVED}
 DTYPES = {"f32": JEPA_F32, "bf16": JEPA_BF16}
@@ -70,6 +72,8 @@ _SIGS = {
     "jepa_layernorm": ([_P, _P, _P, _I, _I, _F, _P, _I, _P], _I),
     "jepa_linear": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
     "jepa_attention": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _I, _I, _F, _I, _P], _I),
+    "jepa_timing_begin": ([_I], _I),
+    "jepa_timing_end": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)], _I),
 }
 
 _lib = None
@@ -307,3 +311,17 @@ def jepa_attention(qkv, out, B: int, N: int, n_head: int, head_dim: int, ids,
     _check("jepa_attention",
            load().jepa_attention(_ptr(qkv), _ptr(out), dt, B, N, n_head, head_dim, _ptr(ids),
                                  gt, gh, gw, LAYOUTS[layout], theta, ref_grid, _stream(stream)))
+
+
+def jepa_timing_begin(cap: int) -> None:
+    """Record a HIP event pair around each launch of the forwards (at most cap per class)."""
+    _check("jepa_timing_begin", load().jepa_timing_begin(cap))
+
+
+def jepa_timing_end() -> dict:
+    """{class name: (summed launch ms, launches)} of the launches recorded since begin."""
+    n = len(KERNEL_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (_I * n)()
+    _check("jepa_timing_end", load().jepa_timing_end(ms, cnt))
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}

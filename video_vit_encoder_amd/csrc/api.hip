@@ -87,6 +87,42 @@ int hip_status(hipError_t e) { return e == hipSuccess ? JEPA_OK : JEPA_ERR_HIP; 
     }                                                \
   } while (0)
 
+// ------------------------------------------------------------------ kernel timing
+
+// Event pairs around the launches of the forwards (jepa_timing_begin / _end).
+struct Timing {
+  bool on = false;
+  int cap = 0;
+  std::vector<hipEvent_t> ev[JEPA_KC_COUNT];  // per class: start, end of launch i at 2i, 2i+1
+  int n[JEPA_KC_COUNT] = {};
+};
+Timing g_timing;
+
+// Records the start event of one launch on construction and its end on destruction.
+struct KTimer {
+  int kc = -1;
+  hipStream_t s;
+  KTimer(int kind, hipStream_t st) : s(st) {
+    if (g_timing.on && g_timing.n[kind] < g_timing.cap) {
+      kc = kind;
+      (void)hipEventRecord(g_timing.ev[kind][2 * g_timing.n[kind]], s);
+    }
+  }
+  ~KTimer() {
+    if (kc >= 0) {
+      (void)hipEventRecord(g_timing.ev[kc][2 * g_timing.n[kc] + 1], s);
+      ++g_timing.n[kc];
+    }
+  }
+};
+
+// A launch of kernel class kc on stream st, timed when timing is on.
+#define JEPA_LAUNCH(kc, st, expr) \
+  do {                            \
+    KTimer _kt((kc), (st));       \
+    JEPA_HIP(expr);               \
+  } while (0)
+
 // One weight tensor: expected shape, kind and device copy.
 struct Tensor {
   std::string name;
@@ -268,22 +304,30 @@ int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_r
   const int hd = D / n_head;
   for (int l = 0; l < n_run; ++l) {
     const BlockIdx& b = blocks[l];
-    JEPA_HIP(launch_layernorm(x, ts.devf(b.ln1w), ts.devf(b.ln1b), M, D, eps, ws.h.p, bf, s));
-    JEPA_HIP(linear(compute, ws.h.p, ts.dev(b.qkvw), ts.devf(b.qkvb), ws.qkv.p, M, 3 * D, D,
-                    JEPA_EPI_STORE, !bf, s));
+    JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
+                launch_layernorm(x, ts.devf(b.ln1w), ts.devf(b.ln1b), M, D, eps, ws.h.p, bf, s));
+    JEPA_LAUNCH(JEPA_KC_GEMM_QKV, s,
+                linear(compute, ws.h.p, ts.dev(b.qkvw), ts.devf(b.qkvb), ws.qkv.p, M, 3 * D, D,
+                       JEPA_EPI_STORE, !bf, s));
     if (bf)
-      JEPA_HIP(launch_attention_bf16(static_cast<const uint16_t*>(ws.qkv.p),
-                                     static_cast<uint16_t*>(ws.o.p), B, N, n_head, hd, ids, rs, s));
+      JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
+                  launch_attention_bf16(static_cast<const uint16_t*>(ws.qkv.p),
+                                        static_cast<uint16_t*>(ws.o.p), B, N, n_head, hd, ids, rs, s));
     else
-      JEPA_HIP(launch_attention_f32(static_cast<const float*>(ws.qkv.p),
-                                    static_cast<float*>(ws.o.p), B, N, n_head, hd, ids, rs, s));
-    JEPA_HIP(linear(compute, ws.o.p, ts.dev(b.outw), ts.devf(b.outb), x, M, D, D,
-                    JEPA_EPI_RESIDUAL, 1, s));
-    JEPA_HIP(launch_layernorm(x, ts.devf(b.ln2w), ts.devf(b.ln2b), M, D, eps, ws.h.p, bf, s));
-    JEPA_HIP(linear(compute, ws.h.p, ts.dev(b.upw), ts.devf(b.upb), ws.g.p, M, F, D,
-                    JEPA_EPI_GELU, !bf, s));
-    JEPA_HIP(linear(compute, ws.g.p, ts.dev(b.downw), ts.devf(b.downb), x, M, D, F,
-                    JEPA_EPI_RESIDUAL, 1, s));
+      JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
+                  launch_attention_f32(static_cast<const float*>(ws.qkv.p),
+                                       static_cast<float*>(ws.o.p), B, N, n_head, hd, ids, rs, s));
+    JEPA_LAUNCH(JEPA_KC_GEMM_OUT, s,
+                linear(compute, ws.o.p, ts.dev(b.outw), ts.devf(b.outb), x, M, D, D,
+                       JEPA_EPI_RESIDUAL, 1, s));
+    JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
+                launch_layernorm(x, ts.devf(b.ln2w), ts.devf(b.ln2b), M, D, eps, ws.h.p, bf, s));
+    JEPA_LAUNCH(JEPA_KC_GEMM_UP, s,
+                linear(compute, ws.h.p, ts.dev(b.upw), ts.devf(b.upb), ws.g.p, M, F, D,
+                       JEPA_EPI_GELU, !bf, s));
+    JEPA_LAUNCH(JEPA_KC_GEMM_DOWN, s,
+                linear(compute, ws.g.p, ts.dev(b.downw), ts.devf(b.downb), x, M, D, F,
+                       JEPA_EPI_RESIDUAL, 1, s));
   }
   return JEPA_OK;
 }
@@ -401,16 +445,18 @@ int jepa_encode(jepa_encoder* enc, const uint8_t* clip_dev, int B, int T, int H,
   const int M = static_cast<int>(B * N);
   const int D = c.embed_dim, bf = c.compute == JEPA_BF16 ? 1 : 0;
   const int feat = c.in_chans * c.tubelet * c.patch * c.patch;
-  JEPA_HIP(launch_patchify(clip_dev, B, T, H, W, enc->ws.a.p, bf, s));
-  JEPA_HIP(linear(c.compute, enc->ws.a.p, enc->ts.dev(enc->pe_w),
-                  static_cast<const float*>(enc->pe_bias_eff.p), out_dev, M, D, feat,
-                  JEPA_EPI_STORE, 1, s));
+  JEPA_LAUNCH(JEPA_KC_PATCHIFY, s, launch_patchify(clip_dev, B, T, H, W, enc->ws.a.p, bf, s));
+  JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
+              linear(c.compute, enc->ws.a.p, enc->ts.dev(enc->pe_w),
+                     static_cast<const float*>(enc->pe_bias_eff.p), out_dev, M, D, feat,
+                     JEPA_EPI_STORE, 1, s));
   const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, c.rope_ref_grid};
   JEPA_TRY(run_blocks(enc->ts, enc->blocks, c.n_layer, enc->ws, out_dev, B, static_cast<int>(N), D,
                       c.ffn_dim, c.n_head, c.ln_eps, nullptr, rs, s));
   if (c.final_norm)
-    JEPA_HIP(launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M, D,
-                              c.ln_eps, out_dev, 0, s));
+    JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
+                launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M,
+                                 D, c.ln_eps, out_dev, 0, s));
   return JEPA_OK;
 }
 
@@ -428,14 +474,16 @@ int jepa_encode_tokens(jepa_encoder* enc, const float* x_dev, int B, int N,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int M = B * N, D = c.embed_dim;
   if (out_dev != x_dev)
-    JEPA_HIP(hipMemcpyAsync(out_dev, x_dev, static_cast<size_t>(M) * D * 4,
-                            hipMemcpyDeviceToDevice, s));
+    JEPA_LAUNCH(JEPA_KC_OTHER, s,
+                hipMemcpyAsync(out_dev, x_dev, static_cast<size_t>(M) * D * 4,
+                               hipMemcpyDeviceToDevice, s));
   const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, c.rope_ref_grid};
   JEPA_TRY(run_blocks(enc->ts, enc->blocks, c.n_layer, enc->ws, out_dev, B, N, D, c.ffn_dim,
                       c.n_head, c.ln_eps, ids_dev, rs, s));
   if (c.final_norm)
-    JEPA_HIP(launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M, D,
-                              c.ln_eps, out_dev, 0, s));
+    JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
+                launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M,
+                                 D, c.ln_eps, out_dev, 0, s));
   return JEPA_OK;
 }
 
@@ -526,26 +574,34 @@ int jepa_predict(jepa_predictor* pred, const float* z_dev, int n_enc,
   int32_t* ids = static_cast<int32_t*>(pred->ids.p);
   // [Notes §3] "2.1 predictor forward": embed the context rows, mask tokens at the
   // targets, concatenate; positions from the concatenated ids ([Notes §4.4]).
-  JEPA_HIP(launch_gather_rows(z_dev, n_enc, c.enc_dim, ids_ctx_dev, n_ctx, pred->ws.a.p, bf, s));
-  JEPA_HIP(linear(c.compute, pred->ws.a.p, pred->ts.dev(pred->emb_w), pred->ts.devf(pred->emb_b),
-                  x, n_ctx, E, c.enc_dim, JEPA_EPI_STORE, 1, s));
+  JEPA_LAUNCH(JEPA_KC_OTHER, s,
+              launch_gather_rows(z_dev, n_enc, c.enc_dim, ids_ctx_dev, n_ctx, pred->ws.a.p, bf, s));
+  JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
+              linear(c.compute, pred->ws.a.p, pred->ts.dev(pred->emb_w), pred->ts.devf(pred->emb_b),
+                     x, n_ctx, E, c.enc_dim, JEPA_EPI_STORE, 1, s));
   int mi = mask_index % c.n_mask_tokens;
   if (mi < 0) mi += c.n_mask_tokens;
-  JEPA_HIP(launch_fill_rows(x + static_cast<size_t>(n_ctx) * E,
-                            pred->ts.devf(pred->mask) + static_cast<size_t>(mi) * E, n_tgt, E, s));
-  JEPA_HIP(hipMemcpyAsync(ids, ids_ctx_dev, static_cast<size_t>(n_ctx) * 4,
-                          hipMemcpyDeviceToDevice, s));
-  JEPA_HIP(hipMemcpyAsync(ids + n_ctx, ids_tgt_dev, static_cast<size_t>(n_tgt) * 4,
-                          hipMemcpyDeviceToDevice, s));
+  JEPA_LAUNCH(JEPA_KC_OTHER, s,
+              launch_fill_rows(x + static_cast<size_t>(n_ctx) * E,
+                               pred->ts.devf(pred->mask) + static_cast<size_t>(mi) * E, n_tgt, E, s));
+  JEPA_LAUNCH(JEPA_KC_OTHER, s,
+              hipMemcpyAsync(ids, ids_ctx_dev, static_cast<size_t>(n_ctx) * 4,
+                             hipMemcpyDeviceToDevice, s));
+  JEPA_LAUNCH(JEPA_KC_OTHER, s,
+              hipMemcpyAsync(ids + n_ctx, ids_tgt_dev, static_cast<size_t>(n_tgt) * 4,
+                             hipMemcpyDeviceToDevice, s));
   const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, 0};
   JEPA_TRY(run_blocks(pred->ts, pred->blocks, c.n_layer, pred->ws, x, 1, M, E, c.ffn_dim,
                       c.n_head, c.ln_eps, ids, rs, s));
   // final norm and output projection on the target rows only
   float* xt = x + static_cast<size_t>(n_ctx) * E;
-  JEPA_HIP(launch_layernorm(xt, pred->ts.devf(pred->norm_w), pred->ts.devf(pred->norm_b), n_tgt, E,
-                            c.ln_eps, pred->ws.h.p, bf, s));
-  JEPA_HIP(linear(c.compute, pred->ws.h.p, pred->ts.dev(pred->proj_w), pred->ts.devf(pred->proj_b),
-                  out_dev, n_tgt, c.out_dim, E, JEPA_EPI_STORE, 1, s));
+  JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
+              launch_layernorm(xt, pred->ts.devf(pred->norm_w), pred->ts.devf(pred->norm_b), n_tgt,
+                               E, c.ln_eps, pred->ws.h.p, bf, s));
+  JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
+              linear(c.compute, pred->ws.h.p, pred->ts.dev(pred->proj_w),
+                     pred->ts.devf(pred->proj_b), out_dev, n_tgt, c.out_dim, E, JEPA_EPI_STORE, 1,
+                     s));
   return JEPA_OK;
 }
 
@@ -625,6 +681,53 @@ int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, 
   return hip_status(launch_attention_f32(static_cast<const float*>(qkv_dev),
                                          static_cast<float*>(out_dev), B, N, n_head, head_dim,
                                          ids_dev, rs, s));
+}
+
+
+int jepa_timing_begin(int cap) {
+  if (cap < 1 || g_timing.on) return JEPA_ERR_ARG;
+  for (int k = 0; k < JEPA_KC_COUNT; ++k) {
+    g_timing.n[k] = 0;
+    g_timing.ev[k].assign(2 * static_cast<size_t>(cap), nullptr);
+    for (hipEvent_t& e : g_timing.ev[k]) {
+      if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipGetLastError();
+        for (int j = 0; j <= k; ++j)
+          for (hipEvent_t& f : g_timing.ev[j])
+            if (f) (void)hipEventDestroy(f);
+        for (int j = 0; j < JEPA_KC_COUNT; ++j) g_timing.ev[j].clear();
+        return JEPA_ERR_HIP;
+      }
+    }
+  }
+  g_timing.cap = cap;
+  g_timing.on = true;
+  return JEPA_OK;
+}
+
+int jepa_timing_end(double* ms, int* launches) {
+  if (!g_timing.on) return JEPA_ERR_STATE;
+  g_timing.on = false;
+  int st = JEPA_OK;
+  for (int k = 0; k < JEPA_KC_COUNT; ++k) {
+    double sum = 0.0;
+    for (int i = 0; i < g_timing.n[k]; ++i) {
+      float t = 0.f;
+      if (hipEventSynchronize(g_timing.ev[k][2 * i + 1]) != hipSuccess ||
+          hipEventElapsedTime(&t, g_timing.ev[k][2 * i], g_timing.ev[k][2 * i + 1]) != hipSuccess) {
+        (void)hipGetLastError();
+        st = JEPA_ERR_HIP;
+        continue;
+      }
+      sum += t;
+    }
+    if (ms) ms[k] = sum;
+    if (launches) launches[k] = g_timing.n[k];
+    for (hipEvent_t& e : g_timing.ev[k]) (void)hipEventDestroy(e);
+    g_timing.ev[k].clear();
+    g_timing.n[k] = 0;
+  }
+  return st;
 }
 
 }  // extern "C"
