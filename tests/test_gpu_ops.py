@@ -156,6 +156,11 @@ LINEAR_CASES = [
     (700, 1024, 4096, J.JEPA_EPI_RESIDUAL, "f32"),
     (33, 768, 1536, J.JEPA_EPI_STORE, "f32"),
     (1, 128, 64, J.JEPA_EPI_GELU, "f32"),
+    # full-height shapes of the 4-clip ViT-L forward with a ragged last row tile: they take
+    # the 256x256 (N = 4096) and 256x192 (N = 3072) tiles
+    (8192 - 5, 4096, 1024, J.JEPA_EPI_GELU, "bf16"),
+    (8192 - 77, 3072, 1024, J.JEPA_EPI_STORE, "bf16"),
+    (8192 - 130, 1024, 4096, J.JEPA_EPI_RESIDUAL, "f32"),
 ]
 
 

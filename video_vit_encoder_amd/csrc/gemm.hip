@@ -3,24 +3,23 @@
 // Weights are stored [out, in] row-major ([Notes §2] key map), so both operands are
 // contiguous along K and map straight onto the MFMA operand layout.
 //
-// bf16 path (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
-//   * a workgroup of 8 wavefronts (2 per SIMD, so one wave's MFMAs cover the other's
-//     LDS reads) computes 256 (rows of A) x 128 or x 256 (rows of W) output tiles, the
-//     wider tile wherever it fills whole rounds of the CUs (it halves the LDS reads per
-//     MFMA); each wave owns 64 x 64 or 128 x 64 of a tile as blocks of 16 x 16;
-//   * the kernel is persistent: one workgroup per CU walks its tiles, and the K-slabs of
-//     all its tiles form one stream through a ring of 3 (64-deep slabs) or 4 (32-deep)
-//     LDS buffers, filled by global_load_lds_dwordx4 (HBM/L2 -> LDS, no register
-//     staging) STAGES - 1 slabs ahead of the MFMAs, so the next tile's first slabs load
-//     while the current tile's epilogue runs; one barrier per slab;
-//   * LDS rows are 128 B (64-deep slabs) or 64 B (32-deep); the 16-byte chunk c of row r
-//     lives at chunk c ^ (r & 7), resp. c ^ ((r >> 2) & 3).  A DMA instruction writes 64 consecutive 16-byte slots (8 rows), so
-//     lane p of it fetches the global chunk that belongs in slot p.  With the 16x16x32
-//     operand pattern (16 rows x 4 chunks per read) this layout keeps ds_read_b128 near
-//     the LDS peak on gfx950;
-//   * the MFMA takes the W fragment as its first operand, so each lane ends up holding 4
-//     consecutive output columns of one output row: the epilogue (bias, GELU, residual)
-//     reads and writes 8- or 16-byte vectors;
+// bf16 path (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   * a workgroup of 8 wavefronts (2 per SIMD) computes 256 (rows of A) x 256, 192 or
+//     128 (rows of W) output tiles: the widest tile whose count fills whole rounds of
+//     the CUs, since the bytes a CU pulls from L2 per MFMA fall as the tile grows and
+//     the L2 -> LDS path, not the LDS or the MFMAs, limits the main loop; each wave
+//     owns a 128x64, 64x96 or 64x64 part of the tile as 32x32 blocks;
+//   * the kernel is persistent: one workgroup per CU walks its tiles, and the 64-deep
+//     K-slabs of all its tiles form one stream through a ring of 2 or 3 LDS buffers,
+//     filled by global_load_lds_dwordx4 (HBM/L2 -> LDS, no register staging) up to
+//     STAGES - 1 slabs ahead of the MFMAs, so the next tile's first slabs load while
+//     the current tile's epilogue runs; one barrier per slab;
+//   * LDS rows are 128 B; the 16-byte chunk c of row r lives at chunk c ^ (r & 7).  A DMA
+//     instruction writes 64 consecutive 16-byte slots (8 rows), so lane p of it fetches
+//     the global chunk that belongs in slot p;
+//   * the MFMA takes the W fragment as its first operand, so each lane ends up holding
+//     runs of 4 consecutive output columns of one output row: the epilogue (bias, GELU,
+//     residual) reads and writes 8- or 16-byte vectors;
 //   * tiles are dealt so that the 32 workgroups of one XCD (work-groups go to the 8
 //     XCDs round-robin) work on neighbouring tiles at the same time.
 //
@@ -46,31 +45,35 @@ __device__ __forceinline__ float gelu_as(float z) {
   return 0.5f * z * (1.0f + copysignf(e, z));
 }
 
-// One tile configuration: BM x BN output tiles, K slabs of BK through STAGES LDS
-// buffers, WGM x WGN waves (2 per SIMD) of WM x WN.
-template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_, int WG_PER_CU_>
+// One tile configuration: BM x BN output tiles, 64-deep K slabs through a ring of STAGES
+// LDS buffers, WGM x WGN waves of WM x WN, each held as 32 x 32 MFMA blocks.
+template <int BM_, int BN_, int STAGES_, int WGM_, int WGN_>
 struct GemmCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
-  static constexpr int WG_PER_CU = WG_PER_CU_;
+  static constexpr int BM = BM_, BN = BN_, BK = 64, STAGES = STAGES_;
   static constexpr int WGM = WGM_, WGN = WGN_, NWAVES = WGM * WGN, NT = NWAVES * 64;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
-  static constexpr int FI = WM / 16, FJ = WN / 16;        // 16x16 blocks per wave
-  static constexpr int ROWB = BK * 2;                     // LDS bytes per tile row
+  static constexpr int FI = WM / 32, FJ = WN / 32;        // 32x32 blocks per wave
+  static constexpr int ROWB = BK * 2;                     // LDS bytes per tile row (128)
   static constexpr int RPI = 1024 / ROWB;                 // rows per 1 KB DMA instruction
   static constexpr int CPR = ROWB / 16;                   // 16-byte chunks per row
-  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int A_LOADS = A_BYTES / 1024 / NWAVES;  // DMA instructions per thread
   static constexpr int B_LOADS = B_BYTES / 1024 / NWAVES;
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int LDS = STAGES * STAGE_BYTES;
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && B_LOADS * NWAVES * 1024 == B_BYTES, "DMA split");
-  static_assert(BK == 64 || BK == 32, "row swizzle");
-  // swizzle key of tile row r: the 16-byte chunk c of row r sits at chunk c ^ key(r)
-  __device__ static int key(int r) { return BK == 64 ? (r & 7) : ((r >> 2) & 3); }
+  static_assert(FI * 32 == WM && FJ * 32 == WN, "wave tile");
+  static_assert(STAGES >= 2 && STAGES <= 4 && LDS <= 160 * 1024, "LDS ring");
+  // the 16-byte chunk c of tile row r sits at chunk c ^ (r & 7)
+  __device__ static int key(int r) { return r & 7; }
 };
-// 256 x 128, BK 64, 3 stages (144 KB), 4 x 2 waves of 64 x 64, one workgroup per CU
-using CfgBig = GemmCfg<256, 128, 64, 3, 4, 2, 1>;
+// 256 x 256: FFN up-projection (N = 4096 gives whole rounds of 256 CUs)
+using Cfg256x256 = GemmCfg<256, 256, 2, 2, 4>;
+// 256 x 192: QKV projection at D = 1024 (N = 3072)
+using Cfg256x192 = GemmCfg<256, 192, 2, 4, 2>;
+// 256 x 128: every other width that is a multiple of 128
+using Cfg256x128 = GemmCfg<256, 128, 3, 4, 2>;
 
 template <class C, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(C::NT)
@@ -85,7 +88,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA LDS bases
   const int wm = wave / C::WGN, wn = wave % C::WGN;
-  const int q16 = lane >> 4, l16 = lane & 15;
+  const int h = lane >> 5, l32 = lane & 31;
 
   const int tiles_n = N / BN;
   const int tiles = ((M + BM - 1) / BM) * tiles_n;
@@ -123,16 +126,16 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     n0 = tn * BN;
   };
 
-  // DMA mapping: instruction q of wave w fills rows [RPI g, RPI (g+1)) of a tile,
-  // g = q*NWAVES + w; lane p -> row RPI g + p/CPR, slot p%CPR holding logical chunk
-  // (p%CPR) ^ key(row) (the key of the row depends on p/CPR only, RPI being a multiple
-  // of its period).
+  // DMA mapping: instruction q of wave w fills rows [8 g, 8 g + 8) of a tile,
+  // g = q*NWAVES + w; lane p -> row 8 g + p/8, slot p%8 holding logical chunk
+  // (p%8) ^ key(row) (the key depends on p/8 only).
   const int prow = lane / C::CPR;
   const int pchunk = (lane % C::CPR) ^ C::key(prow);
   const uint32_t smem_base = lds_addr(smem);
 
   // Issue state: the next slab to load (tile it_iss, slab kt_iss) and the byte offsets
-  // of this lane's source rows in that tile, refreshed when the tile changes.
+  // of this lane's source rows in that tile, refreshed when the tile changes.  Rows of A
+  // past M are clamped to row M - 1 (loaded, never stored).
   int it_iss = 0, kt_iss = 0, s_iss = 0;
   uint32_t a_row[A_LOADS], b_row[B_LOADS];
   auto set_rows = [&](int it) {
@@ -164,18 +167,18 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     }
   };
 
-  // fragment rows of this lane inside the A / W tiles (16x16x32 operand: row l%16,
-  // 8 consecutive k at chunk 4*step + l/16)
+  // fragment rows of this lane inside the A / W tiles (32x32x16 operand: row l%32,
+  // 8 consecutive k at chunk 2*step + l/32)
   int arow[FI], brow[FJ];
 #pragma unroll
-  for (int i = 0; i < FI; ++i) arow[i] = wm * WM + i * 16 + l16;
+  for (int i = 0; i < FI; ++i) arow[i] = wm * WM + i * 32 + l32;
 #pragma unroll
-  for (int j = 0; j < FJ; ++j) brow[j] = wn * WN + j * 16 + l16;
+  for (int j = 0; j < FJ; ++j) brow[j] = wn * WN + j * 32 + l32;
 
-  // Operand fragments of slab s, k-step ks, from LDS.
+  // Operand fragments of slab s, k-step ks (16 deep), from LDS.
   auto load_frags = [&](int s_, int ks, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
     const unsigned char* st = smem + (s_ % STAGES) * STAGE_BYTES;
-    const int ch = ks * 4 + q16;
+    const int ch = ks * 2 + h;
 #pragma unroll
     for (int i = 0; i < FI; ++i)
       af[i] = *reinterpret_cast<const bf16x8*>(st + arow[i] * ROWB + ((ch ^ C::key(arow[i])) << 4));
@@ -183,10 +186,10 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     for (int j = 0; j < FJ; ++j)
       bfr[j] = *reinterpret_cast<const bf16x8*>(st + A_BYTES + brow[j] * ROWB + ((ch ^ C::key(brow[j])) << 4));
   };
-  // Wait until slab s_ has landed in LDS for every lane of the workgroup: at most
-  // min(total - 1, s_ + STAGES - 3) - s_ later slabs may still be in flight.
+  // Wait until slab s_ has landed in LDS for every lane of the workgroup: the slabs
+  // issued after it (at most STAGES - 2, fewer near the end) may stay in flight.
   auto wait_slab = [&](int s_) __attribute__((always_inline)) {
-    const int ahead = min(total - 1 - s_, STAGES - 3);
+    const int ahead = min(s_iss - 1 - s_, STAGES - 2);
     if (ahead >= 2)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS) : "memory");
     else if (ahead == 1)
@@ -196,32 +199,33 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     __syncthreads();
   };
 
-  // Prologue: STAGES - 2 slabs in flight, slab 0 landed, its first fragments loaded.
-  // In the loop, slab s + 1's barrier and first fragment loads come before slab s's last
-  // k-step of MFMAs, so LDS latency hides behind MFMAs; the DMA issued after that barrier
-  // (slab s + STAGES - 2) reuses the buffer of slab s - 2, whose reads all completed
-  // before the barrier.
-  constexpr int KSTEPS = BK / 32;
+  // Prologue: slabs 0 .. STAGES - 2 issued, slab 0 landed, slab STAGES - 1 issued, slab
+  // 0's first fragments loaded.  In the loop, slab s + 1's barrier and first fragment
+  // loads come before slab s's last k-step of MFMAs, so LDS latency hides behind MFMAs;
+  // the DMA issued right after that barrier (slab s + STAGES) reuses the buffer of slab s,
+  // whose reads all completed before the barrier.  Up to STAGES - 1 slabs are in flight
+  // while a slab is consumed.
+  constexpr int KSTEPS = BK / 16;
+  if (total > 0) set_rows(0);
 #pragma unroll
-  for (int p = 0; p < STAGES - 2; ++p) {
-    if (p < total) {
-      if (p == 0) set_rows(0);
-      issue_next();
-    }
-  }
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < total) issue_next();
   bf16x8 af[2][FI], bfr[2][FJ];
   if (total > 0) {
     wait_slab(0);
-    if (STAGES - 2 < total) issue_next();
+    // slab STAGES - 1 goes into the buffer no slab has used yet
+    if (s_iss < total) issue_next();
     load_frags(0, 0, af[0], bfr[0]);
   }
   int s = 0;  // position in this workgroup's slab stream
   for (int it = 0; it < n_my; ++it) {
-    f32x4 acc[FI][FJ];
+    f32x16 acc[FI][FJ];
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
-      for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     for (int kt = 0; kt < KT; ++kt, ++s) {
 #pragma unroll
@@ -231,15 +235,15 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
           load_frags(s, ks + 1, af[nxt], bfr[nxt]);
         } else if (s + 1 < total) {
           wait_slab(s + 1);
-          if (s + STAGES - 1 < total) issue_next();
+          if (s_iss < total) issue_next();
           load_frags(s + 1, 0, af[nxt], bfr[nxt]);
         }
 #pragma unroll
         for (int i = 0; i < FI; ++i)
 #pragma unroll
           for (int j = 0; j < FJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
-        if (KSTEPS == 1 || ks + 1 == KSTEPS) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+        if (ks + 1 == KSTEPS) {
           // the fragments loaded above for slab s + 1 move into slot 0
 #pragma unroll
           for (int i = 0; i < FI; ++i) af[0][i] = af[nxt][i];
@@ -249,38 +253,41 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
       }
     }
 
-    // Epilogue of tile it.  acc[i][j] is the 16 (W rows) x 16 (A rows) block with lane
-    // l, element e at W row 4*(l/16) + e and A row l%16: four consecutive output
-    // columns per lane.
+    // Epilogue of tile it.  acc[i][j] is the 32 (W rows) x 32 (A rows) block with lane
+    // l, element e at W row 8*(e/4) + 4*(l/32) + e%4 and A row l%32: runs of four
+    // consecutive output columns per lane.
     int m0, n0;
     tile_of(it, m0, n0);
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
-      const int row = m0 + wm * WM + i * 16 + l16;
+      const int row = m0 + wm * WM + i * 32 + l32;
       if (row >= M) continue;
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
-        const int col = n0 + wn * WN + j * 16 + 4 * q16;
-        const f32x4 bv = bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = acc[i][j][e] + bv[e];
-          if (EPI == EPI_GELU) v[e] = OUT_F32 ? gelu_erf(v[e]) : gelu_as(v[e]);
-        }
-        const size_t off = static_cast<size_t>(row) * N + col;
-        if (EPI == EPI_RESIDUAL) {
-          f32x4* Cp = reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off);
-          f32x4 c = *Cp;
-          c[0] += v[0]; c[1] += v[1]; c[2] += v[2]; c[3] += v[3];
-          *Cp = c;
-        } else if (OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off) = f32x4{v[0], v[1], v[2], v[3]};
-        } else {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(v[0], v[1]);
-          pk[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cv) + off) = pk;
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * h;
+          const f32x4 bv = bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[i][j][4 * g + e] + bv[e];
+            if (EPI == EPI_GELU) v[e] = OUT_F32 ? gelu_erf(v[e]) : gelu_as(v[e]);
+          }
+          const size_t off = static_cast<size_t>(row) * N + col;
+          if (EPI == EPI_RESIDUAL) {
+            f32x4* Cp = reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off);
+            f32x4 c = *Cp;
+            c[0] += v[0]; c[1] += v[1]; c[2] += v[2]; c[3] += v[3];
+            *Cp = c;
+          } else if (OUT_F32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off) = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(v[0], v[1]);
+            pk[1] = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cv) + off) = pk;
+          }
         }
       }
     }
@@ -310,7 +317,7 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
     configured = true;
   }
   const int tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
-  const dim3 grid(min(tiles, C::WG_PER_CU * num_cus()));
+  const dim3 grid(min(tiles, num_cus()));
   gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, C::LDS, s>>>(A, W, bias, Cp, M, N, K);
   return hipGetLastError();
 }
@@ -334,7 +341,15 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* b
   if (static_cast<size_t>(M) * K * 2 >= (size_t(1) << 31) ||
       static_cast<size_t>(N) * K * 2 >= (size_t(1) << 31))
     return hipErrorInvalidValue;
-  return gemm_dispatch<CfgBig>(A, W, bias, C, M, N, K, epi, out_f32, s);
+  // The widest tile whose count still fills whole rounds of the CUs (fewer, larger tiles
+  // cut the bytes each CU pulls through L2 per MFMA).
+  const int cus = num_cus();
+  const int tm = (M + 255) / 256;
+  if (N % 256 == 0 && tm * (N / 256) >= cus && (tm * (N / 256)) % cus == 0)
+    return gemm_dispatch<Cfg256x256>(A, W, bias, C, M, N, K, epi, out_f32, s);
+  if (N % 192 == 0 && tm * (N / 192) >= cus && (tm * (N / 192)) % cus == 0)
+    return gemm_dispatch<Cfg256x192>(A, W, bias, C, M, N, K, epi, out_f32, s);
+  return gemm_dispatch<Cfg256x128>(A, W, bias, C, M, N, K, epi, out_f32, s);
 }
 
 // ---------------------------------------------------------------- fp32 path
