@@ -127,8 +127,9 @@ int jepa_encoder_set_tensor(jepa_encoder* enc, const char* name, const void* hos
  * (px - 255*mean)/(255*std) ([Parity "Preprocessing parity"]), patchified into
  * 2x16x16x3 tubelets and embedded; then the blocks and the final norm.
  * Shape errors (JEPA_ERR_SHAPE): T odd or < 2, H or W not a multiple of 16, B < 1,
- * B*N > max_rows, interpolation with a grid side of 1 ([Notes §4.3]).
- * JEPA_ERR_STATE if a required tensor was never set. */
+ * B*N > max_rows, interpolation with a grid side of 1 ([Notes §4.3]); on the bf16 path
+ * also B*ceil(N/16)*16 > 2*max_rows + 1024 (only reachable with fewer than 16 tokens per
+ * clip).  JEPA_ERR_STATE if a required tensor was never set. */
 int jepa_encode(jepa_encoder* enc, const uint8_t* clip_dev, int B, int T, int H, int W,
                 float* out_dev, void* stream);
 
@@ -213,16 +214,27 @@ int jepa_layernorm(const float* x_dev, const float* weight_dev, const float* bia
 int jepa_linear(const void* A_dev, const void* W_dev, const float* bias_dev, void* C_dev,
                 int M, int N, int K, int dtype, int epilogue, int out_dtype, void* stream);
 
-/* Multi-head softmax attention with the 3-D RoPE applied to q and k as they are loaded
- * ([Notes §4]: RoPE on q and k, not v, before the 1/sqrt(head_dim) scaling; softmax
- * over every key, no mask):
+/* Multi-head softmax attention with the 3-D RoPE on q and k ([Notes §4]: RoPE on q and
+ * k, not v, before the 1/sqrt(head_dim) scaling; softmax over every key, no mask):
  *   qkv_dev [B*N, 3*n_head*head_dim] in dtype: per row q | k | v, head e at columns
- *   e*head_dim of each third ([Notes §2]: fused rows [q; k; v]);
+ *   e*head_dim of each third ([Notes §2]: fused rows [q; k; v]), not yet rotated;
  *   out_dev [B*N, n_head*head_dim] in dtype, heads concatenated;
- *   ids/grid/layout/theta/ref_grid as jepa_rope3d.  head_dim must be 64 or 32. */
+ *   ids/grid/layout/theta/ref_grid as jepa_rope3d.  head_dim must be 64 or 32.
+ * JEPA_BF16 (bf16 MFMA, fp32 softmax): q and k are first rotated (q also scaled by
+ * log2(e)/sqrt(head_dim)) and v transposed into work_dev, a device buffer of at least
+ * jepa_attention_workspace_size(...) bytes owned by the caller (contents on entry do not
+ * matter; overwritten); then the flash-attention kernel runs on it.  The encoder forward
+ * uses the same kernel with the rotation done by the QKV projection's epilogue.
+ * JEPA_F32 (plain fp32 FMA, RoPE applied as q and k are loaded): work_dev is unused and
+ * may be NULL.
+ * Errors: JEPA_ERR_ARG also when the bf16 workspace is NULL or smaller than needed. */
 int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
                    int head_dim, const int32_t* ids_dev, int gt, int gh, int gw, int layout,
-                   float theta, int ref_grid, void* stream);
+                   float theta, int ref_grid, void* work_dev, size_t work_bytes, void* stream);
+
+/* Bytes of device workspace jepa_attention needs for these sizes (0 for JEPA_F32 or
+ * non-positive sizes). */
+size_t jepa_attention_workspace_size(int dtype, int B, int N, int n_head, int head_dim);
 
 /* ------------------------------------------------------------------ kernel timing */
 

@@ -87,8 +87,15 @@ def test_standalone_ops_validate_before_launch():
     assert lib.jepa_linear(fake, fake, None, fake, 4, 128, 60, 1, 0, 1, None) == _lib.JEPA_ERR_SHAPE
     assert lib.jepa_linear(fake, fake, None, fake, 4, 128, 64, 1, 2, 1, None) == _lib.JEPA_ERR_ARG
     # attention: head dim 48, grid side above the table limit
-    assert lib.jepa_attention(fake, fake, 1, 1, 8, 1, 48, None, 1, 2, 4, 0, 1e4, 0, None) == _lib.JEPA_ERR_SHAPE
-    assert lib.jepa_attention(fake, fake, 1, 1, 65, 1, 64, None, 65, 1, 1, 0, 1e4, 0, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_attention(fake, fake, 1, 1, 8, 1, 48, None, 1, 2, 4, 0, 1e4, 0, None, 0, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_attention(fake, fake, 1, 1, 65, 1, 64, None, 65, 1, 1, 0, 1e4, 0, None, 0, None) == _lib.JEPA_ERR_SHAPE
+    # bf16 needs a workspace of jepa_attention_workspace_size bytes
+    need = lib.jepa_attention_workspace_size(1, 1, 8, 1, 64)
+    assert need > 8 * 3 * 64 * 2
+    assert lib.jepa_attention(fake, fake, 1, 1, 8, 1, 64, None, 1, 2, 4, 0, 1e4, 0, None, 0, None) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_attention(fake, fake, 1, 1, 8, 1, 64, None, 1, 2, 4, 0, 1e4, 0, fake, need - 1, None) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_attention_workspace_size(0, 1, 8, 1, 64) == 0
+    assert lib.jepa_attention_workspace_size(1, 0, 8, 1, 64) == 0
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

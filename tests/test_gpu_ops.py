@@ -216,6 +216,8 @@ ATTN_CASES = [
     ("hd64 interleaved interp", 1, (3, 9, 11), 2, 64, "interleaved", 16, None, "bf16"),
     ("hd32 tiled shuffled ids", 1, (4, 8, 8), 4, 32, "tiled", 0, "perm", "bf16"),
     ("hd64 one tile", 1, (1, 2, 3), 2, 64, "tiled", 0, None, "bf16"),
+    ("hd64 two 2048-token clips", 2, (8, 16, 16), 2, 64, "tiled", 0, None, "bf16"),
+    ("hd32 interleaved 1000 tokens", 1, (10, 10, 10), 3, 32, "interleaved", 16, None, "bf16"),
     ("hd64 f32 tiny grid", 1, (2, 4, 4), 12, 64, "tiled", 0, None, "f32"),
     ("hd64 f32 ragged", 2, (3, 7, 5), 2, 64, "interleaved", 16, None, "f32"),
     ("hd32 f32 ids", 1, (2, 6, 6), 3, 32, "tiled", 0, "perm", "f32"),
@@ -280,3 +282,24 @@ def test_attention_softmax_properties_identical_keys():
     J.jepa_attention(bf16(qkv), od, B, N, H, hd, None, grid, "tiled")
     got = host(od)
     assert np.array_equal(got, np.broadcast_to(vrow.astype(np.float64), (N, D)))
+
+
+def test_attention_growing_scores_rescale():
+    # key norms grow along the clip, so later key tiles keep raising each query's running
+    # maximum by more than 2^8 (the kernel's lazy-rescale threshold, in log2 units) and
+    # the rescale path runs many times; the first tile's scores are small
+    banner("attention growing scores")
+    B, grid, H, hd = 1, (4, 12, 16), 2, 64
+    N, D = 768, 128
+    rng = np.random.default_rng(21)
+    qkv = rng.standard_normal((N, 3 * D))
+    qkv[:, :D] *= 2.0
+    qkv[:, D:2 * D] *= (4.0 * np.arange(N) / N)[:, None]
+    qkv = synth.round_to_bf16(qkv.astype(np.float32))
+    import torch
+    od = torch.empty((N, D), dtype=torch.bfloat16, device="cuda:0")
+    J.jepa_attention(bf16(qkv), od, B, N, H, hd, None, grid, "tiled")
+    got = host(od).reshape(B, N, D)
+    ref = _attn_ref(qkv.astype(np.float64).reshape(B, N, 3 * D), B, N, H, hd,
+                    np.arange(N, dtype=np.int32), grid, "tiled", 0)
+    assert_bf16_gate(got, ref, "growing scores")

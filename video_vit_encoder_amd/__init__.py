@@ -14,7 +14,7 @@ import numpy as np
 
 from ._lib import (  # noqa: F401
     DTYPES, JEPA_BF16, JEPA_EPI_GELU, JEPA_EPI_RESIDUAL, JEPA_EPI_STORE, JEPA_F32, LAYOUTS,
-    KERNEL_CLASSES, JepaError, header_functions, jepa_attention, jepa_encode, jepa_encode_tokens,
+    KERNEL_CLASSES, JepaError, header_functions, jepa_attention, jepa_attention_workspace_size, jepa_encode, jepa_encode_tokens,
     jepa_encoder_config, jepa_encoder_create, jepa_encoder_free, jepa_encoder_set_tensor,
     jepa_layernorm, jepa_linear, jepa_predict, jepa_predictor_config, jepa_predictor_create,
     jepa_predictor_free, jepa_predictor_set_tensor, jepa_rope3d, jepa_status_str,

@@ -71,7 +71,9 @@ _SIGS = {
     "jepa_rope3d": ([_P, _P, _I, _I, _I, _I, _I, _I64, _P, _I, _I, _I, _I, _F, _I, _P], _I),
     "jepa_layernorm": ([_P, _P, _P, _I, _I, _F, _P, _I, _P], _I),
     "jepa_linear": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
-    "jepa_attention": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _I, _I, _F, _I, _P], _I),
+    "jepa_attention": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t,
+                        _P], _I),
+    "jepa_attention_workspace_size": ([_I, _I, _I, _I, _I], ctypes.c_size_t),
     "jepa_timing_begin": ([_I], _I),
     "jepa_timing_end": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)], _I),
 }
@@ -298,19 +300,30 @@ def jepa_linear(A, W, bias, C, epilogue: int = JEPA_EPI_STORE, stream=None) -> N
                               _stream(stream)))
 
 
+def jepa_attention_workspace_size(dtype: int, B: int, N: int, n_head: int, head_dim: int) -> int:
+    return load().jepa_attention_workspace_size(dtype, B, N, n_head, head_dim)
+
+
 def jepa_attention(qkv, out, B: int, N: int, n_head: int, head_dim: int, ids,
                    grid: Sequence[int], layout: str, theta: float = 10000.0, ref_grid: int = 0,
-                   stream=None) -> None:
+                   stream=None, work=None) -> None:
+    """qkv [B*N, 3D] and out [B*N, D] device tensors of one dtype.  The bf16 path needs a
+    device workspace: ``work`` (a uint8 tensor) or one allocated here."""
     import torch
     dt = JEPA_BF16 if qkv.dtype == torch.bfloat16 else JEPA_F32
     D = n_head * head_dim
     _need(qkv.numel() == B * N * 3 * D and out.numel() == B * N * D and out.dtype == qkv.dtype,
           "qkv [B*N, 3D] and out [B*N, D] of one dtype")
     _need(ids is None or (ids.numel() >= N and ids.dtype == torch.int32), "ids must be int32 [N]")
+    nbytes = jepa_attention_workspace_size(dt, B, N, n_head, head_dim)
+    if work is None and nbytes > 0:
+        work = torch.empty(nbytes, dtype=torch.uint8, device=qkv.device)
+    wbytes = 0 if work is None else work.numel() * work.element_size()
     gt, gh, gw = grid
     _check("jepa_attention",
            load().jepa_attention(_ptr(qkv), _ptr(out), dt, B, N, n_head, head_dim, _ptr(ids),
-                                 gt, gh, gw, LAYOUTS[layout], theta, ref_grid, _stream(stream)))
+                                 gt, gh, gw, LAYOUTS[layout], theta, ref_grid, _ptr(work), wbytes,
+                                 _stream(stream)))
 
 
 def jepa_timing_begin(cap: int) -> None:

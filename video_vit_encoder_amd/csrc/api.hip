@@ -29,6 +29,10 @@ constexpr int kVersion = 100;  // 0.1.0
 
 // ------------------------------------------------------------------ helpers
 
+// Bytes past the last transposed-V row that the attention kernel's last key tile reads
+// (at most 63 keys of 2 bytes; rounded up).
+constexpr size_t kVtSlackBytes = 4096;
+
 uint16_t host_f32_to_bf16(float f) {
   uint32_t u;
   std::memcpy(&u, &f, 4);
@@ -262,14 +266,17 @@ int check_grid(int gt, int gh, int gw, int ref_grid) {
 
 // Workspace of the block sequence for `rows` token rows.
 struct Workspace {
-  DevBuf h, qkv, o, g, a;
+  DevBuf h, qkv, o, g, a, vt, tab;
   int rows = 0;
+  size_t vt_rows = 0;  // capacity of vt in (clip, key) rows of D values
   ~Workspace() {
     dev_free(h);
     dev_free(qkv);
     dev_free(o);
     dev_free(g);
     dev_free(a);
+    dev_free(vt);
+    dev_free(tab);
   }
   int alloc(int max_rows, int D, int F, int a_cols, int compute) {
     rows = max_rows;
@@ -280,8 +287,18 @@ struct Workspace {
     JEPA_TRY(dev_alloc(o, m * D * es));
     JEPA_TRY(dev_alloc(g, m * F * es));
     if (a_cols > 0) JEPA_TRY(dev_alloc(a, m * a_cols * es));
+    if (compute == JEPA_BF16) {
+      // v transposed per (clip, head) with rows padded to 16 keys, plus the bytes the
+      // attention kernel's last key tile reads past the final row
+      vt_rows = 2 * m + 1024;
+      JEPA_TRY(dev_alloc(vt, vt_rows * D * 2 + kVtSlackBytes));
+      if (hipMemset(vt.p, 0, vt.bytes) != hipSuccess) return JEPA_ERR_HIP;
+      JEPA_TRY(dev_alloc(tab, static_cast<size_t>(kRopeTabEntries) * 8));
+    }
     return JEPA_OK;
   }
+  // The bf16 attention path fits B clips of N tokens.
+  bool vt_fits(int B, int N) const { return static_cast<size_t>(B) * vt_stride(N) <= vt_rows; }
 };
 
 // GEMM in the compute dtype.  out_f32 selects fp32 output for the STORE/GELU epilogues.
@@ -294,7 +311,9 @@ hipError_t linear(int compute, const void* A, const void* W, const float* bias, 
                          static_cast<float*>(C), M, N, K, epi, s);
 }
 
-// The pre-norm blocks over x (fp32 [B*N, D], in place).
+// The pre-norm blocks over x (fp32 [B*N, D], in place).  On the bf16 path the QKV
+// projection's epilogue applies the 3-D RoPE to q and k (q also takes log2(e)/sqrt(hd))
+// and writes v transposed; the attention kernel then reads all three by DMA.
 int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_run, Workspace& ws,
                float* x, int B, int N, int D, int F, int n_head, float eps, const int32_t* ids,
                const RopeSpec& rs, hipStream_t s) {
@@ -302,21 +321,34 @@ int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_r
   const int bf = compute == JEPA_BF16 ? 1 : 0;
   const int M = B * N;
   const int hd = D / n_head;
+  const int Ns = vt_stride(N);
+  if (bf && n_run > 0) {
+    if (!ws.vt_fits(B, N)) return JEPA_ERR_SHAPE;
+    JEPA_LAUNCH(JEPA_KC_OTHER, s, launch_rope_table(ws.tab.p, rs, hd, s));
+  }
   for (int l = 0; l < n_run; ++l) {
     const BlockIdx& b = blocks[l];
     JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
                 launch_layernorm(x, ts.devf(b.ln1w), ts.devf(b.ln1b), M, D, eps, ws.h.p, bf, s));
-    JEPA_LAUNCH(JEPA_KC_GEMM_QKV, s,
-                linear(compute, ws.h.p, ts.dev(b.qkvw), ts.devf(b.qkvb), ws.qkv.p, M, 3 * D, D,
-                       JEPA_EPI_STORE, !bf, s));
-    if (bf)
+    if (bf) {
+      uint16_t* qkv = static_cast<uint16_t*>(ws.qkv.p);
+      uint16_t* vt = static_cast<uint16_t*>(ws.vt.p);
+      JEPA_LAUNCH(JEPA_KC_GEMM_QKV, s,
+                  launch_gemm_bf16_qkv(static_cast<const uint16_t*>(ws.h.p),
+                                       static_cast<const uint16_t*>(ts.dev(b.qkvw)), ts.devf(b.qkvb),
+                                       qkv, vt, Ns, M, D, D, hd, ids, N, rs, ws.tab.p,
+                                       attn_qscale(hd), s));
       JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
-                  launch_attention_bf16(static_cast<const uint16_t*>(ws.qkv.p),
-                                        static_cast<uint16_t*>(ws.o.p), B, N, n_head, hd, ids, rs, s));
-    else
+                  launch_attention_fwd(qkv, qkv + D, 3 * D, vt, Ns, static_cast<uint16_t*>(ws.o.p), B,
+                                       N, n_head, hd, s));
+    } else {
+      JEPA_LAUNCH(JEPA_KC_GEMM_QKV, s,
+                  linear(compute, ws.h.p, ts.dev(b.qkvw), ts.devf(b.qkvb), ws.qkv.p, M, 3 * D, D,
+                         JEPA_EPI_STORE, 1, s));
       JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
                   launch_attention_f32(static_cast<const float*>(ws.qkv.p),
                                        static_cast<float*>(ws.o.p), B, N, n_head, hd, ids, rs, s));
+    }
     JEPA_LAUNCH(JEPA_KC_GEMM_OUT, s,
                 linear(compute, ws.o.p, ts.dev(b.outw), ts.devf(b.outb), x, M, D, D,
                        JEPA_EPI_RESIDUAL, 1, s));
@@ -660,9 +692,26 @@ int jepa_linear(const void* A_dev, const void* W_dev, const float* bias_dev, voi
                            out_dtype == JEPA_F32, static_cast<hipStream_t>(stream)));
 }
 
+// Workspace of the bf16 stand-alone attention: RoPE table | q', k' [M, 2D] | V^T rows.
+static size_t attn_ws_parts(int B, int N, int D, size_t* off_qk, size_t* off_vt) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t tab = up(static_cast<size_t>(kRopeTabEntries) * 8);
+  const size_t qk = up(static_cast<size_t>(B) * N * 2 * D * 2);
+  const size_t vt = static_cast<size_t>(B) * D * vt_stride(N) * 2 + kVtSlackBytes;
+  *off_qk = tab;
+  *off_vt = tab + qk;
+  return tab + qk + vt;
+}
+
+size_t jepa_attention_workspace_size(int dtype, int B, int N, int n_head, int head_dim) {
+  if (dtype != JEPA_BF16 || B <= 0 || N <= 0 || n_head <= 0 || head_dim <= 0) return 0;
+  size_t a, b;
+  return attn_ws_parts(B, N, n_head * head_dim, &a, &b);
+}
+
 int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
                    int head_dim, const int32_t* ids_dev, int gt, int gh, int gw, int layout,
-                   float theta, int ref_grid, void* stream) {
+                   float theta, int ref_grid, void* work_dev, size_t work_bytes, void* stream) {
   if (!qkv_dev || !out_dev) return JEPA_ERR_ARG;
   if (dtype != JEPA_F32 && dtype != JEPA_BF16) return JEPA_ERR_ARG;
   if (layout != JEPA_ROPE_TILED && layout != JEPA_ROPE_INTERLEAVED) return JEPA_ERR_ARG;
@@ -674,13 +723,24 @@ int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, 
   if (B == 0 || N == 0) return JEPA_OK;
   const RopeSpec rs{gt, gh, gw, layout, theta, ref_grid};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == JEPA_BF16)
-    return hip_status(launch_attention_bf16(static_cast<const uint16_t*>(qkv_dev),
-                                            static_cast<uint16_t*>(out_dev), B, N, n_head,
-                                            head_dim, ids_dev, rs, s));
-  return hip_status(launch_attention_f32(static_cast<const float*>(qkv_dev),
-                                         static_cast<float*>(out_dev), B, N, n_head, head_dim,
-                                         ids_dev, rs, s));
+  if (dtype == JEPA_F32)
+    return hip_status(launch_attention_f32(static_cast<const float*>(qkv_dev),
+                                           static_cast<float*>(out_dev), B, N, n_head, head_dim,
+                                           ids_dev, rs, s));
+  const int D = n_head * head_dim;
+  if (D % 32) return JEPA_ERR_SHAPE;
+  size_t off_qk, off_vt;
+  const size_t need = attn_ws_parts(B, N, D, &off_qk, &off_vt);
+  if (!work_dev || work_bytes < need) return JEPA_ERR_ARG;
+  unsigned char* w = static_cast<unsigned char*>(work_dev);
+  uint16_t* qk = reinterpret_cast<uint16_t*>(w + off_qk);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(w + off_vt);
+  const int Ns = vt_stride(N);
+  JEPA_HIP(launch_rope_table(w, rs, head_dim, s));
+  JEPA_HIP(launch_qkv_prepare(static_cast<const uint16_t*>(qkv_dev), qk, vt, Ns, B, N, n_head,
+                              head_dim, ids_dev, rs, w, attn_qscale(head_dim), s));
+  return hip_status(launch_attention_fwd(qk, qk + D, 2 * D, vt, Ns,
+                                         static_cast<uint16_t*>(out_dev), B, N, n_head, head_dim, s));
 }
 
 

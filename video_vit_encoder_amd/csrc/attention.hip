@@ -1,4 +1,4 @@
-// Multi-head softmax attention with the 3-D RoPE applied to q and k as they are loaded.
+// Multi-head softmax attention with the 3-D RoPE on q and k.
 //
 // What is computed ([Notes §4]): for each clip and head, softmax(R(q) R(k)^T / sqrt(hd)) v
 // over every token of the clip (no mask), with R the 3-D RoPE of the token's (t, h, w)
@@ -6,22 +6,16 @@
 // or interleaved ([Notes §4.2]) frequency layout, optional interpolation ([Notes §4.3]).
 // RoPE acts on q and k only, before the 1/sqrt(hd) scaling.
 //
-// bf16 kernel (gfx950 MFMA, fp32 softmax and accumulation):
-//   * a workgroup owns 128 query rows of one (clip, head); each of its 4 wavefronts owns
-//     32 of them and keeps them, rotated and pre-scaled by log2(e)/sqrt(hd), as bf16
-//     MFMA operands in registers;
-//   * keys/values stream through LDS 64 at a time; K is rotated on its way from HBM to
-//     LDS (angles from per-axis cos/sin tables built in LDS at kernel start), V is
-//     written transposed so it can serve as the A operand of the second product;
-//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16): in the 32x32 accumulator a lane holds 16
-//     keys of one query, so the running max and sum are per lane plus one exchange with
-//     the lane 32 away;
-//   * O^T += V^T P^T: P^T leaves the first product already in the B-operand layout of
-//     the second (the key <-> register-slot map is the same on both sides), and O^T keeps
-//     one query per lane, so the online-softmax rescale is per lane too.
-// fp32 kernel: one query per thread, plain FMA, for the fp32 encoder path.
+// bf16 path: the rotation happens once per token, where q and k are produced (the QKV
+// projection's epilogue in the forwards, qkv_prepare_kernel for the stand-alone entry
+// point), which also folds log2(e)/sqrt(hd) into q and writes v transposed; the flash
+// kernel (attn_fwd_kernel) then only streams tiles and runs the two products and the
+// online softmax.
+// fp32 path: one query per thread, plain FMA, RoPE applied as q and k are loaded (tables
+// in LDS), for the fp32 encoder.
 #include "common.h"
 #include "kernels.h"
+#include "rope_tab.h"
 
 namespace jepa {
 
@@ -96,197 +90,94 @@ __device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
 
 // ---------------------------------------------------------------- bf16 / MFMA
 
-// Unsigned division by a runtime constant d >= 1 for n < 2^31 (round-up multiplier:
-// q = (umulhi(n, mul) + n) >> sh with sh = ceil(log2 d), mul = floor(2^32 (2^sh - d) / d) + 1).
-struct FastDiv {
-  uint32_t d, mul, sh;
-};
-
-static FastDiv make_fastdiv(uint32_t d) {
-  FastDiv f{d, 0, 0};
-  while ((1ull << f.sh) < d) ++f.sh;
-  f.mul = static_cast<uint32_t>(((1ull << 32) * ((1ull << f.sh) - d)) / d + 1);
-  return f;
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
-  return (__umulhi(n, f.mul) + n) >> f.sh;
-}
-
-// Grid coordinates of a (clamped) token id.
-__device__ __forceinline__ Thw decode_fast(int id, const FastDiv& dhw, const FastDiv& dw) {
-  Thw g;
-  g.t = static_cast<int>(fdiv(static_cast<uint32_t>(id), dhw));
-  const int rem = id - g.t * static_cast<int>(dhw.d);
-  g.h = static_cast<int>(fdiv(static_cast<uint32_t>(rem), dw));
-  g.w = rem - g.h * static_cast<int>(dw.d);
-  return g;
-}
-
-// Table code of head dim j: (axis << 24) | (axis*kMaxGridSide*MF + frequency index), or
-// -1 for a pass-through dim.  tiled: frequency j mod d/2 within the axis ([Notes §4.1]);
-// interleaved: frequency (j within the axis) / 2 ([Notes §4.2]).
-template <int HD>
-__device__ __forceinline__ int rope_code(int j, int layout) {
-  constexpr int D3 = 2 * ((HD / 3) / 2);
-  constexpr int MF = D3 / 2;
-  if (j >= 3 * D3) return -1;
-  const int a = j / D3, jl = j - a * D3;
-  return (a << 24) | (a * kMaxGridSide * MF + (layout == 0 ? jl % MF : jl >> 1));
-}
-
-// Rotation of one 8-dim chunk of a head vector held in x[8]; code[e] from rope_code.
-// Both dims of a pair always share the axis (d is even).
-template <int MF>
-__device__ __forceinline__ void rope8(float* x, const int* code, const Thw& g, const float2* tab) {
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    if (code[e] < 0) continue;
-    const int ax = code[e] >> 24;
-    const int c = ax == 0 ? g.t : (ax == 1 ? g.h : g.w);
-    const float2 cs0 = tab[(code[e] & 0xFFFFFF) + c * MF];
-    const float2 cs1 = tab[(code[e + 1] & 0xFFFFFF) + c * MF];
-    const float x0 = x[e], x1 = x[e + 1];
-    x[e] = x0 * cs0.x - x1 * cs0.y;
-    x[e + 1] = x1 * cs1.x + x0 * cs1.y;
-  }
-}
-
-// Flash attention, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 softmax and accumulators.
+// Flash attention, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 softmax and accumulators,
+// on inputs prepared once per token (the QKV projection's epilogue or qkv_prepare_kernel):
+// q rotated and scaled by log2(e)/sqrt(hd), k rotated, v transposed per (clip, head) with
+// the keys of each 16-group in vt_pos order.
 //   * a workgroup of 4 wavefronts owns 256 queries of one (clip, head); each wave keeps
-//     two groups of 32, rotated once and pre-scaled by log2(e)/sqrt(hd), as bf16 MFMA B
-//     operands in registers.  256 queries share every key tile, so rotating K on its way
-//     into LDS costs little next to the MFMAs;
-//   * keys and values stream through LDS 64 at a time, double-buffered: the next tile is
-//     fetched into registers while the current one is consumed, then rotated (K) or
-//     transposed (V) into the other buffer; one barrier per tile;
-//   * S^T = K Q^T puts 16 keys of one query in each lane, so the online max and sum are
-//     per lane plus one exchange with the lane 32 away;
-//   * P^T leaves that MFMA already in the B-operand layout of O^T += V^T P^T, whose slot
-//     s of k-step ks is key 16ks + 8(s/4) + 4(l/32) + s%4.  V^T is stored in LDS with the
-//     keys of each 16-group in that order (quads 1 and 2 swapped), so every A operand is
-//     one 16-byte LDS read.
+//     two groups of 32 as bf16 MFMA B operands in registers;
+//   * 64-key tiles of K and V^T stream through a ring of 3 LDS buffers, filled by
+//     global_load_lds_dwordx4 two tiles ahead (no register staging, no VALU); one barrier
+//     per tile;
+//   * S^T = K Q^T puts 16 keys of one query in each lane, so the row max and sum are per
+//     lane plus one exchange with the lane 32 away; every K and V fragment read from LDS
+//     feeds the MFMAs of both query groups;
+//   * P^T leaves that MFMA already in the B-operand layout of O^T += V^T P^T: slot s of
+//     k-step ks holds key 16ks + 8(s/4) + 4(l/32) + s%4, i.e. position vt_pos of the
+//     16-group, the order V^T is stored in, so every A operand is one 16-byte LDS read;
+//   * the running max moves only when a tile's max exceeds it by more than 2^8 (scores are
+//     in log2 units): between moves the probabilities stay in (0, 256] and the output
+//     accumulators are not rescaled.  The first tile sets the max exactly, so the
+//     running sum never underflows.
 template <int HD>
 __global__ __launch_bounds__(256, 2)
-void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out, int N,
-                      int H, const int32_t* __restrict__ ids, RopeSpec r, RopeFreq fr,
-                      float qscale, FastDiv dhw, FastDiv dw, int nqb) {
-  constexpr int D3 = 2 * ((HD / 3) / 2);
-  constexpr int MF = D3 / 2;
-  constexpr int BQ = 256, BKV = 64, NT = 256;
-  constexpr int CH = HD / 8;                 // 16-byte chunks per head row
-  constexpr int KS = HD / 16;                // MFMA k-steps over the head dim
-  constexpr int DT = HD / 32;                // 32-dim blocks of the output
-  constexpr int KCH = BKV * CH / NT;         // K chunks per thread per tile (2 or 1)
-  constexpr int VCH = (BKV / 2) * CH;        // V (2 keys x 8 dims) units per tile
-  constexpr int VP = BKV + 8;                // padded V^T row (keys), 144 B for 64 keys
-  static_assert(BKV * CH % NT == 0, "K tile mapping");
+void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int ld,
+                     const uint16_t* __restrict__ vt, int Ns, uint16_t* __restrict__ out, int N,
+                     int H, int nqb) {
+  constexpr int BQ = 256, BKV = 64, S = 3;
+  constexpr int KS = HD / 16;                   // MFMA k-steps over the head dim
+  constexpr int DT = HD / 32;                   // 32-dim blocks of the output
+  constexpr int KROW = HD * 2;                  // LDS bytes per K row (128 / 64)
+  constexpr int K_BYTES = BKV * KROW, V_BYTES = HD * BKV * 2;
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int K_RPI = 1024 / KROW;            // K rows per 1 KB DMA instruction
+  constexpr int K_CPR = KROW / 16;              // 16-byte chunks per K row
+  constexpr int K_DMA = K_BYTES / 4096;         // DMA instructions per wave and tile
+  constexpr int V_DMA = V_BYTES / 4096;
+  constexpr int LOADS = K_DMA + V_DMA;
+  constexpr float TAU = 8.0f;
+  static_assert(K_DMA * 4096 == K_BYTES && V_DMA * 4096 == V_BYTES, "DMA split");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S * STAGE];
 
-  __shared__ float2 tab[3 * kMaxGridSide * MF];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * VP];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hh = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
   // Work-groups are dealt to the 8 XCDs round-robin; renumber them so that the query
   // blocks of one (clip, head), which read the same keys and values, share an XCD's L2.
   int wg = blockIdx.x;
   if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
   const int qblk = wg % nqb, bh = wg / nqb;
   const int head = bh % H, b = bh / H;
-  const int D = H * HD, ld = 3 * D;
-  const int ntot = r.gt * r.gh * r.gw;
-  const uint16_t* base = qkv + static_cast<size_t>(b) * N * ld + head * HD;
+  const int D = H * HD;
 
-  build_rope_tables<MF>(tab, r, fr);
+  // K rows are 128 B (hd 64) or 64 B (hd 32); chunk c of row r sits at c ^ kkey(r)
+  auto kkey = [](int r) { return HD == 64 ? (r & 7) : ((r >> 1) & 3); };
+  const int krow_l = lane / K_CPR, kchunk_l = (lane % K_CPR) ^ kkey(lane / K_CPR);
+  const int vrow_l = lane >> 3, vchunk_l = (lane & 7) ^ (vrow_l & 7);
+  const uint32_t sbase = lds_addr(smem);
+  const uint16_t* kbase = k + static_cast<size_t>(b) * N * ld + head * HD;
+  const uint16_t* vbase = vt + static_cast<size_t>(b * H + head) * HD * Ns;
+  const int ntiles = (N + BKV - 1) / BKV;
 
-  // per-thread constants of the K chunks this thread rotates: chunk c = tid % CH
-  const int kc = tid % CH;
-  int kcode[8];
+  // Tile t into buffer t % S: K rows past N repeat row N - 1 (their scores are masked);
+  // V^T rows read 64 keys from position 64t on (the caller's buffer holds them: see
+  // launch_attention_fwd); positions of keys past N are zeroed in LDS below.
+  auto issue = [&](int t) {
+    const uint32_t st = sbase + (t % S) * STAGE;
+    const int kb = t * BKV;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) kcode[e] = rope_code<HD>(kc * 8 + e, r.layout);
-  __syncthreads();
+    for (int qd = 0; qd < K_DMA; ++qd) {
+      const int g = qd * 4 + wave;
+      const int key = min(kb + g * K_RPI + krow_l, N - 1);
+      dma16(kbase, static_cast<uint32_t>(key) * ld * 2 + kchunk_l * 16, st + g * 1024);
+    }
+#pragma unroll
+    for (int qd = 0; qd < V_DMA; ++qd) {
+      const int g = qd * 4 + wave;
+      const int dim = g * 8 + vrow_l;
+      dma16(vbase, (static_cast<uint32_t>(dim) * Ns + kb) * 2 + vchunk_l * 16, st + K_BYTES + g * 1024);
+    }
+  };
 
-  // ---- queries: two groups of 32 per wave, rotated, scaled, bf16 B operands
+  // ---- queries: two groups of 32 per wave, B operands (dims 16kk + 8h .. +8)
   bf16x8 qf[2][KS];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int q = qblk * BQ + wave * 64 + g * 32 + l32;
-    const int qr = min(q, N - 1);
-    int id = ids ? ids[qr] : qr;
-    id = min(max(id, 0), ntot - 1);
-    const Thw gq = decode_fast(id, dhw, dw);
-    const uint16_t* src = base + static_cast<size_t>(qr) * ld;
+    const int qr = min(qblk * BQ + wave * 64 + g * 32 + l32, N - 1);
+    const uint16_t* src = q + (static_cast<size_t>(b) * N + qr) * ld + head * HD;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int c = kk * 2 + hh;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + c * 8);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = bf16_to_f32(static_cast<uint16_t>(raw[e] & 0xFFFF));
-        x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(raw[e] >> 16));
-      }
-      int qcode[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qcode[e] = rope_code<HD>(c * 8 + e, r.layout);
-      rope8<MF>(x, qcode, gq, tab);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[g][kk][e] = static_cast<__bf16>(x[e] * qscale);
-    }
+    for (int kk = 0; kk < KS; ++kk) qf[g][kk] = *reinterpret_cast<const bf16x8*>(src + (2 * kk + h) * 8);
   }
-
-  // ---- tile staging: global -> registers -> (rotate / transpose) -> LDS
-  u32x4 kraw[KCH];
-  int kid[KCH];
-  u32x4 vraw0, vraw1;
-  const int vkp = tid % (BKV / 2), vc = tid / (BKV / 2);   // V: key pair, dim chunk
-  auto fetch = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int key = (tid + i * NT) / CH;
-      const int kr = min(kb + key, N - 1);
-      int id = ids ? ids[kr] : kr;
-      kid[i] = min(max(id, 0), ntot - 1);
-      kraw[i] = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(kr) * ld + D + kc * 8);
-    }
-    if (tid < VCH) {
-      const int k0 = min(kb + 2 * vkp, N - 1), k1 = min(kb + 2 * vkp + 1, N - 1);
-      vraw0 = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(k0) * ld + 2 * D + vc * 8);
-      vraw1 = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(k1) * ld + 2 * D + vc * 8);
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int key = (tid + i * NT) / CH;
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = bf16_to_f32(static_cast<uint16_t>(kraw[i][e] & 0xFFFF));
-        x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(kraw[i][e] >> 16));
-      }
-      rope8<MF>(x, kcode, decode_fast(kid[i], dhw, dw), tab);
-      u32x4 p;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-      const int sw = (HD == 64) ? (kc ^ (key & 7)) : (kc ^ ((key >> 1) & 3));
-      *reinterpret_cast<u32x4*>(&Ks[buf][key * HD + sw * 8]) = p;
-    }
-    if (tid < VCH) {
-      // keys 2vkp, 2vkp+1 go to the pair slot of the quad-swapped order
-      const int k2 = 2 * vkp;
-      const int quad = (k2 >> 2) & 3;
-      const int pos = (k2 & ~15) | (((quad == 1) ? 2 : (quad == 2) ? 1 : quad) << 2) | (k2 & 3);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (vraw0[e] & 0xFFFFu) | (vraw1[e] << 16);
-        const uint32_t hi = (vraw0[e] >> 16) | (vraw1[e] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(&Vt[buf][(vc * 8 + 2 * e) * VP + pos]) = lo;
-        *reinterpret_cast<uint32_t*>(&Vt[buf][(vc * 8 + 2 * e + 1) * VP + pos]) = hi;
-      }
-    }
-  };
 
   f32x16 o[2][DT];
 #pragma unroll
@@ -295,88 +186,118 @@ void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[g][dt][i] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[2] = {0.f, 0.f}, l_run[2] = {0.f, 0.f};
 
-  const int ntiles = (N + BKV - 1) / BKV;
-  fetch(0);
-  stage(0);
-  __syncthreads();
+  int issued = 0;
+  for (; issued < S - 1 && issued < ntiles; ++issued) issue(issued);
   for (int t = 0; t < ntiles; ++t) {
-    const int kb = t * BKV, buf = t & 1;
-    if (t + 1 < ntiles) fetch(kb + BKV);
-    const uint16_t* Kb = Ks[buf];
-    const uint16_t* Vb = Vt[buf];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      // S^T = K Q^T for keys [kb, kb + 64): two 32-key blocks
-      f32x16 sc[2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[t2][i] = 0.f;
-        const int key = t2 * 32 + l32;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const int c = kk * 2 + hh;
-          const int sw = (HD == 64) ? (c ^ (key & 7)) : (c ^ ((key >> 1) & 3));
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + key * HD + sw * 8);
-          sc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][kk], sc[t2], 0, 0, 0);
-        }
+    // tile t has landed once at most issued - 1 - t later tiles are still in flight
+    if (issued - 1 - t >= 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int kb = t * BKV;
+    unsigned char* st = smem + (t % S) * STAGE;
+    if (kb + BKV > N) {
+      // ragged last tile: zero the V^T positions of keys past N (P is 0 there, and the
+      // words read past the clip's keys need not be finite)
+      for (int e = tid; e < HD * BKV; e += 256) {
+        const int dim = e / BKV, pos = e - dim * BKV;
+        if (kb + vt_pos(pos) >= N)
+          *reinterpret_cast<uint16_t*>(st + K_BYTES + dim * 128 + ((((pos >> 3) ^ (dim & 7))) << 4) + (pos & 7) * 2) = 0;
       }
-      // element i of sc[t2] is key kb + 32 t2 + 8(i/4) + 4 hh + i%4 of this lane's query
-      if (kb + BKV > N) {
+      __syncthreads();
+    }
+    // the buffer of tile t - 1 is free: every wave finished it before the barrier
+    if (issued < ntiles) {
+      issue(issued);
+      ++issued;
+    }
+
+    // S^T = K Q^T for the 64 keys: element i of sc[g][t2] is key
+    // kb + 32 t2 + 8(i/4) + 4h + i%4 of query l32 of group g
+    f32x16 sc[2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[g][t2][i] = 0.f;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int r = t2 * 32 + l32;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + r * KROW + (((2 * kk + h) ^ kkey(r)) << 4));
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          sc[g][t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][kk], sc[g][t2], 0, 0, 0);
+      }
+    }
+    if (kb + BKV > N) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (kb + t2 * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= N) sc[t2][i] = -INFINITY;
-      }
-      float mx = fmaxf(sc[0][0], sc[1][0]);
+            if (kb + t2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3) >= N) sc[g][t2][i] = -INFINITY;
+    }
+
+    bf16x8 pf[2][4];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sc[0][i], sc[1][i]));
+    for (int g = 0; g < 2; ++g) {
+      float mx = fmaxf(sc[g][0][0], sc[g][1][0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sc[g][0][i], sc[g][1][i]));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[g], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-      m_run[g] = m_new;
+      if (t == 0) {
+        m_run[g] = mx;
+      } else if (__ballot(mx - m_run[g] > TAU) != 0) {
+        const float d = mx - m_run[g] > TAU ? mx - m_run[g] : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-d);
+        m_run[g] += d;
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[g][dt][i] *= alpha;
+      }
+      const float m = m_run[g];
       float ls = 0.f;
-      bf16x8 pf[4];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(sc[t2][i] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(sc[g][t2][i] - m);
           ls += pv;
-          pf[t2 * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(pv);
+          pf[g][t2 * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(pv);
         }
-      l_run[g] = l_run[g] * alpha + ls;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[g][dt][i] *= alpha;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int dim = dt * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vb + dim * VP + ks * 16 + hh * 8);
-          o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[g][dt], 0, 0, 0);
-        }
-      }
-      // keep the two query groups apart: their score blocks are never live together
-      __builtin_amdgcn_sched_barrier(0);
+      l_run[g] += ls;
     }
-    if (t + 1 < ntiles) stage(buf ^ 1);
-    __syncthreads();
+
+    // O^T += V^T P^T: the A operand is V^T dims 32dt + l32, positions 16ks + 8h .. +8
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dim = dt * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + K_BYTES + dim * 128 + (((2 * ks + h) ^ (dim & 7)) << 4));
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g][ks], o[g][dt], 0, 0, 0);
+      }
+    }
   }
 
-  // ---- normalise and store: element i of o[g][dt] is dim 32 dt + 8(i/4) + 4 hh + i%4
+  // ---- normalise and store: element i of o[g][dt] is dim 32 dt + 8(i/4) + 4h + i%4
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int q = qblk * BQ + wave * 64 + g * 32 + l32;
+    const int qi = qblk * BQ + wave * 64 + g * 32 + l32;
     const float inv = 1.0f / (l_run[g] + __shfl_xor(l_run[g], 32));
-    if (q < N) {
-      uint16_t* dst = out + (static_cast<size_t>(b) * N + q) * D + head * HD;
+    if (qi < N) {
+      uint16_t* dst = out + (static_cast<size_t>(b) * N + qi) * D + head * HD;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -384,10 +305,83 @@ void attn_bf16_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o
           u32x2 pk;
           pk[0] = pack_bf16x2(o[g][dt][4 * g4] * inv, o[g][dt][4 * g4 + 1] * inv);
           pk[1] = pack_bf16x2(o[g][dt][4 * g4 + 2] * inv, o[g][dt][4 * g4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g4 + 4 * hh) = pk;
+          *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g4 + 4 * h) = pk;
         }
     }
   }
+}
+
+hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
+                                int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
+                                hipStream_t s) {
+  if (B <= 0 || N <= 0) return hipSuccess;
+  if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N) || Ns % 16 || ld % 8) return hipErrorInvalidValue;
+  // 32-bit DMA offsets: one clip's rows of q/k and one (clip, head)'s V^T rows
+  if (static_cast<size_t>(N) * ld * 2 >= (size_t(1) << 31) ||
+      static_cast<size_t>(head_dim) * Ns * 2 >= (size_t(1) << 31))
+    return hipErrorInvalidValue;
+  const int nqb = (N + 255) / 256;
+  const dim3 grid(nqb * n_head * B);
+  if (head_dim == 64)
+    attn_fwd_kernel<64><<<grid, 256, 0, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb);
+  else
+    attn_fwd_kernel<32><<<grid, 256, 0, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb);
+  return hipGetLastError();
+}
+
+// Attention inputs from a projection already in memory (the stand-alone entry point):
+// thread i handles 4 consecutive columns of one row of qkv [M, 3D]: q and k are rotated
+// (q also scaled) into qk [M, 2D], v goes to vt as in the QKV epilogue.
+template <int HD>
+__global__ __launch_bounds__(256)
+void qkv_prepare_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ qk,
+                        uint16_t* __restrict__ vt, int Ns, long long M, int D, RopeArgs ra,
+                        float qscale) {
+  const int gpr = 3 * D / 4;  // 4-column groups per row
+  const long long total = M * gpr;
+  for (long long e = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const int row = static_cast<int>(e / gpr);
+    const int col = static_cast<int>(e - static_cast<long long>(row) * gpr) * 4;
+    const int sec = col / D, cin = col - sec * D;
+    const int head = cin / HD, jj = cin - head * HD;
+    const u32x2 raw = *reinterpret_cast<const u32x2*>(qkv + static_cast<size_t>(row) * 3 * D + col);
+    float v[4] = {bf16_to_f32(static_cast<uint16_t>(raw[0] & 0xFFFF)), bf16_to_f32(static_cast<uint16_t>(raw[0] >> 16)),
+                  bf16_to_f32(static_cast<uint16_t>(raw[1] & 0xFFFF)), bf16_to_f32(static_cast<uint16_t>(raw[1] >> 16))};
+    int clip;
+    const Thw g = rope_token(row, ra, &clip);
+    if (sec < 2) {
+      rope_pair<HD>(v[0], v[1], jj, g, ra.layout, ra.tab);
+      rope_pair<HD>(v[2], v[3], jj + 2, g, ra.layout, ra.tab);
+      if (sec == 0)
+        for (int i = 0; i < 4; ++i) v[i] *= qscale;
+      u32x2 pk;
+      pk[0] = pack_bf16x2(v[0], v[1]);
+      pk[1] = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<u32x2*>(qk + static_cast<size_t>(row) * 2 * D + col) = pk;
+    } else {
+      const int n = row - clip * ra.N;
+      uint16_t* dst = vt + (static_cast<size_t>(clip * (D / HD) + head) * HD + jj) * Ns + vt_pos(n);
+      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(i) * Ns] = f32_to_bf16(v[i]);
+    }
+  }
+}
+
+hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, int Ns, int B,
+                              int N, int n_head, int head_dim, const int32_t* ids,
+                              const RopeSpec& r, const void* tab, float qscale, hipStream_t s) {
+  if (B <= 0 || N <= 0) return hipSuccess;
+  if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N)) return hipErrorInvalidValue;
+  const int D = n_head * head_dim;
+  const RopeArgs ra{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw};
+  const long long M = static_cast<long long>(B) * N;
+  const long long total = M * (3 * D / 4);
+  const dim3 grid(static_cast<unsigned>(min(total, 256LL * 2048) / 256 + 1));
+  if (head_dim == 64)
+    qkv_prepare_kernel<64><<<grid, 256, 0, s>>>(qkv, qk, vt, Ns, M, D, ra, qscale);
+  else
+    qkv_prepare_kernel<32><<<grid, 256, 0, s>>>(qkv, qk, vt, Ns, M, D, ra, qscale);
+  return hipGetLastError();
 }
 
 static RopeFreq make_freq(int head_dim, float theta) {
@@ -396,25 +390,6 @@ static RopeFreq make_freq(int head_dim, float theta) {
   for (int k = 0; k < m && k < 16; ++k)
     f.w[k] = static_cast<float>(1.0 / pow(static_cast<double>(theta), static_cast<double>(k) / m));
   return f;
-}
-
-hipError_t launch_attention_bf16(const uint16_t* qkv, uint16_t* out, int B, int N, int n_head,
-                                 int head_dim, const int32_t* ids, const RopeSpec& r,
-                                 hipStream_t s) {
-  if (B <= 0 || N <= 0) return hipSuccess;
-  const RopeFreq fr = make_freq(head_dim, r.theta);
-  const float qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
-  const FastDiv dhw = make_fastdiv(static_cast<uint32_t>(r.gh * r.gw));
-  const FastDiv dw = make_fastdiv(static_cast<uint32_t>(r.gw));
-  const int nqb = (N + 255) / 256;
-  const dim3 grid(nqb * n_head * B);
-  if (head_dim == 64)
-    attn_bf16_kernel<64><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale, dhw, dw, nqb);
-  else if (head_dim == 32)
-    attn_bf16_kernel<32><<<grid, 256, 0, s>>>(qkv, out, N, n_head, ids, r, fr, qscale, dhw, dw, nqb);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- fp32 / FMA

@@ -26,10 +26,24 @@
 // fp32 path: a plain 64x64-tile FMA kernel (no MFMA), used by the fp32 encoder.
 #include "common.h"
 #include "kernels.h"
+#include "rope_tab.h"
 
 namespace jepa {
 
-enum { EPI_STORE = 0, EPI_GELU = 1, EPI_RESIDUAL = 2 };
+enum { EPI_STORE = 0, EPI_GELU = 1, EPI_RESIDUAL = 2, EPI_QKV64 = 3, EPI_QKV32 = 4 };
+
+// Arguments of the QKV epilogue (EPI_QKV64 / EPI_QKV32 for head dim 64 / 32): columns
+// [0, D) are q, [D, 2D) k, [2D, 3D) v of D = H * hd.  q and k are rotated by the 3-D RoPE
+// of the row's token ([Notes §4]) and q is scaled by qscale; both are stored in place.
+// v goes to vt [clip][head][dim][Ns], key n of a clip at position vt_pos(n).
+// The epilogue reads the RoPE table from LDS: rows (axis, coord < ts) of the full table
+// are copied after the slab ring at kernel start (3 * ts * kRopeMaxFreq float2).
+struct QkvEpi {
+  uint16_t* vt;
+  RopeArgs ra;
+  int D, H, Ns, ts;
+  float qscale;
+};
 
 // GELU with erf from Abramowitz & Stegun 7.1.26 (|error of erf| <= 1.5e-7, far below
 // the bf16 rounding of the output): erf(x) = 1 - t(a1 + t(a2 + ...)) exp(-x^2),
@@ -74,11 +88,14 @@ using Cfg256x256 = GemmCfg<256, 256, 2, 2, 4>;
 using Cfg256x192 = GemmCfg<256, 192, 2, 4, 2>;
 // 256 x 128: every other width that is a multiple of 128
 using Cfg256x128 = GemmCfg<256, 128, 3, 4, 2>;
+// 256 x 128 with a 2-buffer ring: leaves LDS for the RoPE table of the QKV epilogue
+using Cfg256x128q = GemmCfg<256, 128, 2, 4, 2>;
 
 template <class C, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(C::NT)
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                      const float* __restrict__ bias, void* __restrict__ Cv, int M, int N, int K) {
+                      const float* __restrict__ bias, void* __restrict__ Cv, int M, int N, int K,
+                      QkvEpi qe) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STAGES = C::STAGES, NWAVES = C::NWAVES;
   constexpr int FI = C::FI, FJ = C::FJ, WM = C::WM, WN = C::WN;
   constexpr int A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS;
@@ -206,6 +223,15 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   // whose reads all completed before the barrier.  Up to STAGES - 1 slabs are in flight
   // while a slab is consumed.
   constexpr int KSTEPS = BK / 16;
+  if constexpr (EPI == EPI_QKV64 || EPI == EPI_QKV32) {
+    // RoPE table rows (axis, coord < ts) after the ring; the prologue's barrier publishes them
+    float2* tabs = reinterpret_cast<float2*>(smem + C::LDS);
+    const int n = 3 * qe.ts * kRopeMaxFreq;
+    for (int e = tid; e < n; e += C::NT) {
+      const int a = e / (qe.ts * kRopeMaxFreq), rest = e - a * qe.ts * kRopeMaxFreq;
+      tabs[e] = qe.ra.tab[a * kMaxGridSide * kRopeMaxFreq + rest];
+    }
+  }
   if (total > 0) set_rows(0);
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
@@ -258,6 +284,57 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     // consecutive output columns per lane.
     int m0, n0;
     tile_of(it, m0, n0);
+    if constexpr (EPI == EPI_QKV64 || EPI == EPI_QKV32) {
+      constexpr int HD = EPI == EPI_QKV64 ? 64 : 32;
+      const float2* tabs = reinterpret_cast<const float2*>(smem + C::LDS);
+      Thw g[FI];
+      int clip[FI], nn[FI];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const int row = min(m0 + wm * WM + i * 32 + l32, M - 1);
+        g[i] = rope_token(row, qe.ra, &clip[i]);
+        nn[i] = row - clip[i] * qe.ra.N;
+      }
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        // a 32-column block lies inside one third (q, k or v) and one head
+        const int col0 = n0 + wn * WN + j * 32;
+        const int sec = col0 / qe.D, cin = col0 - sec * qe.D;
+        const int head = cin / HD, jb = cin - head * HD;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = col0 + 8 * gq + 4 * h, jj = jb + 8 * gq + 4 * h;
+          const f32x4 bv = bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+          const RopePairIdx p0 = rope_pair_idx<HD>(jj, qe.ra.layout);
+          const RopePairIdx p1 = rope_pair_idx<HD>(jj + 2, qe.ra.layout);
+#pragma unroll
+          for (int i = 0; i < FI; ++i) {
+            const int row = m0 + wm * WM + i * 32 + l32;
+            if (row >= M) continue;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e] + bv[e];
+            if (sec < 2) {
+              rope_apply(v[0], v[1], p0, g[i], tabs, qe.ts);
+              rope_apply(v[2], v[3], p1, g[i], tabs, qe.ts);
+              if (sec == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= qe.qscale;
+              }
+              u32x2 pk;
+              pk[0] = pack_bf16x2(v[0], v[1]);
+              pk[1] = pack_bf16x2(v[2], v[3]);
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cv) + static_cast<size_t>(row) * N + col) = pk;
+            } else {
+              uint16_t* dst = qe.vt + (static_cast<size_t>(clip[i] * qe.H + head) * HD + jj) * qe.Ns + vt_pos(nn[i]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dst[static_cast<size_t>(e) * qe.Ns] = f32_to_bf16(v[e]);
+            }
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
       const int row = m0 + wm * WM + i * 32 + l32;
@@ -308,17 +385,21 @@ static int num_cus() {
 
 template <class C, int EPI, bool OUT_F32>
 static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float* bias, void* Cp,
-                              int M, int N, int K, hipStream_t s) {
+                              int M, int N, int K, hipStream_t s, const QkvEpi& qe = QkvEpi{}) {
+  constexpr bool QKV = EPI == EPI_QKV64 || EPI == EPI_QKV32;
+  constexpr int MAX_LDS = QKV ? 160 * 1024 : C::LDS;
+  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kRopeMaxFreq * 8 <= MAX_LDS, "LDS for the RoPE table");
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI, OUT_F32>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, MAX_LDS);
     if (e != hipSuccess) return e;
     configured = true;
   }
+  const int lds = C::LDS + (QKV ? 3 * qe.ts * kRopeMaxFreq * 8 : 0);
   const int tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
   const dim3 grid(min(tiles, num_cus()));
-  gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, C::LDS, s>>>(A, W, bias, Cp, M, N, K);
+  gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, lds, s>>>(A, W, bias, Cp, M, N, K, qe);
   return hipGetLastError();
 }
 
@@ -333,23 +414,63 @@ static hipError_t gemm_dispatch(const uint16_t* A, const uint16_t* W, const floa
                  : gemm_launch<C, EPI_STORE, false>(A, W, bias, Cp, M, N, K, s);
 }
 
+// The widest tile whose count still fills whole rounds of the CUs (fewer, larger tiles
+// cut the bytes each CU pulls through L2 per MFMA): 256 = 256 x 256, 192, else 128.
+static int tile_width(int M, int N) {
+  const int cus = num_cus();
+  const int tm = (M + 255) / 256;
+  if (N % 256 == 0 && tm * (N / 256) >= cus && (tm * (N / 256)) % cus == 0) return 256;
+  if (N % 192 == 0 && tm * (N / 192) >= cus && (tm * (N / 192)) % cus == 0) return 192;
+  return 128;
+}
+
+static bool gemm_shape_ok(int M, int N, int K) {
+  // N in whole 128-column tiles, K in whole slabs; the DMA addressing uses 32-bit byte
+  // offsets
+  return N % 128 == 0 && K % 64 == 0 && static_cast<size_t>(M) * K * 2 < (size_t(1) << 31) &&
+         static_cast<size_t>(N) * K * 2 < (size_t(1) << 31);
+}
+
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C,
                             int M, int N, int K, int epi, int out_f32, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (N % 128 || K % 64) return hipErrorInvalidValue;
-  // the DMA addressing uses 32-bit byte offsets
-  if (static_cast<size_t>(M) * K * 2 >= (size_t(1) << 31) ||
-      static_cast<size_t>(N) * K * 2 >= (size_t(1) << 31))
-    return hipErrorInvalidValue;
-  // The widest tile whose count still fills whole rounds of the CUs (fewer, larger tiles
-  // cut the bytes each CU pulls through L2 per MFMA).
-  const int cus = num_cus();
-  const int tm = (M + 255) / 256;
-  if (N % 256 == 0 && tm * (N / 256) >= cus && (tm * (N / 256)) % cus == 0)
-    return gemm_dispatch<Cfg256x256>(A, W, bias, C, M, N, K, epi, out_f32, s);
-  if (N % 192 == 0 && tm * (N / 192) >= cus && (tm * (N / 192)) % cus == 0)
-    return gemm_dispatch<Cfg256x192>(A, W, bias, C, M, N, K, epi, out_f32, s);
+  if (!gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
+  const int tw = tile_width(M, N);
+  if (tw == 256) return gemm_dispatch<Cfg256x256>(A, W, bias, C, M, N, K, epi, out_f32, s);
+  if (tw == 192) return gemm_dispatch<Cfg256x192>(A, W, bias, C, M, N, K, epi, out_f32, s);
   return gemm_dispatch<Cfg256x128>(A, W, bias, C, M, N, K, epi, out_f32, s);
+}
+
+template <class C>
+static hipError_t gemm_qkv_dispatch(const uint16_t* A, const uint16_t* W, const float* bias,
+                                    uint16_t* Cp, int M, int N, int K, int head_dim,
+                                    const QkvEpi& qe, hipStream_t s) {
+  if (head_dim == 64) return gemm_launch<C, EPI_QKV64, false>(A, W, bias, Cp, M, N, K, s, qe);
+  return gemm_launch<C, EPI_QKV32, false>(A, W, bias, Cp, M, N, K, s, qe);
+}
+
+hipError_t launch_gemm_bf16_qkv(const uint16_t* A, const uint16_t* W, const float* bias,
+                                uint16_t* C, uint16_t* vt, int Ns, int M, int D, int K,
+                                int head_dim, const int32_t* ids, int N, const RopeSpec& r,
+                                const void* tab, float qscale, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  const int Ncol = 3 * D;
+  if (!gemm_shape_ok(M, Ncol, K) || (head_dim != 64 && head_dim != 32) || D % head_dim ||
+      D % 32 || N <= 0 || M % N || Ns < N)
+    return hipErrorInvalidValue;
+  QkvEpi qe;
+  qe.vt = vt;
+  qe.ra = RopeArgs{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw};
+  qe.D = D;
+  qe.H = D / head_dim;
+  qe.Ns = Ns;
+  qe.ts = max(r.gt, max(r.gh, r.gw));
+  qe.qscale = qscale;
+  if (qe.ts > kMaxGridSide) return hipErrorInvalidValue;
+  const int tw = tile_width(M, Ncol);
+  if (tw == 256) return gemm_qkv_dispatch<Cfg256x256>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
+  if (tw == 192) return gemm_qkv_dispatch<Cfg256x192>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
+  return gemm_qkv_dispatch<Cfg256x128q>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
 }
 
 // ---------------------------------------------------------------- fp32 path

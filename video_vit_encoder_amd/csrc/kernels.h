@@ -16,6 +16,10 @@ struct RopeSpec {
 
 // Largest grid side the attention kernels keep RoPE tables for.
 constexpr int kMaxGridSide = 64;
+// Frequencies per axis the RoPE tables hold (d/2 <= 16, i.e. head dims up to 96).
+constexpr int kRopeMaxFreq = 16;
+// Entries of a RoPE table (float2 each): 3 axes x kMaxGridSide coordinates x kRopeMaxFreq.
+constexpr int kRopeTabEntries = 3 * kMaxGridSide * kRopeMaxFreq;
 
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* bias, void* C,
                             int M, int N, int K, int epi, int out_f32, hipStream_t s);
@@ -26,9 +30,31 @@ hipError_t launch_layernorm(const float* x, const float* w, const float* b, int 
 hipError_t launch_rope3d(const void* x, void* y, int bf16, int B, int N, int n_head,
                          int head_dim, int64_t row_stride, const int32_t* ids,
                          const RopeSpec& r, hipStream_t s);
-hipError_t launch_attention_bf16(const uint16_t* qkv, uint16_t* out, int B, int N, int n_head,
-                                 int head_dim, const int32_t* ids, const RopeSpec& r,
-                                 hipStream_t s);
+// (cos, sin) table of the grid for head dim head_dim (layout in rope_tab.h).
+hipError_t launch_rope_table(void* tab, const RopeSpec& r, int head_dim, hipStream_t s);
+// QKV projection (bf16) whose epilogue rotates q and k, scales q by qscale and writes v
+// transposed: q, k into C [M, 3D] (columns [0, 2D)), v into vt [B][H][hd][Ns].
+hipError_t launch_gemm_bf16_qkv(const uint16_t* A, const uint16_t* W, const float* bias,
+                                uint16_t* C, uint16_t* vt, int Ns, int M, int D, int K,
+                                int head_dim, const int32_t* ids, int N, const RopeSpec& r,
+                                const void* tab, float qscale, hipStream_t s);
+// The same preparation from a projection already in memory: qkv [M, 3D] bf16 ->
+// q', k' into qk [M, 2D] and v into vt [B][H][hd][Ns].
+hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, int Ns, int B,
+                              int N, int n_head, int head_dim, const int32_t* ids,
+                              const RopeSpec& r, const void* tab, float qscale, hipStream_t s);
+// Flash attention on prepared inputs: q (rotated, scaled by log2(e)/sqrt(hd)) and k
+// (rotated) rows of leading dimension ld (elements), v transposed [B][H][hd][Ns];
+// out [B*N, H*hd] bf16.
+hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
+                                int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
+                                hipStream_t s);
+// Row stride (keys) of the transposed V layout for N tokens.
+inline int vt_stride(int N) { return (N + 15) / 16 * 16; }
+// Scale folded into q: log2(e) / sqrt(head_dim).
+inline float attn_qscale(int head_dim) {
+  return static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(head_dim)));
+}
 hipError_t launch_attention_f32(const float* qkv, float* out, int B, int N, int n_head,
                                 int head_dim, const int32_t* ids, const RopeSpec& r,
                                 hipStream_t s);

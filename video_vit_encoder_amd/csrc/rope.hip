@@ -108,4 +108,35 @@ hipError_t launch_rope3d(const void* x, void* y, int bf16, int B, int N, int n_h
   return hipGetLastError();
 }
 
+// (cos, sin) table of one grid for the RoPE-by-table helpers of rope_tab.h: entry
+// (axis, coord, k) = p_axis(coord) * omega_k with the angle formed in fp64 and its cos/sin
+// rounded to fp32, as in rope3d_kernel.  Entries past the grid side or past d/2
+// frequencies hold (1, 0).
+__global__ __launch_bounds__(256)
+void rope_table_kernel(float2* __restrict__ tab, RopeSpec r, RopeOmega om, int mf) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= kRopeTabEntries) return;
+  const int k = e % kRopeMaxFreq, rest = e / kRopeMaxFreq;
+  const int coord = rest % kMaxGridSide, axis = rest / kMaxGridSide;
+  const int side = axis == 0 ? r.gt : (axis == 1 ? r.gh : r.gw);
+  float2 v = make_float2(1.f, 0.f);
+  if (k < mf && coord < side) {
+    double p = coord;
+    if (axis > 0 && r.ref_grid > 0) p = p * (r.ref_grid - 1) / (side - 1);
+    double sv, cv;
+    sincos(p * om.w[k], &sv, &cv);
+    v = make_float2(static_cast<float>(cv), static_cast<float>(sv));
+  }
+  tab[e] = v;
+}
+
+hipError_t launch_rope_table(void* tab, const RopeSpec& r, int head_dim, hipStream_t s) {
+  const int m = (2 * ((head_dim / 3) / 2)) / 2;
+  if (m > kRopeMaxFreq) return hipErrorInvalidValue;
+  RopeOmega om{};
+  for (int k = 0; k < m; ++k) om.w[k] = 1.0 / pow(static_cast<double>(r.theta), static_cast<double>(k) / m);
+  rope_table_kernel<<<(kRopeTabEntries + 255) / 256, 256, 0, s>>>(static_cast<float2*>(tab), r, om, m);
+  return hipGetLastError();
+}
+
 }  // namespace jepa
