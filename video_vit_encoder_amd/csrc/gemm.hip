@@ -301,34 +301,61 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
         const int col0 = n0 + wn * WN + j * 32;
         const int sec = col0 / qe.D, cin = col0 - sec * qe.D;
         const int head = cin / HD, jb = cin - head * HD;
+        // this lane's columns col0 + 8gq + 4h .. +3: bias and the table coordinates of
+        // their two pairs
+        f32x4 bv[4];
+        RopePairIdx pidx[4][2];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int col = col0 + 8 * gq + 4 * h, jj = jb + 8 * gq + 4 * h;
-          const f32x4 bv = bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-          const RopePairIdx p0 = rope_pair_idx<HD>(jj, qe.ra.layout);
-          const RopePairIdx p1 = rope_pair_idx<HD>(jj + 2, qe.ra.layout);
+          bv[gq] = bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+          pidx[gq][0] = rope_pair_idx<HD>(jj, qe.ra.layout);
+          pidx[gq][1] = rope_pair_idx<HD>(jj + 2, qe.ra.layout);
+        }
 #pragma unroll
-          for (int i = 0; i < FI; ++i) {
-            const int row = m0 + wm * WM + i * 32 + l32;
-            if (row >= M) continue;
-            float v[4];
+        for (int i = 0; i < FI; ++i) {
+          const int row = m0 + wm * WM + i * 32 + l32;
+          if (row >= M) continue;
+          if (sec < 2) {
+            // all table reads of the row first, so their LDS latency overlaps
+            float2 cs[4][2][2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e] + bv[e];
-            if (sec < 2) {
-              rope_apply(v[0], v[1], p0, g[i], tabs, qe.ts);
-              rope_apply(v[2], v[3], p1, g[i], tabs, qe.ts);
-              if (sec == 0) {
+            for (int gq = 0; gq < 4; ++gq)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] *= qe.qscale;
+              for (int pp = 0; pp < 2; ++pp) {
+                const RopePairIdx& pi = pidx[gq][pp];
+                const int c = pi.axis == 0 ? g[i].t : (pi.axis == 1 ? g[i].h : g[i].w);
+                const float2* tr = tabs + (pi.axis * qe.ts + c) * kRopeMaxFreq;
+                cs[gq][pp][0] = pi.rot ? tr[pi.i0] : make_float2(1.f, 0.f);
+                cs[gq][pp][1] = pi.rot ? tr[pi.i1] : make_float2(1.f, 0.f);
+              }
+            const float sc = sec == 0 ? qe.qscale : 1.0f;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = col0 + 8 * gq + 4 * h;
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e] + bv[gq][e];
+              float y[4];
+#pragma unroll
+              for (int pp = 0; pp < 2; ++pp) {
+                const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
+                const float2 c0 = cs[gq][pp][0], c1 = cs[gq][pp][1];
+                y[2 * pp] = (x0 * c0.x - x1 * c0.y) * sc;
+                y[2 * pp + 1] = (x1 * c1.x + x0 * c1.y) * sc;
               }
               u32x2 pk;
-              pk[0] = pack_bf16x2(v[0], v[1]);
-              pk[1] = pack_bf16x2(v[2], v[3]);
+              pk[0] = pack_bf16x2(y[0], y[1]);
+              pk[1] = pack_bf16x2(y[2], y[3]);
               *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cv) + static_cast<size_t>(row) * N + col) = pk;
-            } else {
+            }
+          } else {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int jj = jb + 8 * gq + 4 * h;
               uint16_t* dst = qe.vt + (static_cast<size_t>(clip[i] * qe.H + head) * HD + jj) * qe.Ns + vt_pos(nn[i]);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) dst[static_cast<size_t>(e) * qe.Ns] = f32_to_bf16(v[e]);
+              for (int e = 0; e < 4; ++e) dst[static_cast<size_t>(e) * qe.Ns] = f32_to_bf16(acc[i][j][4 * gq + e] + bv[gq][e]);
             }
           }
         }
@@ -467,8 +494,8 @@ hipError_t launch_gemm_bf16_qkv(const uint16_t* A, const uint16_t* W, const floa
   qe.ts = max(r.gt, max(r.gh, r.gw));
   qe.qscale = qscale;
   if (qe.ts > kMaxGridSide) return hipErrorInvalidValue;
+  // the 256 x 256 tile leaves too few registers for the RoPE epilogue
   const int tw = tile_width(M, Ncol);
-  if (tw == 256) return gemm_qkv_dispatch<Cfg256x256>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
   if (tw == 192) return gemm_qkv_dispatch<Cfg256x192>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
   return gemm_qkv_dispatch<Cfg256x128q>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
 }
