@@ -37,8 +37,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libjepa)")
 
 
-# per-source extra flags
-EXTRA = {}
+# per-source extra flags: the attention kernels compare scores with -inf but never see a
+# NaN they must order, so fmax needs no NaN canonicalisation of its inputs
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

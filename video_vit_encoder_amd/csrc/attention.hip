@@ -105,10 +105,13 @@ __device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
 //   * P^T leaves that MFMA already in the B-operand layout of O^T += V^T P^T: slot s of
 //     k-step ks holds key 16ks + 8(s/4) + 4(l/32) + s%4, i.e. position vt_pos of the
 //     16-group, the order V^T is stored in, so every A operand is one 16-byte LDS read;
-//   * the running max moves only when a tile's max exceeds it by more than 2^8 (scores are
-//     in log2 units): between moves the probabilities stay in (0, 256] and the output
-//     accumulators are not rescaled.  The first tile sets the max exactly, so the
-//     running sum never underflows.
+//   * the score accumulators start at minus the running max, so the MFMA hands back
+//     scores relative to it (log2 units); the running max moves only when a tile's max
+//     exceeds it by more than 8: between moves the probabilities stay in (0, 256] and
+//     neither the scores nor the output accumulators are touched before exp2.  The first
+//     tile sets the max exactly, so the running sum never underflows;
+//   * the row sum adds the bf16-rounded probabilities (the values the second product
+//     uses) with v_dot2_f32_bf16.
 template <int HD>
 __global__ __launch_bounds__(256, 2)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int ld,
@@ -217,13 +220,15 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
     // S^T = K Q^T for the 64 keys: element i of sc[g][t2] is key
     // kb + 32 t2 + 8(i/4) + 4h + i%4 of query l32 of group g
+    // the accumulators start at -m_run, so the product comes out relative to the running
+    // max: the common case takes exp2 of it directly
     f32x16 sc[2][2];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[g][t2][i] = 0.f;
+        for (int i = 0; i < 16; ++i) sc[g][t2][i] = -m_run[g];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int r = t2 * 32 + l32;
@@ -245,36 +250,57 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             if (kb + t2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3) >= N) sc[g][t2][i] = -INFINITY;
     }
 
-    bf16x8 pf[2][4];
+    // Row max of the tile relative to the running max; one wave-uniform decision for
+    // both groups.  The first tile sets the running max to its exact max; later tiles
+    // move it only for queries whose tile max exceeds it by more than TAU.
+    float mxs[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       float mx = fmaxf(sc[g][0][0], sc[g][1][0]);
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sc[g][0][i], sc[g][1][i]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (t == 0) {
-        m_run[g] = mx;
-      } else if (__ballot(mx - m_run[g] > TAU) != 0) {
-        const float d = mx - m_run[g] > TAU ? mx - m_run[g] : 0.f;
-        const float alpha = __builtin_amdgcn_exp2f(-d);
+      mxs[g] = fmaxf(mx, __shfl_xor(mx, 32));
+    }
+    if (t == 0 || __ballot(mxs[0] > TAU || mxs[1] > TAU) != 0) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float d = t == 0 ? mxs[g] : (mxs[g] > TAU ? mxs[g] : 0.f);
+        const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-d);
         m_run[g] += d;
         l_run[g] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[g][dt][i] *= alpha;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[g][t2][i] -= d;
       }
-      const float m = m_run[g];
-      float ls = 0.f;
+    }
+    // P = exp2(S - m) in (0, 2^TAU], rounded to bf16; the row sum adds those bf16 values
+    // (the ones the second product uses) two at a time
+    bf16x8 pf[2][4];
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+    for (int g = 0; g < 2; ++g) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(sc[g][t2][i] - m);
-          ls += pv;
-          pf[g][t2 * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(pv);
+      for (int ks = 0; ks < 4; ++ks) {
+        // slot s of k-step ks = element 8 (ks % 2) + s of sc[g][ks / 2]
+        // each pair is converted as one bf16x2 value (v_cvt_pk_bf16_f32) that feeds both
+        // the dot product and the operand word
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * (ks & 1) + 2 * e;
+          const f32x2 pp = {__builtin_amdgcn_exp2f(sc[g][ks >> 1][i]),
+                            __builtin_amdgcn_exp2f(sc[g][ks >> 1][i + 1])};
+          const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+          l_run[g] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_run[g], false);
+          w[e] = __builtin_bit_cast(uint32_t, pb);
         }
-      l_run[g] += ls;
+        pf[g][ks] = __builtin_bit_cast(bf16x8, w);
+      }
     }
 
     // O^T += V^T P^T: the A operand is V^T dims 32dt + l32, positions 16ks + 8h .. +8
