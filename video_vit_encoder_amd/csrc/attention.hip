@@ -181,6 +181,14 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) qf[g][kk] = *reinterpret_cast<const bf16x8*>(src + (2 * kk + h) * 8);
   }
+  // Let the query loads land here, before any tile DMA is issued: the compiler cannot see
+  // the DMAs, so a wait it placed at the first use of a fragment inside the loop would
+  // also wait for the tiles in flight.  The empty asm takes the fragments as outputs, so
+  // nothing after it depends on the loads.
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[g][kk]));
 
   f32x16 o[2][DT];
 #pragma unroll

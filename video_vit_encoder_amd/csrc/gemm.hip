@@ -50,12 +50,12 @@ struct QkvEpi {
 // t = 1 / (1 + p|x|), odd in x.
 __device__ __forceinline__ float gelu_as(float z) {
   const float x = fabsf(z) * 0.70710678118654752440f;
-  const float t = __frcp_rn(fmaf(0.3275911f, x, 1.0f));
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));  // v_rcp_f32, 1 ulp
   float y = fmaf(1.061405429f, t, -1.453152027f);
   y = fmaf(y, t, 1.421413741f);
   y = fmaf(y, t, -0.284496736f);
   y = fmaf(y, t, 0.254829592f);
-  const float e = 1.0f - y * t * __expf(-x * x);
+  const float e = 1.0f - y * t * __builtin_amdgcn_exp2f(-1.4426950408889634f * x * x);
   return 0.5f * z * (1.0f + copysignf(e, z));
 }
 
@@ -95,7 +95,7 @@ template <class C, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(C::NT)
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                       const float* __restrict__ bias, void* __restrict__ Cv, int M, int N, int K,
-                      QkvEpi qe) {
+                      QkvEpi qe, int bias_lds) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STAGES = C::STAGES, NWAVES = C::NWAVES;
   constexpr int FI = C::FI, FJ = C::FJ, WM = C::WM, WN = C::WN;
   constexpr int A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS;
@@ -223,8 +223,11 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   // whose reads all completed before the barrier.  Up to STAGES - 1 slabs are in flight
   // while a slab is consumed.
   constexpr int KSTEPS = BK / 16;
+  // LDS after the ring: the RoPE table rows (axis, coord < ts) of the QKV epilogue, then the
+  // bias row when bias_lds.  Both are copied here, before the first slab DMA, so the waits
+  // for these loads cannot hold up the ring; the prologue's barrier publishes them.
+  const int tab_bytes = (EPI == EPI_QKV64 || EPI == EPI_QKV32) ? 3 * qe.ts * kRopeMaxFreq * 8 : 0;
   if constexpr (EPI == EPI_QKV64 || EPI == EPI_QKV32) {
-    // RoPE table rows (axis, coord < ts) after the ring; the prologue's barrier publishes them
     float2* tabs = reinterpret_cast<float2*>(smem + C::LDS);
     const int n = 3 * qe.ts * kRopeMaxFreq;
     for (int e = tid; e < n; e += C::NT) {
@@ -232,6 +235,16 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
       tabs[e] = qe.ra.tab[a * kMaxGridSide * kRopeMaxFreq + rest];
     }
   }
+  const float* bias_s = reinterpret_cast<const float*>(smem + C::LDS + tab_bytes);
+  if (bias_lds) {
+    f32x4* dst = reinterpret_cast<f32x4*>(smem + C::LDS + tab_bytes);
+    for (int e = tid; e < N / 4; e += C::NT) dst[e] = reinterpret_cast<const f32x4*>(bias)[e];
+  }
+  // bias of output columns col .. col + 3
+  auto bias4 = [&](int col) __attribute__((always_inline)) {
+    if (bias_lds) return *reinterpret_cast<const f32x4*>(bias_s + col);
+    return bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
   if (total > 0) set_rows(0);
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
@@ -308,7 +321,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int col = col0 + 8 * gq + 4 * h, jj = jb + 8 * gq + 4 * h;
-          bv[gq] = bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+          bv[gq] = bias4(col);
           pidx[gq][0] = rope_pair_idx<HD>(jj, qe.ra.layout);
           pidx[gq][1] = rope_pair_idx<HD>(jj + 2, qe.ra.layout);
         }
@@ -366,12 +379,22 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     for (int i = 0; i < FI; ++i) {
       const int row = m0 + wm * WM + i * 32 + l32;
       if (row >= M) continue;
+      // the residual of this lane's row is read with all loads in flight together
+      f32x4 xr[EPI == EPI_RESIDUAL ? FJ : 1][4];
+      if constexpr (EPI == EPI_RESIDUAL) {
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            xr[j][g] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(Cv) + static_cast<size_t>(row) * N +
+                                                       n0 + wn * WN + j * 32 + 8 * g + 4 * h);
+      }
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * h;
-          const f32x4 bv = bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+          const f32x4 bv = bias4(col);
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -379,11 +402,10 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
             if (EPI == EPI_GELU) v[e] = OUT_F32 ? gelu_erf(v[e]) : gelu_as(v[e]);
           }
           const size_t off = static_cast<size_t>(row) * N + col;
-          if (EPI == EPI_RESIDUAL) {
-            f32x4* Cp = reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off);
-            f32x4 c = *Cp;
+          if constexpr (EPI == EPI_RESIDUAL) {
+            f32x4 c = xr[j][g];
             c[0] += v[0]; c[1] += v[1]; c[2] += v[2]; c[3] += v[3];
-            *Cp = c;
+            *reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off) = c;
           } else if (OUT_F32) {
             *reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off) = f32x4{v[0], v[1], v[2], v[3]};
           } else {
@@ -414,7 +436,7 @@ template <class C, int EPI, bool OUT_F32>
 static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float* bias, void* Cp,
                               int M, int N, int K, hipStream_t s, const QkvEpi& qe = QkvEpi{}) {
   constexpr bool QKV = EPI == EPI_QKV64 || EPI == EPI_QKV32;
-  constexpr int MAX_LDS = QKV ? 160 * 1024 : C::LDS;
+  constexpr int MAX_LDS = 160 * 1024;
   static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kRopeMaxFreq * 8 <= MAX_LDS, "LDS for the RoPE table");
   static bool configured = false;
   if (!configured) {
@@ -423,10 +445,13 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int lds = C::LDS + (QKV ? 3 * qe.ts * kRopeMaxFreq * 8 : 0);
+  int lds = C::LDS + (QKV ? 3 * qe.ts * kRopeMaxFreq * 8 : 0);
+  // the bias row goes to LDS when it fits beside the ring (else it is read from L2)
+  const int bias_lds = bias && lds + N * 4 <= MAX_LDS ? 1 : 0;
+  if (bias_lds) lds += N * 4;
   const int tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
   const dim3 grid(min(tiles, num_cus()));
-  gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, lds, s>>>(A, W, bias, Cp, M, N, K, qe);
+  gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, lds, s>>>(A, W, bias, Cp, M, N, K, qe, bias_lds);
   return hipGetLastError();
 }
 
