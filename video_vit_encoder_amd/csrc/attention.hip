@@ -94,14 +94,21 @@ __device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
 // on inputs prepared once per token (the QKV projection's epilogue or qkv_prepare_kernel):
 // q rotated and scaled by log2(e)/sqrt(hd), k rotated, v transposed per (clip, head) with
 // the keys of each 16-group in vt_pos order.
-//   * a workgroup of 4 wavefronts owns 256 queries of one (clip, head); each wave keeps
-//     two groups of 32 as bf16 MFMA B operands in registers;
-//   * 64-key tiles of K and V^T stream through a ring of 3 LDS buffers, filled by
-//     global_load_lds_dwordx4 two tiles ahead (no register staging, no VALU); one barrier
-//     per tile;
+//   * a workgroup of 8 wavefronts owns 512 queries of one (clip, head); each wave keeps
+//     two groups of 32 as bf16 MFMA B operands in registers, and every K or V fragment it
+//     reads from LDS feeds the MFMAs of both groups;
+//   * the waves form two halves of four (one wave of each half per SIMD) that take turns
+//     between workgroup barriers: in one phase half A runs the matrix products of a key
+//     tile (P V of the previous tile, then S = K Q of this one) while half B runs the
+//     softmax of the tile it multiplied in the phase before (max, exp2, bf16 rounding,
+//     row sums), and the other way round in the next phase, so each SIMD's matrix core
+//     and vector ALU are busy at the same time;
+//   * 64-key tiles of K and V^T stream through a ring of 4 LDS buffers, filled by
+//     global_load_lds_dwordx4 two tiles ahead (no register staging, no VALU); tile t is
+//     read in phases 2t .. 2t + 3, so its buffer is refilled with tile t + 4 from phase
+//     2t + 4 on;
 //   * S^T = K Q^T puts 16 keys of one query in each lane, so the row max and sum are per
-//     lane plus one exchange with the lane 32 away; every K and V fragment read from LDS
-//     feeds the MFMAs of both query groups;
+//     lane plus one exchange with the lane 32 away;
 //   * P^T leaves that MFMA already in the B-operand layout of O^T += V^T P^T: slot s of
 //     k-step ks holds key 16ks + 8(s/4) + 4(l/32) + s%4, i.e. position vt_pos of the
 //     16-group, the order V^T is stored in, so every A operand is one 16-byte LDS read;
@@ -113,11 +120,11 @@ __device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
 //   * the row sum adds the bf16-rounded probabilities (the values the second product
 //     uses) with v_dot2_f32_bf16.
 template <int HD>
-__global__ __launch_bounds__(256, 2)
+__global__ __launch_bounds__(512, 1)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int ld,
                      const uint16_t* __restrict__ vt, int Ns, uint16_t* __restrict__ out, int N,
                      int H, int nqb) {
-  constexpr int BQ = 256, BKV = 64, S = 3;
+  constexpr int NW = 8, BQ = NW * 64, BKV = 64, S = 4;
   constexpr int KS = HD / 16;                   // MFMA k-steps over the head dim
   constexpr int DT = HD / 32;                   // 32-dim blocks of the output
   constexpr int KROW = HD * 2;                  // LDS bytes per K row (128 / 64)
@@ -125,15 +132,15 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int STAGE = K_BYTES + V_BYTES;
   constexpr int K_RPI = 1024 / KROW;            // K rows per 1 KB DMA instruction
   constexpr int K_CPR = KROW / 16;              // 16-byte chunks per K row
-  constexpr int K_DMA = K_BYTES / 4096;         // DMA instructions per wave and tile
-  constexpr int V_DMA = V_BYTES / 4096;
-  constexpr int LOADS = K_DMA + V_DMA;
+  constexpr int K_INS = K_BYTES / 1024, V_INS = V_BYTES / 1024;  // DMA instructions per tile
+  constexpr int LOADS = (K_INS + V_INS) / NW;   // per wave and tile
   constexpr float TAU = 8.0f;
-  static_assert(K_DMA * 4096 == K_BYTES && V_DMA * 4096 == V_BYTES, "DMA split");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[S * STAGE];
+  static_assert(LOADS * NW == K_INS + V_INS, "DMA split");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave >> 2;                   // 0: A, 1: B
   const int h = lane >> 5, l32 = lane & 31;
   // Work-groups are dealt to the 8 XCDs round-robin; renumber them so that the query
   // blocks of one (clip, head), which read the same keys and values, share an XCD's L2.
@@ -152,23 +159,24 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const uint16_t* vbase = vt + static_cast<size_t>(b * H + head) * HD * Ns;
   const int ntiles = (N + BKV - 1) / BKV;
 
-  // Tile t into buffer t % S: K rows past N repeat row N - 1 (their scores are masked);
-  // V^T rows read 64 keys from position 64t on (the caller's buffer holds them: see
+  // Tile t into buffer t % S: instruction i = qd*NW + wave of the tile fills 1 KB of K
+  // (i < K_INS) or of V^T.  K rows past N repeat row N - 1 (their scores are masked); V^T
+  // rows read 64 keys from position 64t on (the caller's buffer holds them: see
   // launch_attention_fwd); positions of keys past N are zeroed in LDS below.
   auto issue = [&](int t) {
     const uint32_t st = sbase + (t % S) * STAGE;
     const int kb = t * BKV;
 #pragma unroll
-    for (int qd = 0; qd < K_DMA; ++qd) {
-      const int g = qd * 4 + wave;
-      const int key = min(kb + g * K_RPI + krow_l, N - 1);
-      dma16(kbase, static_cast<uint32_t>(key) * ld * 2 + kchunk_l * 16, st + g * 1024);
-    }
-#pragma unroll
-    for (int qd = 0; qd < V_DMA; ++qd) {
-      const int g = qd * 4 + wave;
-      const int dim = g * 8 + vrow_l;
-      dma16(vbase, (static_cast<uint32_t>(dim) * Ns + kb) * 2 + vchunk_l * 16, st + K_BYTES + g * 1024);
+    for (int qd = 0; qd < LOADS; ++qd) {
+      const int ins = qd * NW + wave;
+      if (ins < K_INS) {
+        const int key = min(kb + ins * K_RPI + krow_l, N - 1);
+        dma16(kbase, static_cast<uint32_t>(key) * ld * 2 + kchunk_l * 16, st + ins * 1024);
+      } else {
+        const int vi = ins - K_INS;
+        const int dim = vi * 8 + vrow_l;
+        dma16(vbase, (static_cast<uint32_t>(dim) * Ns + kb) * 2 + vchunk_l * 16, st + K_BYTES + vi * 1024);
+      }
     }
   };
 
@@ -198,39 +206,64 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[g][dt][i] = 0.f;
   float m_run[2] = {0.f, 0.f}, l_run[2] = {0.f, 0.f};
+  f32x16 sc[2][2];   // scores of the tile this wave multiplied last
+  bf16x8 pf[2][4];   // probabilities of the tile whose softmax this wave ran last
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   int issued = 0;
-  for (; issued < S - 1 && issued < ntiles; ++issued) issue(issued);
-  for (int t = 0; t < ntiles; ++t) {
-    // tile t has landed once at most issued - 1 - t later tiles are still in flight
-    if (issued - 1 - t >= 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int kb = t * BKV;
-    unsigned char* st = smem + (t % S) * STAGE;
-    if (kb + BKV > N) {
-      // ragged last tile: zero the V^T positions of keys past N (P is 0 there, and the
-      // words read past the clip's keys need not be finite)
-      for (int e = tid; e < HD * BKV; e += 256) {
-        const int dim = e / BKV, pos = e - dim * BKV;
-        if (kb + vt_pos(pos) >= N)
-          *reinterpret_cast<uint16_t*>(st + K_BYTES + dim * 128 + ((((pos >> 3) ^ (dim & 7))) << 4) + (pos & 7) * 2) = 0;
-      }
-      __syncthreads();
-    }
-    // the buffer of tile t - 1 is free: every wave finished it before the barrier
-    if (issued < ntiles) {
-      issue(issued);
-      ++issued;
-    }
+  for (; issued < 2 && issued < ntiles; ++issued) issue(issued);
 
-    // S^T = K Q^T for the 64 keys: element i of sc[g][t2] is key
-    // kb + 32 t2 + 8(i/4) + 4h + i%4 of query l32 of group g
-    // the accumulators start at -m_run, so the product comes out relative to the running
-    // max: the common case takes exp2 of it directly
-    f32x16 sc[2][2];
+  // Barrier k opens phase k.  Before an even barrier, tile k/2 (first read in phase k)
+  // must have landed for every wave: at most the one tile issued after it may still be in
+  // flight.  After it, tile k/2 + 2 goes into the buffer of tile k/2 - 2 (read for the last
+  // time in phase k - 1), and a ragged last tile gets its V^T positions of keys past N
+  // zeroed (P is 0 there, and the words read past the clip's keys need not be finite;
+  // V^T of tile t is first read in phase 2t + 2, two barriers later).
+  auto sync = [&](int kph) __attribute__((always_inline)) {
+    const int t = kph >> 1;
+    if ((kph & 1) == 0 && t < ntiles) {
+      if (issued - 1 - t >= 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if ((kph & 1) == 0) {
+      if (issued < ntiles) {
+        issue(issued);
+        ++issued;
+      }
+      if (t == ntiles - 1 && t * BKV + BKV > N) {
+        unsigned char* st = smem + (t % S) * STAGE;
+        const int kb = t * BKV;
+        for (int e = tid; e < HD * BKV; e += NW * 64) {
+          const int dim = e / BKV, pos = e - dim * BKV;
+          if (kb + vt_pos(pos) >= N)
+            *reinterpret_cast<uint16_t*>(st + K_BYTES + dim * 128 + ((((pos >> 3) ^ (dim & 7))) << 4) + (pos & 7) * 2) = 0;
+        }
+      }
+    }
+  };
+  // O^T += V^T P^T for tile t (probabilities pf)
+  auto mma_pv = [&](int t) __attribute__((always_inline)) {
+    const unsigned char* st = smem + (t % S) * STAGE;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dim = dt * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + K_BYTES + dim * 128 + (((2 * ks + h) ^ (dim & 7)) << 4));
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g][ks], o[g][dt], 0, 0, 0);
+      }
+    }
+  };
+  // S^T = K Q^T for tile t: element i of sc[g][t2] is key 64t + 32 t2 + 8(i/4) + 4h + i%4
+  // of query l32 of group g; the accumulators start at -m_run, so the product comes out
+  // relative to the running max
+  auto mma_qk = [&](int t) __attribute__((always_inline)) {
+    const unsigned char* st = smem + (t % S) * STAGE;
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -248,6 +281,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           sc[g][t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][kk], sc[g][t2], 0, 0, 0);
       }
     }
+  };
+  // Softmax of tile t's scores into pf, updating m_run, l_run (and o on a rescale).
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    const int kb = t * BKV;
     if (kb + BKV > N) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
@@ -257,16 +294,16 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           for (int i = 0; i < 16; ++i)
             if (kb + t2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3) >= N) sc[g][t2][i] = -INFINITY;
     }
-
-    // Row max of the tile relative to the running max; one wave-uniform decision for
-    // both groups.  The first tile sets the running max to its exact max; later tiles
-    // move it only for queries whose tile max exceeds it by more than TAU.
+    // Row max of the tile relative to the running max, one wave-uniform decision for both
+    // groups: the first tile sets the running max to its exact max; later tiles move it
+    // only for queries whose tile max exceeds it by more than TAU.
     float mxs[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
+      // a linear chain of 3-input maxima (v_max3_f32): half an op per score
       float mx = fmaxf(sc[g][0][0], sc[g][1][0]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sc[g][0][i], sc[g][1][i]));
+      for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, sc[g][0][i]), sc[g][1][i]);
       mxs[g] = fmaxf(mx, __shfl_xor(mx, 32));
     }
     if (t == 0 || __ballot(mxs[0] > TAU || mxs[1] > TAU) != 0) {
@@ -287,16 +324,13 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     }
     // P = exp2(S - m) in (0, 2^TAU], rounded to bf16; the row sum adds those bf16 values
-    // (the ones the second product uses) two at a time
-    bf16x8 pf[2][4];
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    // two at a time
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        // slot s of k-step ks = element 8 (ks % 2) + s of sc[g][ks / 2]
-        // each pair is converted as one bf16x2 value (v_cvt_pk_bf16_f32) that feeds both
-        // the dot product and the operand word
+        // slot s of k-step ks = element 8 (ks % 2) + s of sc[g][ks / 2]; each pair is
+        // converted as one bf16x2 value that feeds both the dot product and the word
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -310,19 +344,41 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         pf[g][ks] = __builtin_bit_cast(bf16x8, w);
       }
     }
+  };
 
-    // O^T += V^T P^T: the A operand is V^T dims 32dt + l32, positions 16ks + 8h .. +8
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int dim = dt * 32 + l32;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + K_BYTES + dim * 128 + (((2 * ks + h) ^ (dim & 7)) << 4));
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-          o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g][ks], o[g][dt], 0, 0, 0);
-      }
+  // Phase k: half A multiplies tile k/2 for even k (P V of tile k/2 - 1, then K Q of tile
+  // k/2) and runs the softmax of tile (k-1)/2 for odd k; half B does the same one phase
+  // later.  Both halves pass the same 2 ntiles + 2 barriers.
+  if (half == 0) {
+    sync(0);
+    mma_qk(0);
+    sync(1);
+    softmax(0);
+    for (int t = 1; t < ntiles; ++t) {
+      sync(2 * t);
+      mma_pv(t - 1);
+      mma_qk(t);
+      sync(2 * t + 1);
+      softmax(t);
     }
+    sync(2 * ntiles);
+    mma_pv(ntiles - 1);
+    sync(2 * ntiles + 1);
+  } else {
+    sync(0);
+    sync(1);
+    mma_qk(0);
+    sync(2);
+    softmax(0);
+    for (int t = 1; t < ntiles; ++t) {
+      sync(2 * t + 1);
+      mma_pv(t - 1);
+      mma_qk(t);
+      sync(2 * t + 2);
+      softmax(t);
+    }
+    sync(2 * ntiles + 1);
+    mma_pv(ntiles - 1);
   }
 
   // ---- normalise and store: element i of o[g][dt] is dim 32 dt + 8(i/4) + 4h + i%4
@@ -345,6 +401,23 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 }
 
+template <int HD>
+static hipError_t attn_launch(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt, int Ns,
+                              uint16_t* out, int B, int N, int n_head, hipStream_t s) {
+  constexpr int LDS = 4 * (64 * HD * 2 + HD * 64 * 2);
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<HD>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int nqb = (N + 511) / 512;
+  const dim3 grid(nqb * n_head * B);
+  attn_fwd_kernel<HD><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
                                 int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
                                 hipStream_t s) {
@@ -354,13 +427,8 @@ hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, co
   if (static_cast<size_t>(N) * ld * 2 >= (size_t(1) << 31) ||
       static_cast<size_t>(head_dim) * Ns * 2 >= (size_t(1) << 31))
     return hipErrorInvalidValue;
-  const int nqb = (N + 255) / 256;
-  const dim3 grid(nqb * n_head * B);
-  if (head_dim == 64)
-    attn_fwd_kernel<64><<<grid, 256, 0, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb);
-  else
-    attn_fwd_kernel<32><<<grid, 256, 0, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb);
-  return hipGetLastError();
+  if (head_dim == 64) return attn_launch<64>(q, k, ld, vt, Ns, out, B, N, n_head, s);
+  return attn_launch<32>(q, k, ld, vt, Ns, out, B, N, n_head, s);
 }
 
 // Attention inputs from a projection already in memory (the stand-alone entry point):
