@@ -244,7 +244,7 @@ enum jepa_kernel_class {
   JEPA_KC_GEMM_EMBED = 1, /* patch / predictor embedding and predictor output GEMMs  */
   JEPA_KC_LAYERNORM = 2,  /* LN1, LN2 and the final norm                            */
   JEPA_KC_GEMM_QKV = 3,   /* fused QKV projection                                   */
-  JEPA_KC_ATTENTION = 4,  /* RoPE-on-load flash attention                           */
+  JEPA_KC_ATTENTION = 4,  /* flash attention (fp32 path: RoPE on the Q/K load)       */
   JEPA_KC_GEMM_OUT = 5,   /* attention output projection + residual                 */
   JEPA_KC_GEMM_UP = 6,    /* FFN up-projection + GELU                               */
   JEPA_KC_GEMM_DOWN = 7,  /* FFN down-projection + residual                         */
