@@ -150,10 +150,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int head = bh % H, b = bh / H;
   const int D = H * HD;
 
-  // K rows are 128 B (hd 64) or 64 B (hd 32); chunk c of row r sits at c ^ kkey(r)
-  auto kkey = [](int r) { return HD == 64 ? (r & 7) : ((r >> 1) & 3); };
-  const int krow_l = lane / K_CPR, kchunk_l = (lane % K_CPR) ^ kkey(lane / K_CPR);
-  const int vrow_l = lane >> 3, vchunk_l = (lane & 7) ^ (vrow_l & 7);
+  // K rows are 128 B (hd 64) or 64 B (hd 32), V^T rows 128 B; chunk c of row r sits at
+  // c ^ kkey(r) (K) or c ^ lds_key128(r) (V^T)
+  auto kkey = [](int r) { return HD == 64 ? lds_key128(r) : lds_key64(r); };
+  const int krow_l = lane / K_CPR, kslot_l = lane % K_CPR;
+  const int vrow_l = lane >> 3, vslot_l = lane & 7;
   const uint32_t sbase = lds_addr(smem);
   const uint16_t* kbase = k + static_cast<size_t>(b) * N * ld + head * HD;
   const uint16_t* vbase = vt + static_cast<size_t>(b * H + head) * HD * Ns;
@@ -170,12 +171,14 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int qd = 0; qd < LOADS; ++qd) {
       const int ins = qd * NW + wave;
       if (ins < K_INS) {
-        const int key = min(kb + ins * K_RPI + krow_l, N - 1);
-        dma16(kbase, static_cast<uint32_t>(key) * ld * 2 + kchunk_l * 16, st + ins * 1024);
+        const int r = ins * K_RPI + krow_l;   // row in the tile
+        const int key = min(kb + r, N - 1);
+        dma16(kbase, static_cast<uint32_t>(key) * ld * 2 + ((kslot_l ^ kkey(r)) << 4), st + ins * 1024);
       } else {
         const int vi = ins - K_INS;
         const int dim = vi * 8 + vrow_l;
-        dma16(vbase, (static_cast<uint32_t>(dim) * Ns + kb) * 2 + vchunk_l * 16, st + K_BYTES + vi * 1024);
+        dma16(vbase, (static_cast<uint32_t>(dim) * Ns + kb) * 2 + ((vslot_l ^ lds_key128(dim)) << 4),
+              st + K_BYTES + vi * 1024);
       }
     }
   };
@@ -239,7 +242,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         for (int e = tid; e < HD * BKV; e += NW * 64) {
           const int dim = e / BKV, pos = e - dim * BKV;
           if (kb + vt_pos(pos) >= N)
-            *reinterpret_cast<uint16_t*>(st + K_BYTES + dim * 128 + ((((pos >> 3) ^ (dim & 7))) << 4) + (pos & 7) * 2) = 0;
+            *reinterpret_cast<uint16_t*>(st + K_BYTES + dim * 128 + (((pos >> 3) ^ lds_key128(dim)) << 4) + (pos & 7) * 2) = 0;
         }
       }
     }
@@ -252,7 +255,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       const int dim = dt * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + K_BYTES + dim * 128 + (((2 * ks + h) ^ (dim & 7)) << 4));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + K_BYTES + dim * 128 + (((2 * ks + h) ^ lds_key128(dim)) << 4));
 #pragma unroll
         for (int g = 0; g < 2; ++g)
           o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g][ks], o[g][dt], 0, 0, 0);

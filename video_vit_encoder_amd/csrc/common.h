@@ -63,6 +63,15 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                : "memory");
 }
 
+// XOR swizzles of 16-byte chunks in LDS tiles read by ds_read_b128 down a column of
+// chunks: the chunk c of row r sits at chunk c ^ key(r).  The LDS serves such a read 16
+// lanes (16 consecutive rows) at a time from 64 four-byte banks, so 16 consecutive rows
+// must land in 16 different 16-byte bank groups (and any 8 consecutive rows in 8).
+// 128-byte rows (two rows per bank sweep): rows of one parity take 8 different keys.
+__device__ __forceinline__ int lds_key128(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+// 64-byte rows (four rows per bank sweep): rows 4 apart take 4 different keys.
+__device__ __forceinline__ int lds_key64(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p)));

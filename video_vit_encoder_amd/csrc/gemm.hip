@@ -14,9 +14,10 @@
 //     filled by global_load_lds_dwordx4 (HBM/L2 -> LDS, no register staging) up to
 //     STAGES - 1 slabs ahead of the MFMAs, so the next tile's first slabs load while
 //     the current tile's epilogue runs; one barrier per slab;
-//   * LDS rows are 128 B; the 16-byte chunk c of row r lives at chunk c ^ (r & 7).  A DMA
-//     instruction writes 64 consecutive 16-byte slots (8 rows), so lane p of it fetches
-//     the global chunk that belongs in slot p;
+//   * LDS rows are 128 B; the 16-byte chunk c of row r lives at chunk c ^ key(r), with a
+//     key that keeps 16 consecutive rows of one chunk column in 16 different bank groups.
+//     A DMA instruction writes 64 consecutive 16-byte slots (8 rows), so lane p of it
+//     fetches the global chunk that belongs in slot p;
 //   * the MFMA takes the W fragment as its first operand, so each lane ends up holding
 //     runs of 4 consecutive output columns of one output row: the epilogue (bias, GELU,
 //     residual) reads and writes 8- or 16-byte vectors;
@@ -78,9 +79,9 @@ struct GemmCfg {
   static constexpr int LDS = STAGES * STAGE_BYTES;
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && B_LOADS * NWAVES * 1024 == B_BYTES, "DMA split");
   static_assert(FI * 32 == WM && FJ * 32 == WN, "wave tile");
-  static_assert(STAGES >= 2 && STAGES <= 4 && LDS <= 160 * 1024, "LDS ring");
-  // the 16-byte chunk c of tile row r sits at chunk c ^ (r & 7)
-  __device__ static int key(int r) { return r & 7; }
+  static_assert(STAGES >= 2 && STAGES <= 4 && LDS + 2048 <= 160 * 1024, "LDS ring");
+  static_assert(BN <= 256, "bias slot of 1 KB");
+  __device__ static int key(int r) { return lds_key128(r); }
 };
 // 256 x 256: FFN up-projection (N = 4096 gives whole rounds of 256 CUs)
 using Cfg256x256 = GemmCfg<256, 256, 2, 2, 4>;
@@ -95,7 +96,7 @@ template <class C, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(C::NT)
 void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                       const float* __restrict__ bias, void* __restrict__ Cv, int M, int N, int K,
-                      QkvEpi qe, int bias_lds) {
+                      QkvEpi qe) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STAGES = C::STAGES, NWAVES = C::NWAVES;
   constexpr int FI = C::FI, FJ = C::FJ, WM = C::WM, WN = C::WN;
   constexpr int A_LOADS = C::A_LOADS, B_LOADS = C::B_LOADS;
@@ -145,33 +146,43 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
 
   // DMA mapping: instruction q of wave w fills rows [8 g, 8 g + 8) of a tile,
   // g = q*NWAVES + w; lane p -> row 8 g + p/8, slot p%8 holding logical chunk
-  // (p%8) ^ key(row) (the key depends on p/8 only).
-  const int prow = lane / C::CPR;
-  const int pchunk = (lane % C::CPR) ^ C::key(prow);
+  // (p%8) ^ key(row).
+  const int prow = lane / C::CPR, pslot = lane % C::CPR;
   const uint32_t smem_base = lds_addr(smem);
 
   // Issue state: the next slab to load (tile it_iss, slab kt_iss) and the byte offsets
   // of this lane's source rows in that tile, refreshed when the tile changes.  Rows of A
   // past M are clamped to row M - 1 (loaded, never stored).
-  int it_iss = 0, kt_iss = 0, s_iss = 0;
+  int it_iss = 0, kt_iss = 0, s_iss = 0, n0_iss = 0;
   uint32_t a_row[A_LOADS], b_row[B_LOADS];
   auto set_rows = [&](int it) {
     int m0, n0;
     tile_of(it, m0, n0);
+    n0_iss = n0;
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) {
       const int r = (q * NWAVES + wave) * C::RPI + prow;
-      a_row[q] = static_cast<uint32_t>(static_cast<size_t>(min(m0 + r, M - 1)) * K * 2) + pchunk * 16;
+      a_row[q] = static_cast<uint32_t>(static_cast<size_t>(min(m0 + r, M - 1)) * K * 2) + ((pslot ^ C::key(r)) << 4);
     }
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q) {
       const int r = (q * NWAVES + wave) * C::RPI + prow;
-      b_row[q] = static_cast<uint32_t>(static_cast<size_t>(n0 + r) * K * 2) + pchunk * 16;
+      b_row[q] = static_cast<uint32_t>(static_cast<size_t>(n0 + r) * K * 2) + ((pslot ^ C::key(r)) << 4);
     }
   };
+  // LDS after the ring: [RoPE table of the QKV epilogue] [two 1 KB bias slots].  The bias
+  // columns of tile i go to slot i & 1 by one DMA of wave 0, issued just before the
+  // tile's first slab: every wait for that slab or a later one in wave 0 covers it, and
+  // the barrier after that wait publishes it.  The slot is rewritten for tile i + 2 only
+  // after barriers that follow tile i's epilogue in every wave.
+  const int tab_bytes = (EPI == EPI_QKV64 || EPI == EPI_QKV32) ? 3 * qe.ts * kRopeMaxFreq * 8 : 0;
+  const uint32_t bias_base = smem_base + C::LDS + tab_bytes;
+  const bool has_bias = bias != nullptr;
   auto issue_next = [&]() {
     const uint32_t st = smem_base + (s_iss % STAGES) * STAGE_BYTES;
     const uint32_t k0 = kt_iss * BK * 2;
+    if (kt_iss == 0 && has_bias && wave == 0)
+      dma16(bias, static_cast<uint32_t>(n0_iss * 4 + min(lane, BN / 4 - 1) * 16), bias_base + (it_iss & 1) * 1024);
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) dma16(A, a_row[q] + k0, st + (q * NWAVES + wave) * 1024);
 #pragma unroll
@@ -223,10 +234,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   // whose reads all completed before the barrier.  Up to STAGES - 1 slabs are in flight
   // while a slab is consumed.
   constexpr int KSTEPS = BK / 16;
-  // LDS after the ring: the RoPE table rows (axis, coord < ts) of the QKV epilogue, then the
-  // bias row when bias_lds.  Both are copied here, before the first slab DMA, so the waits
-  // for these loads cannot hold up the ring; the prologue's barrier publishes them.
-  const int tab_bytes = (EPI == EPI_QKV64 || EPI == EPI_QKV32) ? 3 * qe.ts * kRopeMaxFreq * 8 : 0;
+  // The RoPE table rows (axis, coord < ts) of the QKV epilogue are copied before the first
+  // slab DMA, so the waits for these loads cannot hold up the ring; the prologue's barrier
+  // publishes them.
   if constexpr (EPI == EPI_QKV64 || EPI == EPI_QKV32) {
     float2* tabs = reinterpret_cast<float2*>(smem + C::LDS);
     const int n = 3 * qe.ts * kRopeMaxFreq;
@@ -235,15 +245,10 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
       tabs[e] = qe.ra.tab[a * kMaxGridSide * kRopeMaxFreq + rest];
     }
   }
-  const float* bias_s = reinterpret_cast<const float*>(smem + C::LDS + tab_bytes);
-  if (bias_lds) {
-    f32x4* dst = reinterpret_cast<f32x4*>(smem + C::LDS + tab_bytes);
-    for (int e = tid; e < N / 4; e += C::NT) dst[e] = reinterpret_cast<const f32x4*>(bias)[e];
-  }
-  // bias of output columns col .. col + 3
-  auto bias4 = [&](int col) __attribute__((always_inline)) {
-    if (bias_lds) return *reinterpret_cast<const f32x4*>(bias_s + col);
-    return bias ? *reinterpret_cast<const f32x4*>(bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+  // bias of the tile's columns c .. c + 3 (c relative to the tile) for tile it
+  auto bias4 = [&](int it, int c) __attribute__((always_inline)) {
+    if (!has_bias) return f32x4{0.f, 0.f, 0.f, 0.f};
+    return *reinterpret_cast<const f32x4*>(smem + C::LDS + tab_bytes + (it & 1) * 1024 + c * 4);
   };
   if (total > 0) set_rows(0);
 #pragma unroll
@@ -321,7 +326,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int col = col0 + 8 * gq + 4 * h, jj = jb + 8 * gq + 4 * h;
-          bv[gq] = bias4(col);
+          bv[gq] = bias4(it, col - n0);
           pidx[gq][0] = rope_pair_idx<HD>(jj, qe.ra.layout);
           pidx[gq][1] = rope_pair_idx<HD>(jj + 2, qe.ra.layout);
         }
@@ -394,7 +399,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * h;
-          const f32x4 bv = bias4(col);
+          const f32x4 bv = bias4(it, col - n0);
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -437,7 +442,7 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
                               int M, int N, int K, hipStream_t s, const QkvEpi& qe = QkvEpi{}) {
   constexpr bool QKV = EPI == EPI_QKV64 || EPI == EPI_QKV32;
   constexpr int MAX_LDS = 160 * 1024;
-  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kRopeMaxFreq * 8 <= MAX_LDS, "LDS for the RoPE table");
+  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kRopeMaxFreq * 8 + 2048 <= MAX_LDS, "LDS for the RoPE table");
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI, OUT_F32>),
@@ -445,13 +450,10 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
     if (e != hipSuccess) return e;
     configured = true;
   }
-  int lds = C::LDS + (QKV ? 3 * qe.ts * kRopeMaxFreq * 8 : 0);
-  // the bias row goes to LDS when it fits beside the ring (else it is read from L2)
-  const int bias_lds = bias && lds + N * 4 <= MAX_LDS ? 1 : 0;
-  if (bias_lds) lds += N * 4;
+  const int lds = C::LDS + (QKV ? 3 * qe.ts * kRopeMaxFreq * 8 : 0) + 2048;
   const int tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
   const dim3 grid(min(tiles, num_cus()));
-  gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, lds, s>>>(A, W, bias, Cp, M, N, K, qe, bias_lds);
+  gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, lds, s>>>(A, W, bias, Cp, M, N, K, qe);
   return hipGetLastError();
 }
 
