@@ -90,6 +90,14 @@ __device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
 
 // ---------------------------------------------------------------- bf16 / MFMA
 
+// max(x[l], x[l ^ 32]) in every lane l: v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second, so the two results hold, lane by lane,
+// the value of the lane and of its partner in the other half (no LDS round trip).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Flash attention, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 softmax and accumulators,
 // on inputs prepared once per token (the QKV projection's epilogue or qkv_prepare_kernel):
 // q rotated and scaled by log2(e)/sqrt(hd), k rotated, v transposed per (clip, head) with
@@ -102,7 +110,8 @@ __device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
 //     tile (P V of the previous tile, then S = K Q of this one) while half B runs the
 //     softmax of the tile it multiplied in the phase before (max, exp2, bf16 rounding,
 //     row sums), and the other way round in the next phase, so each SIMD's matrix core
-//     and vector ALU are busy at the same time;
+//     and vector ALU are busy at the same time (the matrix phase runs at raised wave
+//     priority, so its MFMAs issue ahead of the other wave's vector instructions);
 //   * 64-key tiles of K and V^T stream through a ring of 4 LDS buffers, filled by
 //     global_load_lds_dwordx4 two tiles ahead (no register staging, no VALU); tile t is
 //     read in phases 2t .. 2t + 3, so its buffer is refilled with tile t + 4 from phase
@@ -307,7 +316,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       float mx = fmaxf(sc[g][0][0], sc[g][1][0]);
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, sc[g][0][i]), sc[g][1][i]);
-      mxs[g] = fmaxf(mx, __shfl_xor(mx, 32));
+      mxs[g] = max_halves(mx);
     }
     if (t == 0 || __ballot(mxs[0] > TAU || mxs[1] > TAU) != 0) {
 #pragma unroll
@@ -349,18 +358,28 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   };
 
+  // Matrix phase of tile t: P V of tile t - 1 and K Q of tile t at raised wave priority.
+  // The SIMD's arbiter otherwise favours the older waves (half A), so half B's MFMAs
+  // would wait behind half A's softmax; with the matrix wave first, the other wave's
+  // vector instructions fill the MFMA shadow.
+  auto mma_phase = [&](int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    if (t > 0) mma_pv(t - 1);
+    mma_qk(t);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
   // Phase k: half A multiplies tile k/2 for even k (P V of tile k/2 - 1, then K Q of tile
   // k/2) and runs the softmax of tile (k-1)/2 for odd k; half B does the same one phase
   // later.  Both halves pass the same 2 ntiles + 2 barriers.
   if (half == 0) {
     sync(0);
-    mma_qk(0);
+    mma_phase(0);
     sync(1);
     softmax(0);
     for (int t = 1; t < ntiles; ++t) {
       sync(2 * t);
-      mma_pv(t - 1);
-      mma_qk(t);
+      mma_phase(t);
       sync(2 * t + 1);
       softmax(t);
     }
@@ -370,13 +389,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   } else {
     sync(0);
     sync(1);
-    mma_qk(0);
+    mma_phase(0);
     sync(2);
     softmax(0);
     for (int t = 1; t < ntiles; ++t) {
       sync(2 * t + 1);
-      mma_pv(t - 1);
-      mma_qk(t);
+      mma_phase(t);
       sync(2 * t + 2);
       softmax(t);
     }
