@@ -60,6 +60,22 @@ __device__ __forceinline__ float gelu_as(float z) {
   return 0.5f * z * (1.0f + copysignf(e, z));
 }
 
+// Store of one row's 32 bf16 columns of a 32 x 32 MFMA block.  Lane l (h = l / 32) holds
+// the packed columns 8 gq + 4 h .. + 3 in pk[gq]; lanes l and l + 32 hold the same row.
+// v_permlane32_swap trades the upper half of one word with the lower half of the next, so
+// that each lane ends up with 8 contiguous columns: 16 p + 8 h .. + 7 for p = 0, 1, and
+// two 16-byte stores per lane write the row in 32-byte pieces (four 8-byte stores
+// otherwise).  Both lanes of a pair must be active.
+__device__ __forceinline__ void store_row32_bf16(uint16_t* dst /* row, column 0 */, const u32x2 (&pk)[4], int h) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const auto w0 = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0], false, false);
+    const auto w1 = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1], false, false);
+    const u32x4 w = {w0[0], w1[0], w0[1], w1[1]};
+    *reinterpret_cast<u32x4*>(dst + 16 * p + 8 * h) = w;
+  }
+}
+
 // One tile configuration: BM x BN output tiles, 64-deep K slabs through a ring of STAGES
 // LDS buffers, WGM x WGN waves of WM x WN, each held as 32 x 32 MFMA blocks.
 template <int BM_, int BN_, int STAGES_, int WGM_, int WGN_>
@@ -348,9 +364,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
                 cs[gq][pp][1] = pi.rot ? tr[pi.i1] : make_float2(1.f, 0.f);
               }
             const float sc = sec == 0 ? qe.qscale : 1.0f;
+            u32x2 pk[4];
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const int col = col0 + 8 * gq + 4 * h;
               float v[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e] + bv[gq][e];
@@ -362,11 +378,10 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
                 y[2 * pp] = (x0 * c0.x - x1 * c0.y) * sc;
                 y[2 * pp + 1] = (x1 * c1.x + x0 * c1.y) * sc;
               }
-              u32x2 pk;
-              pk[0] = pack_bf16x2(y[0], y[1]);
-              pk[1] = pack_bf16x2(y[2], y[3]);
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cv) + static_cast<size_t>(row) * N + col) = pk;
+              pk[gq][0] = pack_bf16x2(y[0], y[1]);
+              pk[gq][1] = pack_bf16x2(y[2], y[3]);
             }
+            store_row32_bf16(static_cast<uint16_t*>(Cv) + static_cast<size_t>(row) * N + col0, pk, h);
           } else {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
@@ -396,6 +411,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
       }
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
+        u32x2 pk[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * h;
@@ -414,12 +430,12 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
           } else if (OUT_F32) {
             *reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off) = f32x4{v[0], v[1], v[2], v[3]};
           } else {
-            u32x2 pk;
-            pk[0] = pack_bf16x2(v[0], v[1]);
-            pk[1] = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cv) + off) = pk;
+            pk[g][0] = pack_bf16x2(v[0], v[1]);
+            pk[g][1] = pack_bf16x2(v[2], v[3]);
           }
         }
+        if constexpr (EPI != EPI_RESIDUAL && !OUT_F32)
+          store_row32_bf16(static_cast<uint16_t*>(Cv) + static_cast<size_t>(row) * N + n0 + wn * WN + j * 32, pk, h);
       }
     }
   }
