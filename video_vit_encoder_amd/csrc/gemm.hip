@@ -47,17 +47,20 @@ struct QkvEpi {
 };
 
 // GELU with erf from Abramowitz & Stegun 7.1.26 (|error of erf| <= 1.5e-7, far below
-// the bf16 rounding of the output): erf(x) = 1 - t(a1 + t(a2 + ...)) exp(-x^2),
-// t = 1 / (1 + p|x|), odd in x.
+// the bf16 rounding of the output): for x = |z| / sqrt(2), 1 - erf(x) = q(t) exp(-x^2)
+// with t = 1 / (1 + p x) and q a degree-5 polynomial in t without constant term.  Since
+// GELU(z) = z Phi(z) = max(z, 0) - |z| (1 - erf(x)) / 2 for either sign of z, the tail term
+// is formed directly (no 1 - erf cancellation for negative z) in 12 vector instructions
+// plus v_rcp_f32 and v_exp_f32.
 __device__ __forceinline__ float gelu_as(float z) {
-  const float x = fabsf(z) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));  // v_rcp_f32, 1 ulp
-  float y = fmaf(1.061405429f, t, -1.453152027f);
-  y = fmaf(y, t, 1.421413741f);
-  y = fmaf(y, t, -0.284496736f);
-  y = fmaf(y, t, 0.254829592f);
-  const float e = 1.0f - y * t * __builtin_amdgcn_exp2f(-1.4426950408889634f * x * x);
-  return 0.5f * z * (1.0f + copysignf(e, z));
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, az, 1.0f));
+  float y = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+  y = fmaf(y, t, 0.5f * 1.421413741f);
+  y = fmaf(y, t, 0.5f * -0.284496736f);
+  y = fmaf(y, t, 0.5f * 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(z * (z * -0.72134752044448170368f));   // exp(-z^2 / 2)
+  return fmaf(-az, y * t * e, fmaxf(z, 0.0f));
 }
 
 // Store of one row's 32 bf16 columns of a 32 x 32 MFMA block.  Lane l (h = l / 32) holds
@@ -261,9 +264,11 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
       tabs[e] = qe.ra.tab[a * kMaxGridSide * kRopeMaxFreq + rest];
     }
   }
-  // bias of the tile's columns c .. c + 3 (c relative to the tile) for tile it
+  // bias of the tile's columns c .. c + 3 (c relative to the tile) for tile it; without a
+  // bias the slots hold zeros (written here, published by the prologue's barrier)
+  if (!has_bias)
+    for (int e = tid; e < 512; e += C::NT) reinterpret_cast<float*>(smem + C::LDS + tab_bytes)[e] = 0.f;
   auto bias4 = [&](int it, int c) __attribute__((always_inline)) {
-    if (!has_bias) return f32x4{0.f, 0.f, 0.f, 0.f};
     return *reinterpret_cast<const f32x4*>(smem + C::LDS + tab_bytes + (it & 1) * 1024 + c * 4);
   };
   if (total > 0) set_rows(0);
