@@ -223,10 +223,8 @@ int jepa_linear(const void* A_dev, const void* W_dev, const float* bias_dev, voi
  * JEPA_BF16 (bf16 MFMA, fp32 softmax): q and k are first rotated (q also scaled by
  * log2(e)/sqrt(head_dim)) and v transposed into work_dev, a device buffer of at least
  * jepa_attention_workspace_size(...) bytes owned by the caller (contents on entry do not
- * matter; overwritten); then the flash-attention kernel runs on it.  From N = 2048 on,
- * the workspace also holds partial results: query blocks of a last, partial round of the
- * CUs run as key-tile pieces that a merge kernel combines.  The encoder forward uses the
- * same kernels with the rotation done by the QKV projection's epilogue.
+ * matter; overwritten); then the flash-attention kernel runs on it.  The encoder forward
+ * uses the same kernel with the rotation done by the QKV projection's epilogue.
  * JEPA_F32 (plain fp32 FMA, RoPE applied as q and k are loaded): work_dev is unused and
  * may be NULL.
  * Errors: JEPA_ERR_ARG also when the bf16 workspace is NULL or smaller than needed. */

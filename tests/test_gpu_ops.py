@@ -267,35 +267,6 @@ def test_attention(case):
     assert metrics.rel_max(got, wrong) > 5e-2
 
 
-def test_attention_split_runs():
-    # 4 clips x 2166 tokens x 16 heads = 320 query blocks of 512: on 256 CUs one whole round
-    # and 64 blocks left over, which run as key-tile pieces whose partial results a merge
-    # kernel combines.  Checked on sampled rows (every block, the block edges and the
-    # ragged tail), and twice in a row (same result).
-    import torch
-    B, grid, H, hd = 4, (6, 19, 19), 16, 64
-    N, D = 2166, 1024
-    banner("attention split runs", B, N, H, hd)
-    rng = np.random.default_rng(2166)
-    qkv = synth.round_to_bf16(rng.standard_normal((B, N, 3 * D)).astype(np.float32))
-    ids = np.arange(N, dtype=np.int32)
-    pos = oracle.rope_positions(ids, grid[1], grid[2], 0)
-    rows = np.unique(np.concatenate([np.arange(0, N, 37), np.arange(505, 520), np.arange(1020, 1030),
-                                     np.arange(N - 20, N)]))
-    qd = bf16(qkv)
-    outs = []
-    for _ in range(2):
-        od = torch.empty((B * N, D), dtype=torch.bfloat16, device="cuda:0")
-        J.jepa_attention(qd, od, B, N, H, hd, None, grid, "tiled")
-        outs.append(host(od).reshape(B, N, D))
-    assert np.array_equal(outs[0], outs[1])
-    q64 = qkv.astype(np.float64)
-    for b in range(B):
-        ref = oracle.attention(q64[b, :, :D], q64[b, :, D:2 * D], q64[b, :, 2 * D:], H, pos, pos, "tiled",
-                               rows=rows)
-        assert_bf16_gate(outs[0][b, rows], ref, f"split runs clip {b}")
-
-
 def test_attention_softmax_properties_identical_keys():
     # every key identical -> each head's output is that value row, whatever the query
     banner("attention identical keys")

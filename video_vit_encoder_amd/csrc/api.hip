@@ -266,7 +266,7 @@ int check_grid(int gt, int gh, int gw, int ref_grid) {
 
 // Workspace of the block sequence for `rows` token rows.
 struct Workspace {
-  DevBuf h, qkv, o, g, a, vt, tab, split;
+  DevBuf h, qkv, o, g, a, vt, tab;
   int rows = 0;
   size_t vt_rows = 0;  // capacity of vt in (clip, key) rows of D values
   ~Workspace() {
@@ -277,7 +277,6 @@ struct Workspace {
     dev_free(a);
     dev_free(vt);
     dev_free(tab);
-    dev_free(split);
   }
   int alloc(int max_rows, int D, int F, int a_cols, int compute) {
     rows = max_rows;
@@ -295,9 +294,6 @@ struct Workspace {
       JEPA_TRY(dev_alloc(vt, vt_rows * D * 2 + kVtSlackBytes));
       if (hipMemset(vt.p, 0, vt.bytes) != hipSuccess) return JEPA_ERR_HIP;
       JEPA_TRY(dev_alloc(tab, static_cast<size_t>(kRopeTabEntries) * 8));
-      // partial results of attention items run as key-tile pieces (clips of 2048 tokens
-      // or more)
-      if (max_rows >= 2048) JEPA_TRY(dev_alloc(split, attention_split_bytes(64)));
     }
     return JEPA_OK;
   }
@@ -344,7 +340,7 @@ int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_r
                                        attn_qscale(hd), s));
       JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
                   launch_attention_fwd(qkv, qkv + D, 3 * D, vt, Ns, static_cast<uint16_t*>(ws.o.p), B,
-                                       N, n_head, hd, ws.split.p, s));
+                                       N, n_head, hd, s));
     } else {
       JEPA_LAUNCH(JEPA_KC_GEMM_QKV, s,
                   linear(compute, ws.h.p, ts.dev(b.qkvw), ts.devf(b.qkvb), ws.qkv.p, M, 3 * D, D,
@@ -697,25 +693,20 @@ int jepa_linear(const void* A_dev, const void* W_dev, const float* bias_dev, voi
 }
 
 // Workspace of the bf16 stand-alone attention: RoPE table | q', k' [M, 2D] | V^T rows.
-// Workspace of the bf16 stand-alone attention: RoPE table | q', k' [M, 2D] | V^T rows |
-// (N >= 2048) partial results of items run as key-tile pieces.
-static size_t attn_ws_parts(int B, int N, int D, int head_dim, size_t* off_qk, size_t* off_vt,
-                            size_t* off_split) {
+static size_t attn_ws_parts(int B, int N, int D, size_t* off_qk, size_t* off_vt) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t tab = up(static_cast<size_t>(kRopeTabEntries) * 8);
   const size_t qk = up(static_cast<size_t>(B) * N * 2 * D * 2);
-  const size_t vt = up(static_cast<size_t>(B) * D * vt_stride(N) * 2 + kVtSlackBytes);
-  const size_t split = N >= 2048 ? attention_split_bytes(head_dim) : 0;
+  const size_t vt = static_cast<size_t>(B) * D * vt_stride(N) * 2 + kVtSlackBytes;
   *off_qk = tab;
   *off_vt = tab + qk;
-  *off_split = tab + qk + vt;
-  return tab + qk + vt + split;
+  return tab + qk + vt;
 }
 
 size_t jepa_attention_workspace_size(int dtype, int B, int N, int n_head, int head_dim) {
   if (dtype != JEPA_BF16 || B <= 0 || N <= 0 || n_head <= 0 || head_dim <= 0) return 0;
-  size_t a, b, c;
-  return attn_ws_parts(B, N, n_head * head_dim, head_dim, &a, &b, &c);
+  size_t a, b;
+  return attn_ws_parts(B, N, n_head * head_dim, &a, &b);
 }
 
 int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
@@ -738,8 +729,8 @@ int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, 
                                            ids_dev, rs, s));
   const int D = n_head * head_dim;
   if (D % 32) return JEPA_ERR_SHAPE;
-  size_t off_qk, off_vt, off_split;
-  const size_t need = attn_ws_parts(B, N, D, head_dim, &off_qk, &off_vt, &off_split);
+  size_t off_qk, off_vt;
+  const size_t need = attn_ws_parts(B, N, D, &off_qk, &off_vt);
   if (!work_dev || work_bytes < need) return JEPA_ERR_ARG;
   unsigned char* w = static_cast<unsigned char*>(work_dev);
   uint16_t* qk = reinterpret_cast<uint16_t*>(w + off_qk);
@@ -749,8 +740,7 @@ int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, 
   JEPA_HIP(launch_qkv_prepare(static_cast<const uint16_t*>(qkv_dev), qk, vt, Ns, B, N, n_head,
                               head_dim, ids_dev, rs, w, attn_qscale(head_dim), s));
   return hip_status(launch_attention_fwd(qk, qk + D, 2 * D, vt, Ns,
-                                         static_cast<uint16_t*>(out_dev), B, N, n_head, head_dim,
-                                         N >= 2048 ? w + off_split : nullptr, s));
+                                         static_cast<uint16_t*>(out_dev), B, N, n_head, head_dim, s));
 }
 
 

@@ -90,10 +90,6 @@ __device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
 
 // ---------------------------------------------------------------- bf16 / MFMA
 
-// Floats of one partial result of a key-tile piece: o (2 groups x hd/32 blocks x 16), the
-// running max and the running sum of each of the 512 threads.
-__host__ __device__ constexpr int attn_part_floats(int hd) { return 512 * (2 * (hd / 32) * 16 + 4); }
-
 // max(x[l], x[l ^ 32]) in every lane l: v_permlane32_swap exchanges the upper half of its
 // first operand with the lower half of its second, so the two results hold, lane by lane,
 // the value of the lane and of its partner in the other half (no LDS round trip).
@@ -132,11 +128,11 @@ __device__ __forceinline__ float max_halves(float x) {
 //     tile sets the max exactly, so the running sum never underflows;
 //   * the row sum adds the bf16-rounded probabilities (the values the second product
 //     uses) with v_dot2_f32_bf16.
-template <int HD, bool PART>
+template <int HD>
 __global__ __launch_bounds__(512, 1)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int ld,
                      const uint16_t* __restrict__ vt, int Ns, uint16_t* __restrict__ out, int N,
-                     int H, int nqb, int item0, int nsplit, float* __restrict__ part) {
+                     int H, int nqb) {
   constexpr int NW = 8, BQ = NW * 64, BKV = 64, S = 4;
   constexpr int KS = HD / 16;                   // MFMA k-steps over the head dim
   constexpr int DT = HD / 32;                   // 32-dim blocks of the output
@@ -159,16 +155,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // blocks of one (clip, head), which read the same keys and values, share an XCD's L2.
   int wg = blockIdx.x;
   if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
-  // item = (clip, head, query block); with PART the workgroup runs key-tile piece
-  // wg % nsplit of item item0 + wg / nsplit and leaves an unnormalised partial result
-  const int item = item0 + (PART ? wg / nsplit : wg);
-  const int qblk = item % nqb, bh = item / nqb;
+  const int qblk = wg % nqb, bh = wg / nqb;
   const int head = bh % H, b = bh / H;
   const int D = H * HD;
-  const int ntiles_all = (N + 63) / 64;
-  const int piece = PART ? wg % nsplit : 0;
-  const int ts = PART ? piece * ntiles_all / nsplit : 0;
-  const int te = PART ? (piece + 1) * ntiles_all / nsplit : ntiles_all;
 
   // K rows are 128 B (hd 64) or 64 B (hd 32), V^T rows 128 B; chunk c of row r sits at
   // c ^ kkey(r) (K) or c ^ lds_key128(r) (V^T)
@@ -178,7 +167,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const uint32_t sbase = lds_addr(smem);
   const uint16_t* kbase = k + static_cast<size_t>(b) * N * ld + head * HD;
   const uint16_t* vbase = vt + static_cast<size_t>(b * H + head) * HD * Ns;
-  const int ntiles = te - ts;                  // key tiles of this workgroup
+  const int ntiles = (N + BKV - 1) / BKV;
 
   // Tile t into buffer t % S: instruction i = qd*NW + wave of the tile fills 1 KB of K
   // (i < K_INS) or of V^T.  K rows past N repeat row N - 1 (their scores are masked); V^T
@@ -186,7 +175,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // launch_attention_fwd); positions of keys past N are zeroed in LDS below.
   auto issue = [&](int t) {
     const uint32_t st = sbase + (t % S) * STAGE;
-    const int kb = (ts + t) * BKV;
+    const int kb = t * BKV;
 #pragma unroll
     for (int qd = 0; qd < LOADS; ++qd) {
       const int ins = qd * NW + wave;
@@ -256,9 +245,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         issue(issued);
         ++issued;
       }
-      if (t == ntiles - 1 && (ts + t) * BKV + BKV > N) {
+      if (t == ntiles - 1 && t * BKV + BKV > N) {
         unsigned char* st = smem + (t % S) * STAGE;
-        const int kb = (ts + t) * BKV;
+        const int kb = t * BKV;
         for (int e = tid; e < HD * BKV; e += NW * 64) {
           const int dim = e / BKV, pos = e - dim * BKV;
           if (kb + vt_pos(pos) >= N)
@@ -307,7 +296,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   // Softmax of tile t's scores into pf, updating m_run, l_run (and o on a rescale).
   auto softmax = [&](int t) __attribute__((always_inline)) {
-    const int kb = (ts + t) * BKV;
+    const int kb = t * BKV;
     if (kb + BKV > N) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
@@ -413,21 +402,6 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     mma_pv(ntiles - 1);
   }
 
-  if constexpr (PART) {
-    // unnormalised o, running max and sum of this piece, thread-major (coalesced)
-    constexpr int NT = NW * 64;
-    float* dst = part + static_cast<size_t>(wg) * attn_part_floats(HD);
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dst[((g * DT + dt) * 16 + i) * NT + tid] = o[g][dt][i];
-      dst[(2 * DT * 16 + g) * NT + tid] = m_run[g];
-      dst[(2 * DT * 16 + 2 + g) * NT + tid] = l_run[g];
-    }
-    return;
-  }
   // ---- normalise and store: element i of o[g][dt] is dim 32 dt + 8(i/4) + 4h + i%4
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -448,134 +422,34 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 }
 
-// Result of items split into nsplit key-tile pieces: thread tid of workgroup it combines
-// the pieces' partial results for its queries (the attention kernel's thread layout) over
-// a common running max, normalises and stores.
-template <int HD>
-__global__ __launch_bounds__(512)
-void attn_merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ out, int N, int H,
-                       int nqb, int item0, int nsplit) {
-  constexpr int DT = HD / 32, NT = 512, PF = attn_part_floats(HD);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int item = item0 + blockIdx.x;
-  const int qblk = item % nqb, bh = item / nqb;
-  const int head = bh % H, b = bh / H;
-  const int D = H * HD;
-  const float* base = part + static_cast<size_t>(blockIdx.x) * nsplit * PF;
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    float m = -INFINITY;
-    for (int p = 0; p < nsplit; ++p) m = fmaxf(m, base[p * PF + (2 * DT * 16 + g) * NT + tid]);
-    float l = 0.f, o[DT][16];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-    for (int p = 0; p < nsplit; ++p) {
-      const float* src = base + p * PF;
-      const float a = __builtin_amdgcn_exp2f(src[(2 * DT * 16 + g) * NT + tid] - m);
-      l += a * src[(2 * DT * 16 + 2 + g) * NT + tid];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] += a * src[((g * DT + dt) * 16 + i) * NT + tid];
-    }
-    // both half-waves hold the same running max; each summed its own half of the keys
-    const float inv = 1.0f / (l + __shfl_xor(l, 32));
-    const int qi = qblk * NT + wave * 64 + g * 32 + l32;
-    if (qi < N) {
-      uint16_t* dst = out + (static_cast<size_t>(b) * N + qi) * D + head * HD;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv);
-          pk[1] = pack_bf16x2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g4 + 4 * h) = pk;
-        }
-    }
-  }
-}
-
-static int num_cus_attn() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    hipDeviceProp_t p;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess)
-      n = p.multiProcessorCount;
-    if (n <= 0) n = 256;
-  }
-  return n;
-}
-
-size_t attention_split_bytes(int head_dim) {
-  return static_cast<size_t>(kAttnSplitPieces) * attn_part_floats(head_dim) * 4;
-}
-
-// Pieces per remainder item: the n in [2, 8] (pieces within kAttnSplitPieces) that
-// minimises the rounds of pieces per piece length, ceil(rem * n / cus) / n; 1 if no n
-// beats the plain extra round of whole items.
-static int split_pieces(int rem, int cus) {
-  int best = 1;
-  double best_t = 1.0;
-  for (int n = 2; n <= 8; ++n) {
-    if (static_cast<long long>(rem) * n > kAttnSplitPieces) break;
-    const double t = static_cast<double>((rem * n + cus - 1) / cus) / n;
-    if (t < best_t - 1e-9) {
-      best_t = t;
-      best = n;
-    }
-  }
-  return best;
-}
-
 template <int HD>
 static hipError_t attn_launch(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt, int Ns,
-                              uint16_t* out, int B, int N, int n_head, void* split_ws, hipStream_t s) {
+                              uint16_t* out, int B, int N, int n_head, hipStream_t s) {
   constexpr int LDS = 4 * (64 * HD * 2 + HD * 64 * 2);
   static bool configured = false;
   if (!configured) {
-    for (const void* f : {reinterpret_cast<const void*>(&attn_fwd_kernel<HD, false>),
-                          reinterpret_cast<const void*>(&attn_fwd_kernel<HD, true>)}) {
-      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-      if (e != hipSuccess) return e;
-    }
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<HD>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
     configured = true;
   }
   const int nqb = (N + 511) / 512;
-  const int items = nqb * n_head * B;
-  // Whole rounds of items (one per CU) run whole.  A last, partial round of rem items
-  // leaves CUs idle; with a split workspace those items run instead as nsplit key-tile
-  // pieces each (one workgroup per piece), merged afterwards.
-  const int cus = num_cus_attn();
-  const int rem = items % cus;
-  const int nsplit = split_ws && items > cus && rem > 0 && N >= 2048 ? split_pieces(rem, cus) : 1;
-  const int whole = nsplit > 1 ? items - rem : items;
-  if (whole > 0)
-    attn_fwd_kernel<HD, false><<<dim3(whole), 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb, 0, 1, nullptr);
-  if (nsplit > 1) {
-    float* part = static_cast<float*>(split_ws);
-    attn_fwd_kernel<HD, true><<<dim3(rem * nsplit), 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb,
-                                                                   whole, nsplit, part);
-    attn_merge_kernel<HD><<<dim3(rem), 512, 0, s>>>(part, out, N, n_head, nqb, whole, nsplit);
-  }
+  const dim3 grid(nqb * n_head * B);
+  attn_fwd_kernel<HD><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
                                 int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
-                                void* split_ws, hipStream_t s) {
+                                hipStream_t s) {
   if (B <= 0 || N <= 0) return hipSuccess;
   if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N) || Ns % 16 || ld % 8) return hipErrorInvalidValue;
   // 32-bit DMA offsets: one clip's rows of q/k and one (clip, head)'s V^T rows
   if (static_cast<size_t>(N) * ld * 2 >= (size_t(1) << 31) ||
       static_cast<size_t>(head_dim) * Ns * 2 >= (size_t(1) << 31))
     return hipErrorInvalidValue;
-  if (head_dim == 64) return attn_launch<64>(q, k, ld, vt, Ns, out, B, N, n_head, split_ws, s);
-  return attn_launch<32>(q, k, ld, vt, Ns, out, B, N, n_head, split_ws, s);
+  if (head_dim == 64) return attn_launch<64>(q, k, ld, vt, Ns, out, B, N, n_head, s);
+  return attn_launch<32>(q, k, ld, vt, Ns, out, B, N, n_head, s);
 }
 
 // Attention inputs from a projection already in memory (the stand-alone entry point):

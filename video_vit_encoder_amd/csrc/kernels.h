@@ -46,13 +46,9 @@ hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, i
 // Flash attention on prepared inputs: q (rotated, scaled by log2(e)/sqrt(hd)) and k
 // (rotated) rows of leading dimension ld (elements), v transposed [B][H][hd][Ns];
 // out [B*N, H*hd] bf16.
-// Pieces the split workspace of launch_attention_fwd holds (items of a last, partial round
-// of the CUs run as key-tile pieces whose partial results are merged).
-constexpr int kAttnSplitPieces = 768;
-size_t attention_split_bytes(int head_dim);
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
                                 int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
-                                void* split_ws, hipStream_t s);
+                                hipStream_t s);
 // Row stride (keys) of the transposed V layout for N tokens.
 inline int vt_stride(int N) { return (N + 15) / 16 * 16; }
 // Scale folded into q: log2(e) / sqrt(head_dim).
