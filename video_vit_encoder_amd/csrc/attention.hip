@@ -66,7 +66,7 @@ __device__ __forceinline__ void rope_chunk(float* x, int j0, const Thw& g, int l
     const int j = j0 + e;
     if (j < 3 * D3) {
       const int a = j / D3, jl = j - a * D3;
-      const int coord = a == 0 ? g.t : (a == 1 ? g.h : g.w);
+      const int coord = thw_coord(thw_pack(g), a);
       int i0, i1;
       if (layout == 0) {
         i0 = jl % MF;

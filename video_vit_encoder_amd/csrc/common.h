@@ -47,6 +47,16 @@ __device__ __forceinline__ Thw decode_id(int id, int gh, int gw) {
   return r;
 }
 
+// t, h and w (each below 256) one per byte, and the coordinate on axis a (0 t, 1 h, 2 w)
+// taken back by one bit-field extract.  Picking a field of Thw by a lane-varying axis with
+// selects can be lowered to an indexed load from private (scratch) memory instead.
+__device__ __forceinline__ uint32_t thw_pack(const Thw& g) {
+  return static_cast<uint32_t>(g.t) | (static_cast<uint32_t>(g.h) << 8) | (static_cast<uint32_t>(g.w) << 16);
+}
+__device__ __forceinline__ int thw_coord(uint32_t pk, int a) {
+  return static_cast<int>(__builtin_amdgcn_ubfe(pk, 8 * a, 8));
+}
+
 // HBM/L2 -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane p of the wave
 // writes LDS bytes [lds + 16p, lds + 16p + 16) from base + voff.  Issued through inline
 // asm so that the kernel, not the compiler, decides how many of these may still be in

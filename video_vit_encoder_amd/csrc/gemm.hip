@@ -38,7 +38,11 @@ enum { EPI_STORE = 0, EPI_GELU = 1, EPI_RESIDUAL = 2, EPI_QKV64 = 3, EPI_QKV32 =
 // of the row's token ([Notes §4]) and q is scaled by qscale; both are stored in place.
 // v goes to vt [clip][head][dim][Ns], key n of a clip at position vt_pos(n).
 // The epilogue reads the RoPE table from LDS: rows (axis, coord < ts) of the full table
-// are copied after the slab ring at kernel start (3 * ts * kRopeMaxFreq float2).
+// are copied after the slab ring at kernel start, kLdsTabRow float2 apart.  The 32 lanes
+// of a half-wave hold consecutive tokens, up to 32 distinct coordinates on the w axis; a
+// row of kRopeMaxFreq float2 (32 dwords) would put coordinates two apart on the same
+// banks, the padded row (34 dwords) spreads 32 of them over distinct bank pairs.
+constexpr int kLdsTabRow = kRopeMaxFreq + 1;
 struct QkvEpi {
   uint16_t* vt;
   RopeArgs ra;
@@ -194,7 +198,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   // tile's first slab: every wait for that slab or a later one in wave 0 covers it, and
   // the barrier after that wait publishes it.  The slot is rewritten for tile i + 2 only
   // after barriers that follow tile i's epilogue in every wave.
-  const int tab_bytes = (EPI == EPI_QKV64 || EPI == EPI_QKV32) ? 3 * qe.ts * kRopeMaxFreq * 8 : 0;
+  const int tab_bytes = (EPI == EPI_QKV64 || EPI == EPI_QKV32) ? 3 * qe.ts * kLdsTabRow * 8 : 0;
   const uint32_t bias_base = smem_base + C::LDS + tab_bytes;
   const bool has_bias = bias != nullptr;
   auto issue_next = [&]() {
@@ -260,8 +264,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     float2* tabs = reinterpret_cast<float2*>(smem + C::LDS);
     const int n = 3 * qe.ts * kRopeMaxFreq;
     for (int e = tid; e < n; e += C::NT) {
-      const int a = e / (qe.ts * kRopeMaxFreq), rest = e - a * qe.ts * kRopeMaxFreq;
-      tabs[e] = qe.ra.tab[a * kMaxGridSide * kRopeMaxFreq + rest];
+      const int row = e / kRopeMaxFreq, k = e - row * kRopeMaxFreq;   // row = axis * ts + coord
+      const int a = row / qe.ts, c = row - a * qe.ts;
+      tabs[row * kLdsTabRow + k] = qe.ra.tab[(a * kMaxGridSide + c) * kRopeMaxFreq + k];
     }
   }
   // bias of the tile's columns c .. c + 3 (c relative to the tile) for tile it; without a
@@ -326,12 +331,12 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     if constexpr (EPI == EPI_QKV64 || EPI == EPI_QKV32) {
       constexpr int HD = EPI == EPI_QKV64 ? 64 : 32;
       const float2* tabs = reinterpret_cast<const float2*>(smem + C::LDS);
-      Thw g[FI];
+      uint32_t g[FI];   // the row's t, h, w packed by thw_pack
       int clip[FI], nn[FI];
 #pragma unroll
       for (int i = 0; i < FI; ++i) {
         const int row = min(m0 + wm * WM + i * 32 + l32, M - 1);
-        g[i] = rope_token(row, qe.ra, &clip[i]);
+        g[i] = thw_pack(rope_token(row, qe.ra, &clip[i]));
         nn[i] = row - clip[i] * qe.ra.N;
       }
 #pragma unroll
@@ -363,10 +368,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
 #pragma unroll
               for (int pp = 0; pp < 2; ++pp) {
                 const RopePairIdx& pi = pidx[gq][pp];
-                const int c = pi.axis == 0 ? g[i].t : (pi.axis == 1 ? g[i].h : g[i].w);
-                const float2* tr = tabs + (pi.axis * qe.ts + c) * kRopeMaxFreq;
-                cs[gq][pp][0] = pi.rot ? tr[pi.i0] : make_float2(1.f, 0.f);
-                cs[gq][pp][1] = pi.rot ? tr[pi.i1] : make_float2(1.f, 0.f);
+                const float2* tr = tabs + (pi.axis * qe.ts + thw_coord(g[i], pi.axis)) * kLdsTabRow;
+                cs[gq][pp][0] = tr[pi.i0];   // pass-through pairs read the (1, 0) entry
+                cs[gq][pp][1] = tr[pi.i1];
               }
             const float sc = sec == 0 ? qe.qscale : 1.0f;
             u32x2 pk[4];
@@ -463,7 +467,7 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
                               int M, int N, int K, hipStream_t s, const QkvEpi& qe = QkvEpi{}) {
   constexpr bool QKV = EPI == EPI_QKV64 || EPI == EPI_QKV32;
   constexpr int MAX_LDS = 160 * 1024;
-  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kRopeMaxFreq * 8 + 2048 <= MAX_LDS, "LDS for the RoPE table");
+  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kLdsTabRow * 8 + 2048 <= MAX_LDS, "LDS for the RoPE table");
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI, OUT_F32>),
@@ -471,7 +475,7 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int lds = C::LDS + (QKV ? 3 * qe.ts * kRopeMaxFreq * 8 : 0) + 2048;
+  const int lds = C::LDS + (QKV ? 3 * qe.ts * kLdsTabRow * 8 : 0) + 2048;
   const int tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
   const dim3 grid(min(tiles, num_cus()));
   gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, lds, s>>>(A, W, bias, Cp, M, N, K, qe);

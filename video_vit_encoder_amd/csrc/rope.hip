@@ -132,7 +132,7 @@ void rope_table_kernel(float2* __restrict__ tab, RopeSpec r, RopeOmega om, int m
 
 hipError_t launch_rope_table(void* tab, const RopeSpec& r, int head_dim, hipStream_t s) {
   const int m = (2 * ((head_dim / 3) / 2)) / 2;
-  if (m > kRopeMaxFreq) return hipErrorInvalidValue;
+  if (m >= kRopeMaxFreq) return hipErrorInvalidValue;   // the last entry stays (1, 0)
   RopeOmega om{};
   for (int k = 0; k < m; ++k) om.w[k] = 1.0 / pow(static_cast<double>(r.theta), static_cast<double>(k) / m);
   rope_table_kernel<<<(kRopeTabEntries + 255) / 256, 256, 0, s>>>(static_cast<float2*>(tab), r, om, m);

@@ -36,19 +36,23 @@ __device__ __forceinline__ Thw rope_token(int r, const RopeArgs& ra, int* clip) 
 }
 
 // Table coordinates of the pair at head dims (j0, j0 + 1), j0 even: whether it rotates,
-// its axis and the frequency indices of its two dims.
+// its axis and the frequency indices of its two dims.  A pass-through pair points at the
+// last entry of an axis row, which the table holds as (cos, sin) = (1, 0) (frequencies
+// stop below kRopeMaxFreq - 1), so reading it leaves the pair unchanged: readers may skip
+// the rot test.
 struct RopePairIdx {
   int rot, axis, i0, i1;
 };
 template <int HD>
 __device__ __forceinline__ RopePairIdx rope_pair_idx(int j0, int layout) {
   constexpr int D3 = 2 * ((HD / 3) / 2), MF = D3 / 2;
+  static_assert(MF < kRopeMaxFreq, "identity entry");
   RopePairIdx r;
   r.rot = j0 < 3 * D3;
   r.axis = min(j0 / D3, 2);
   const int jl = j0 - r.axis * D3;
-  r.i0 = layout == 0 ? jl % MF : jl >> 1;
-  r.i1 = layout == 0 ? (jl + 1) % MF : jl >> 1;
+  r.i0 = !r.rot ? kRopeMaxFreq - 1 : (layout == 0 ? jl % MF : jl >> 1);
+  r.i1 = !r.rot ? kRopeMaxFreq - 1 : (layout == 0 ? (jl + 1) % MF : jl >> 1);
   return r;
 }
 
@@ -56,7 +60,7 @@ __device__ __forceinline__ RopePairIdx rope_pair_idx(int j0, int layout) {
 __device__ __forceinline__ void rope_apply(float& x0, float& x1, const RopePairIdx& p, const Thw& g,
                                            const float2* tab, int ts) {
   if (!p.rot) return;
-  const int c = p.axis == 0 ? g.t : (p.axis == 1 ? g.h : g.w);
+  const int c = thw_coord(thw_pack(g), p.axis);
   const float2* row = tab + (p.axis * ts + c) * kRopeMaxFreq;
   const float2 cs0 = row[p.i0], cs1 = row[p.i1];
   const float y0 = x0 * cs0.x - x1 * cs0.y;
