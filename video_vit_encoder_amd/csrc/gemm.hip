@@ -43,6 +43,10 @@ enum { EPI_STORE = 0, EPI_GELU = 1, EPI_RESIDUAL = 2, EPI_QKV64 = 3, EPI_QKV32 =
 // row of kRopeMaxFreq float2 (32 dwords) would put coordinates two apart on the same
 // banks, the padded row (34 dwords) spreads 32 of them over distinct bank pairs.
 constexpr int kLdsTabRow = kRopeMaxFreq + 1;
+// After the table and the bias slots: one int4 per rotation pair of a head (at most 32),
+// {byte offset of its two table entries at coordinate 0, bit offset of its axis'
+// coordinate in the packed t, h, w}, built at kernel start.
+constexpr int kPairMapBytes = 32 * 16;
 struct QkvEpi {
   uint16_t* vt;
   RopeArgs ra;
@@ -193,11 +197,11 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
       b_row[q] = static_cast<uint32_t>(static_cast<size_t>(n0 + r) * K * 2) + ((pslot ^ C::key(r)) << 4);
     }
   };
-  // LDS after the ring: [RoPE table of the QKV epilogue] [two 1 KB bias slots].  The bias
-  // columns of tile i go to slot i & 1 by one DMA of wave 0, issued just before the
-  // tile's first slab: every wait for that slab or a later one in wave 0 covers it, and
-  // the barrier after that wait publishes it.  The slot is rewritten for tile i + 2 only
-  // after barriers that follow tile i's epilogue in every wave.
+  // LDS after the ring: [RoPE table of the QKV epilogue] [two 1 KB bias slots] [pair map of
+  // the QKV epilogue].  The bias columns of tile i go to slot i & 1 by one DMA of wave 0,
+  // issued just before the tile's first slab: every wait for that slab or a later one in
+  // wave 0 covers it, and the barrier after that wait publishes it.  The slot is rewritten
+  // for tile i + 2 only after barriers that follow tile i's epilogue in every wave.
   const int tab_bytes = (EPI == EPI_QKV64 || EPI == EPI_QKV32) ? 3 * qe.ts * kLdsTabRow * 8 : 0;
   const uint32_t bias_base = smem_base + C::LDS + tab_bytes;
   const bool has_bias = bias != nullptr;
@@ -261,6 +265,13 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   // slab DMA, so the waits for these loads cannot hold up the ring; the prologue's barrier
   // publishes them.
   if constexpr (EPI == EPI_QKV64 || EPI == EPI_QKV32) {
+    constexpr int HD = EPI == EPI_QKV64 ? 64 : 32;
+    if (tid < HD / 2) {
+      const RopePairIdx r = rope_pair_idx<HD>(2 * tid, qe.ra.layout);
+      const int row0 = r.axis * qe.ts * kLdsTabRow;
+      reinterpret_cast<int4*>(smem + C::LDS + tab_bytes + 2048)[tid] =
+          make_int4((row0 + r.i0) * 8, (row0 + r.i1) * 8, 8 * r.axis, 0);
+    }
     float2* tabs = reinterpret_cast<float2*>(smem + C::LDS);
     const int n = 3 * qe.ts * kRopeMaxFreq;
     for (int e = tid; e < n; e += C::NT) {
@@ -330,7 +341,8 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     tile_of(it, m0, n0);
     if constexpr (EPI == EPI_QKV64 || EPI == EPI_QKV32) {
       constexpr int HD = EPI == EPI_QKV64 ? 64 : 32;
-      const float2* tabs = reinterpret_cast<const float2*>(smem + C::LDS);
+      const unsigned char* tabs = smem + C::LDS;
+      const int4* pmap = reinterpret_cast<const int4*>(smem + C::LDS + tab_bytes + 2048);
       uint32_t g[FI];   // the row's t, h, w packed by thw_pack
       int clip[FI], nn[FI];
 #pragma unroll
@@ -345,16 +357,16 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
         const int col0 = n0 + wn * WN + j * 32;
         const int sec = col0 / qe.D, cin = col0 - sec * qe.D;
         const int head = cin / HD, jb = cin - head * HD;
-        // this lane's columns col0 + 8gq + 4h .. +3: bias and the table coordinates of
+        // this lane's columns col0 + 8gq + 4h .. +3: bias and the pair map entries of
         // their two pairs
         f32x4 bv[4];
-        RopePairIdx pidx[4][2];
+        int4 pm[4][2];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int col = col0 + 8 * gq + 4 * h, jj = jb + 8 * gq + 4 * h;
-          bv[gq] = bias4(it, col - n0);
-          pidx[gq][0] = rope_pair_idx<HD>(jj, qe.ra.layout);
-          pidx[gq][1] = rope_pair_idx<HD>(jj + 2, qe.ra.layout);
+          bv[gq] = bias4(it, col0 + 8 * gq + 4 * h - n0);
+          const int p0 = (jb + 8 * gq + 4 * h) >> 1;
+          pm[gq][0] = pmap[p0];
+          pm[gq][1] = pmap[p0 + 1];
         }
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
@@ -367,10 +379,11 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
             for (int gq = 0; gq < 4; ++gq)
 #pragma unroll
               for (int pp = 0; pp < 2; ++pp) {
-                const RopePairIdx& pi = pidx[gq][pp];
-                const float2* tr = tabs + (pi.axis * qe.ts + thw_coord(g[i], pi.axis)) * kLdsTabRow;
-                cs[gq][pp][0] = tr[pi.i0];   // pass-through pairs read the (1, 0) entry
-                cs[gq][pp][1] = tr[pi.i1];
+                const int4& m = pm[gq][pp];
+                const int c = static_cast<int>(__builtin_amdgcn_ubfe(g[i], m.z, 8)) * (kLdsTabRow * 8);
+                // pass-through pairs read the (1, 0) entry
+                cs[gq][pp][0] = *reinterpret_cast<const float2*>(tabs + m.x + c);
+                cs[gq][pp][1] = *reinterpret_cast<const float2*>(tabs + m.y + c);
               }
             const float sc = sec == 0 ? qe.qscale : 1.0f;
             u32x2 pk[4];
@@ -467,7 +480,8 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
                               int M, int N, int K, hipStream_t s, const QkvEpi& qe = QkvEpi{}) {
   constexpr bool QKV = EPI == EPI_QKV64 || EPI == EPI_QKV32;
   constexpr int MAX_LDS = 160 * 1024;
-  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kLdsTabRow * 8 + 2048 <= MAX_LDS, "LDS for the RoPE table");
+  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kLdsTabRow * 8 + kPairMapBytes + 2048 <= MAX_LDS,
+                "LDS for the RoPE table");
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<C, EPI, OUT_F32>),
@@ -475,7 +489,7 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int lds = C::LDS + (QKV ? 3 * qe.ts * kLdsTabRow * 8 : 0) + 2048;
+  const int lds = C::LDS + (QKV ? 3 * qe.ts * kLdsTabRow * 8 + kPairMapBytes : 0) + 2048;
   const int tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
   const dim3 grid(min(tiles, num_cus()));
   gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, lds, s>>>(A, W, bias, Cp, M, N, K, qe);

@@ -49,10 +49,13 @@ __device__ __forceinline__ RopePairIdx rope_pair_idx(int j0, int layout) {
   static_assert(MF < kRopeMaxFreq, "identity entry");
   RopePairIdx r;
   r.rot = j0 < 3 * D3;
-  r.axis = min(j0 / D3, 2);
+  r.axis = (j0 >= D3) + (j0 >= 2 * D3);   // pass-through pairs land on axis 2
+  // by compares rather than division: a rotated pair has jl in [0, D3 - 2], jl even
   const int jl = j0 - r.axis * D3;
-  r.i0 = !r.rot ? kRopeMaxFreq - 1 : (layout == 0 ? jl % MF : jl >> 1);
-  r.i1 = !r.rot ? kRopeMaxFreq - 1 : (layout == 0 ? (jl + 1) % MF : jl >> 1);
+  const int t0 = jl >= MF ? jl - MF : jl;               // jl mod MF
+  const int t1 = jl + 1 >= MF ? jl + 1 - MF : jl + 1;   // (jl + 1) mod MF
+  r.i0 = !r.rot ? kRopeMaxFreq - 1 : (layout == 0 ? t0 : jl >> 1);
+  r.i1 = !r.rot ? kRopeMaxFreq - 1 : (layout == 0 ? t1 : jl >> 1);
   return r;
 }
 
