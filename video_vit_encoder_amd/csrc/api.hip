@@ -749,8 +749,10 @@ int jepa_timing_begin(int cap) {
   for (int k = 0; k < JEPA_KC_COUNT; ++k) {
     g_timing.n[k] = 0;
     g_timing.ev[k].assign(2 * static_cast<size_t>(cap), nullptr);
+    // timing-only events: no system-scope fence (cache write-back and invalidate) on
+    // record, which would add its own cost to every bracketed launch
     for (hipEvent_t& e : g_timing.ev[k]) {
-      if (hipEventCreate(&e) != hipSuccess) {
+      if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
         (void)hipGetLastError();
         for (int j = 0; j <= k; ++j)
           for (hipEvent_t& f : g_timing.ev[j])
