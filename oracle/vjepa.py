@@ -19,7 +19,7 @@ __all__ = [
     "normalize_frames", "patchify", "id_to_thw", "rope_positions", "rope_axis_dim",
     "rope_omegas", "rope_angle_index", "rope_angles", "rope_rotate", "rope_rotate_with_angles",
     "layer_norm", "gelu_erf", "linear", "attention", "block", "encoder_forward",
-    "encode_tokens", "encoder_forward_batch", "predictor_forward",
+    "encode_tokens", "encoder_forward_batch", "masked_encoder_forward", "predictor_forward",
 ]
 
 # [Notes §1 "pre.mean / std / rescale": ImageNet, 1/255]; values as given on [HFport
@@ -320,6 +320,30 @@ def encoder_forward(clip: np.ndarray, W: Dict[str, np.ndarray], spec: EncoderSpe
     grid = (T // spec.tubelet, H // spec.patch, Wd_ // spec.patch)
     ids = np.arange(grid[0] * grid[1] * grid[2])
     return encode_tokens(x, W, spec, ids, grid, last_rows=last_rows)
+
+
+def masked_encoder_forward(clip: np.ndarray, W: Dict[str, np.ndarray], spec: EncoderSpec,
+                           ctx_ids: np.ndarray) -> np.ndarray:
+    """Pre-training forward on the context tokens of one clip, uint8 [T, H, W, 3] ->
+    [K, D] float64 for the K grid ids ``ctx_ids`` ([HFport "Usage"]: masks passed to the
+    encoder; [HFport "Validation"], masked-encoder row).
+
+    The tokens outside ``ctx_ids`` are dropped before the first block: the patch rows are
+    embedded as in ``encoder_forward``, the rows of the kept ids are taken in the given
+    order, and the blocks and the final norm run on those K rows with the RoPE positions
+    of their own grid ids.  Attention therefore sees only the context, which is not the
+    same as taking rows of the full forward's output.
+    """
+    X = normalize_frames(clip)
+    p = patchify(X, spec.tubelet, spec.patch)
+    Wd = _f64(W)
+    x = linear(p, Wd["enc.patch_embed.weight"], Wd["enc.patch_embed.bias"])
+    if spec.has_mod_embed:
+        x = x + Wd["enc.mod_embed_video"]
+    T, H, Wd_ = clip.shape[0], clip.shape[1], clip.shape[2]
+    grid = (T // spec.tubelet, H // spec.patch, Wd_ // spec.patch)
+    ids = np.asarray(ctx_ids, dtype=np.int64)
+    return encode_tokens(x[ids], W, spec, ids, grid)
 
 
 def encoder_forward_batch(clips: np.ndarray, W, spec: EncoderSpec) -> np.ndarray:

@@ -116,8 +116,9 @@ def block(x, W, prefix, n_head, pos, layout, theta, eps):
 
 
 def encoder(clip, Wnp: Dict, n_layer, n_head, layout, ref_grid=0, mod_embed=False,
-            final_norm=True, theta=10000.0, eps=1e-6, tubelet=2, patch=16):
-    """clip: uint8 [T, H, W, 3] (numpy or nested lists)."""
+            final_norm=True, theta=10000.0, eps=1e-6, tubelet=2, patch=16, ctx_ids=None):
+    """clip: uint8 [T, H, W, 3] (numpy or nested lists).  ctx_ids: keep only these tokens
+    (in this order) before the first block, each at its own grid position."""
     W = {k: to_list(v) for k, v in Wnp.items()}
     c = to_list(clip)
     T, H, Wd = len(c), len(c[0]), len(c[0][0])
@@ -138,6 +139,10 @@ def encoder(clip, Wnp: Dict, n_layer, n_head, layout, ref_grid=0, mod_embed=Fals
     if mod_embed:
         x = [[r[i] + W["enc.mod_embed_video"][i] for i in range(len(r))] for r in x]
     pos = [positions(n, gh, gw, ref_grid) for n in range(N)]
+    if ctx_ids is not None:
+        keep = [int(i) for i in ctx_ids]
+        x = [x[i] for i in keep]
+        pos = [pos[i] for i in keep]
     for li in range(n_layer):
         x = block(x, W, f"enc.blk.{li}", n_head, pos, layout, theta, eps)
     if final_norm:
