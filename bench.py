@@ -1,6 +1,6 @@
 """Throughput of the V-JEPA 2 ViT-L/16 encoder forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--masked]
 
 One step is one jepa_encode call on a batch of 4 synthetic clips of 16 frames x 256x256
 uint8 (2048 tokens per clip, 8192 token rows), already resident in HBM: patch
@@ -18,6 +18,11 @@ on the stream the library launches on, bracketed by device synchronisation).  Be
   * ``kernels``: the same figures for every kernel class of the step;
   * ``cpu_baseline``: the float64 oracle timed on the host on one clip through a few
     layers, scaled to the 24-layer forward (a reported baseline, not a target).
+
+``--masked`` measures the masked-encoder forward instead (jepa_encode_masked, the
+pre-training path): the same clips, each with the context of a seeded tube mask (an 8x8
+block of patches in every temporal slot, 512 of the 2048 tokens); ``value`` is context
+tokens/s and the oracle baseline runs oracle.masked_encoder_forward.
 """
 from __future__ import annotations
 
@@ -123,9 +128,10 @@ def measured_traffic(kind):
     return ent["read_bytes"] + ent["write_bytes"]
 
 
-def cpu_baseline(w, W, clips, budget_layers=12):
+def cpu_baseline(w, W, clips, budget_layers=12, ids0=None):
     """The float64 oracle on clip 0: patch embedding + final norm alone, then with
-    ``budget_layers`` blocks; the per-block time scales the forward to 24 blocks."""
+    ``budget_layers`` blocks; the per-block time scales the forward to 24 blocks.  With
+    ``ids0`` the masked forward on those context tokens."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -137,17 +143,23 @@ def cpu_baseline(w, W, clips, budget_layers=12):
     def spec(n):
         return oracle.EncoderSpec(e.embed_dim, n, e.n_head, e.ffn_dim, layout=w["layout"])
 
+    def run(n):
+        if ids0 is None:
+            return oracle.encoder_forward(clips[0], W, spec(n))
+        return oracle.masked_encoder_forward(clips[0], W, spec(n), ids0)
+
     t0 = time.perf_counter()
-    oracle.encoder_forward(clips[0], W, spec(0))
+    run(0)
     t_fixed = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.encoder_forward(clips[0], W, spec(budget_layers))
+    run(budget_layers)
     t_run = time.perf_counter() - t0
     t_layer = max(t_run - t_fixed, 1e-9) / budget_layers
     t_clip = t_fixed + e.n_layer * t_layer
-    N = w["grid"][0] * w["grid"][1] * w["grid"][2]
+    N = w["grid"][0] * w["grid"][1] * w["grid"][2] if ids0 is None else len(ids0)
+    what = "masked forward, " if ids0 is not None else ""
     return {"value": N / t_clip, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"float64 numpy oracle, clip 0 only (2048 tokens): embedding+norm "
+            "sample": (f"float64 numpy oracle, {what}clip 0 only ({N} tokens): embedding+norm "
                        f"{t_fixed:.2f} s, {budget_layers} blocks {t_run - t_fixed:.2f} s; "
                        f"scaled to 24 blocks = {t_clip:.1f} s/clip")}
 
@@ -160,6 +172,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--masked", action="store_true",
+                    help="time the masked-encoder forward on tube-mask contexts (512 of 2048 "
+                         "tokens per clip) instead of the full forward")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy 3 times, the "
                          "reference for scaling HBM traffic counters")
@@ -186,7 +201,21 @@ def main():
                     max_rows=B * N)
     enc.set_weights(W)
     clip_d = torch.from_numpy(clips).to(dev)
-    out = torch.empty((B, N, D), dtype=torch.float32, device=dev)
+    ids = None
+    if args.masked:
+        ids = np.stack([synth.tube_mask(args.seed + b, *w["grid"])[0] for b in range(B)])
+        ids_d = torch.from_numpy(ids.astype(np.int32)).to(dev)
+        K = ids.shape[1]
+        out = torch.empty((B, K, D), dtype=torch.float32, device=dev)
+
+        def step():
+            enc.encode_masked(clip_d, ids_d, out=out)
+    else:
+        K = N
+        out = torch.empty((B, N, D), dtype=torch.float32, device=dev)
+
+        def step():
+            enc.encode(clip_d, out=out)
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -196,7 +225,7 @@ def main():
         del src, dst
     log("warmup")
     for _ in range(args.warmup):
-        enc.encode(clip_d, out=out)
+        step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -204,15 +233,15 @@ def main():
     t_wall = time.perf_counter()
     start.record()
     for _ in range(args.steps):
-        enc.encode(clip_d, out=out)
+        step()
     end.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(end) / args.steps
     if not bool(torch.isfinite(out).all()):
         raise RuntimeError("non-finite encoder output")
-    tok_s = B * N / (ms * 1e-3)
-    flops = forward_flops(B, N, D, F, L)
+    tok_s = B * K / (ms * 1e-3)
+    flops = forward_flops(B, K, D, F, L)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{ms:.3f} ms/step, {tok_s:,.0f} tokens/s, {tflops:.1f} TFLOP/s "
         f"(wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
@@ -220,19 +249,20 @@ def main():
     roof, kernels = None, None
     if not args.no_kernels:
         log(f"per-kernel launch timing over {args.steps} more steps (HIP events in the library)")
-        kernels, prof_ms = kernel_timing(J, lambda: enc.encode(clip_d, out=out), args.steps,
-                                         kernel_work(B, N, D, F, L))
+        kernels, prof_ms = kernel_timing(J, step, args.steps, kernel_work(B, K, D, F, L))
         dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
         k = kernels[dom]
+        # the committed counter passes were taken on the full forward's shapes
+        traffic = None if args.masked else measured_traffic(dom)
         if k["bound"] == "mfma":
             roof = {"kernel": dom, "bound": "mfma", "achieved": k["tflops"],
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": k["frac"],
-                    "traffic": measured_traffic(dom), "launch_ms": k["avg_ms"],
+                    "traffic": traffic, "launch_ms": k["avg_ms"],
                     "flops_per_launch": k["flops_per_launch"]}
         else:
             roof = {"kernel": dom, "bound": "hbm", "achieved": k["gbs"],
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": k["frac"],
-                    "traffic": measured_traffic(dom), "launch_ms": k["avg_ms"],
+                    "traffic": traffic, "launch_ms": k["avg_ms"],
                     "bytes_per_launch": k["bytes_per_launch"]}
         log(f"dominant kernel {dom}: {k['avg_ms'] * 1e3:.1f} us/launch, frac {k['frac']:.3f}; "
             f"timed pass {prof_ms:.3f} ms/step (wall)")
@@ -240,17 +270,24 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(w, W, clips)
+        cpu = cpu_baseline(w, W, clips, ids0=None if ids is None else ids[0])
 
+    metric = "encoder tokens/sec at 1 GPU (ViT-L, 16f/256px); % bf16 MFMA peak"
+    workload = ("V-JEPA 2 ViT-L/16 encoder forward, 4 clips x 16 frames x 256x256 (2048 tokens "
+                "per clip), 24 layers, bf16 MFMA")
+    if args.masked:
+        metric = "masked-encoder context tokens/sec at 1 GPU (ViT-L, 16f/256px); % bf16 MFMA peak"
+        workload = ("V-JEPA 2 ViT-L/16 masked-encoder forward, 4 clips x 16 frames x 256x256, "
+                    f"context = tube mask of 8x8 patches in each of 8 temporal slots ({K} of "
+                    f"{N} tokens per clip), 24 layers, bf16 MFMA")
     res = {
-        "metric": "encoder tokens/sec at 1 GPU (ViT-L, 16f/256px); % bf16 MFMA peak",
+        "metric": metric,
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (uniform uint8 clips, random N(0,0.02) bf16 weights)",
-        "config": {"workload": "V-JEPA 2 ViT-L/16 encoder forward, 4 clips x 16 frames x "
-                               "256x256 (2048 tokens per clip), 24 layers, bf16 MFMA",
-                   "batch_clips": B, "tokens_per_clip": N, "embed_dim": D, "layers": L,
+        "config": {"workload": workload,
+                   "batch_clips": B, "tokens_per_clip": K, "embed_dim": D, "layers": L,
                    "heads": H, "ffn_dim": F, "rope": "tiled 3-D"},
         "clips_per_s": round(B / (ms * 1e-3), 2),
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),

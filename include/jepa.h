@@ -141,6 +141,27 @@ int jepa_encode_tokens(jepa_encoder* enc, const float* x_dev, int B, int N,
                        const int32_t* ids_dev, int gt, int gh, int gw, float* out_dev,
                        void* stream);
 
+/* Masked-encoder forward, the pre-training path ([HFport "Usage"]: masks passed to the
+ * encoder; [HFport "Validation"], masked-encoder row): the tokens outside each clip's
+ * context are dropped before the first block, so attention sees only the context and
+ * RoPE takes each kept token's own grid position.  This differs from taking rows of
+ * jepa_encode's output.
+ *   clip_dev: uint8 [B, T, H, W, 3] as for jepa_encode (same preprocessing);
+ *   ids_dev:  int32 [B, K] device array, the context tokens of clip b are
+ *             ids_dev[b*K .. b*K + K) as T-major grid ids in [0, N), N = (T/2)(H/16)(W/16);
+ *             any order, one clip's list may differ from another's; values outside
+ *             [0, N) are clamped;
+ *   out_dev:  fp32 [B, K, D], row k of clip b for token ids_dev[b*K + k].
+ * Only the K context tubelets of each clip are patchified and embedded (the embedding
+ * acts on each row alone), then the blocks and the final norm run on B clips of K tokens.
+ * Needs B*K <= max_rows (not B*N).  Asynchronous on `stream`; the caller keeps ids_dev
+ * alive until the work is done.
+ * Errors: JEPA_ERR_ARG (null pointer); JEPA_ERR_SHAPE (T, H, W, interpolation as for
+ * jepa_encode; K < 1 or K > N; B*K > max_rows; on the bf16 path also
+ * B*ceil(K/16)*16 > 2*max_rows + 1024); JEPA_ERR_STATE (a tensor never set). */
+int jepa_encode_masked(jepa_encoder* enc, const uint8_t* clip_dev, int B, int T, int H, int W,
+                       const int32_t* ids_dev, int K, float* out_dev, void* stream);
+
 /* ------------------------------------------------------------------ predictor */
 
 /* V-JEPA 2 masked predictor ([Notes §1]: 384 / 12 / 12 / 1536, 10 mask tokens, output

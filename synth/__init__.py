@@ -183,6 +183,13 @@ def tube_mask(seed: int, gt: int, gh: int, gw: int, bh: int = 8, bw: int = 8,
     return ids[flat], ids[~flat]
 
 
+def context_ids(seed: int, B: int, N: int, K: int, k: int = 4) -> np.ndarray:
+    """Seeded context ids of the masked-encoder forward: for each of B clips, K distinct
+    grid ids in [0, N) in random order.  int32 [B, K]."""
+    g = rng(seed, k)
+    return np.stack([g.permutation(N)[:K] for _ in range(B)]).astype(np.int32)
+
+
 # --------------------------------------------------------------------------- workloads
 
 # The five workloads of the build, by what they are.  ``grid`` is (t, h, w) in

@@ -3,8 +3,8 @@ masked predictor) as hand-written gfx950 HIP kernels behind the C ABI of include
 
 The functions named ``jepa_*`` are the C entry points (see ``_lib``).  ``Encoder`` and
 ``Predictor`` are small owners of a C handle: they upload a dict of host weights by name
-and call ``jepa_encode`` / ``jepa_encode_tokens`` / ``jepa_predict``.  Nothing here
-computes any part of the forward.
+and call ``jepa_encode`` / ``jepa_encode_masked`` / ``jepa_encode_tokens`` /
+``jepa_predict``.  Nothing here computes any part of the forward.
 """
 from __future__ import annotations
 
@@ -14,7 +14,8 @@ import numpy as np
 
 from ._lib import (  # noqa: F401
     DTYPES, JEPA_BF16, JEPA_EPI_GELU, JEPA_EPI_RESIDUAL, JEPA_EPI_STORE, JEPA_F32, LAYOUTS,
-    KERNEL_CLASSES, JepaError, header_functions, jepa_attention, jepa_attention_workspace_size, jepa_encode, jepa_encode_tokens,
+    KERNEL_CLASSES, JepaError, header_functions, jepa_attention, jepa_attention_workspace_size,
+    jepa_encode, jepa_encode_masked, jepa_encode_tokens,
     jepa_encoder_config, jepa_encoder_create, jepa_encoder_free, jepa_encoder_set_tensor,
     jepa_layernorm, jepa_linear, jepa_predict, jepa_predictor_config, jepa_predictor_create,
     jepa_predictor_free, jepa_predictor_set_tensor, jepa_rope3d, jepa_status_str,
@@ -50,6 +51,16 @@ class Encoder:
         if out is None:
             out = torch.empty((B, N, self.embed_dim), dtype=torch.float32, device=clip.device)
         jepa_encode(self.handle, clip, out, stream)
+        return out
+
+    def encode_masked(self, clip, ids, out=None, stream=None):
+        """clip: uint8 device tensor [B, T, H, W, 3], ids: int32 device tensor [B, K] ->
+        fp32 [B, K, D], the blocks run on each clip's K context tokens only."""
+        import torch
+        if out is None:
+            out = torch.empty((clip.shape[0], ids.shape[1], self.embed_dim), dtype=torch.float32,
+                              device=clip.device)
+        jepa_encode_masked(self.handle, clip, ids, out, stream)
         return out
 
     def encode_tokens(self, x, grid: Sequence[int], ids=None, out=None, stream=None):

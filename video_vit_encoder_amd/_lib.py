@@ -64,6 +64,7 @@ _SIGS = {
     "jepa_encoder_set_tensor": ([_P, ctypes.c_char_p, _P, _I, ctypes.POINTER(_I64), _I], _I),
     "jepa_encode": ([_P, _P, _I, _I, _I, _I, _P, _P], _I),
     "jepa_encode_tokens": ([_P, _P, _I, _I, _P, _I, _I, _I, _P, _P], _I),
+    "jepa_encode_masked": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
     "jepa_predictor_create": ([ctypes.POINTER(jepa_predictor_config), ctypes.POINTER(_P)], _I),
     "jepa_predictor_free": ([_P], None),
     "jepa_predictor_set_tensor": ([_P, ctypes.c_char_p, _P, _I, ctypes.POINTER(_I64), _I], _I),
@@ -218,6 +219,20 @@ def jepa_encode_tokens(handle: int, x, ids, grid: Sequence[int], out, stream=Non
     _check("jepa_encode_tokens",
            load().jepa_encode_tokens(handle, _ptr(x), B, N, _ptr(ids), gt, gh, gw, _ptr(out),
                                      _stream(stream)))
+
+
+def jepa_encode_masked(handle: int, clip, ids, out, stream=None) -> None:
+    """clip: uint8 device tensor [B, T, H, W, 3]; ids: int32 device tensor [B, K] (context
+    grid ids of each clip); out: fp32 device tensor [B, K, D]."""
+    B, T, H, W, C = clip.shape
+    _need(C == 3 and clip.dtype == _torch().uint8, "clip must be uint8 [B, T, H, W, 3]")
+    _need(ids is not None and ids.dtype == _torch().int32 and ids.dim() == 2 and ids.shape[0] == B
+          and ids.is_contiguous(), "ids must be contiguous int32 [B, K]")
+    K = ids.shape[1]
+    _need(out.dtype == _torch().float32 and out.numel() == B * K * _enc_dim(handle),
+          "out must be fp32 [B, K, D]")
+    _check("jepa_encode_masked", load().jepa_encode_masked(handle, _ptr(clip), B, T, H, W, _ptr(ids), K,
+                                                           _ptr(out), _stream(stream)))
 
 
 def jepa_predictor_create(cfg: jepa_predictor_config) -> int:

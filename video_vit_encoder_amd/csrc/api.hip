@@ -313,10 +313,11 @@ hipError_t linear(int compute, const void* A, const void* W, const float* bias, 
 
 // The pre-norm blocks over x (fp32 [B*N, D], in place).  On the bf16 path the QKV
 // projection's epilogue applies the 3-D RoPE to q and k (q also takes log2(e)/sqrt(hd))
-// and writes v transposed; the attention kernel then reads all three by DMA.
+// and writes v transposed; the attention kernel then reads all three by DMA.  Token n of
+// clip b sits at grid id ids[b * ids_stride + n] (ids NULL: n).
 int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_run, Workspace& ws,
                float* x, int B, int N, int D, int F, int n_head, float eps, const int32_t* ids,
-               const RopeSpec& rs, hipStream_t s) {
+               int ids_stride, const RopeSpec& rs, hipStream_t s) {
   const int compute = ts.compute;
   const int bf = compute == JEPA_BF16 ? 1 : 0;
   const int M = B * N;
@@ -336,7 +337,7 @@ int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_r
       JEPA_LAUNCH(JEPA_KC_GEMM_QKV, s,
                   launch_gemm_bf16_qkv(static_cast<const uint16_t*>(ws.h.p),
                                        static_cast<const uint16_t*>(ts.dev(b.qkvw)), ts.devf(b.qkvb),
-                                       qkv, vt, Ns, M, D, D, hd, ids, N, rs, ws.tab.p,
+                                       qkv, vt, Ns, M, D, D, hd, ids, ids_stride, N, rs, ws.tab.p,
                                        attn_qscale(hd), s));
       JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
                   launch_attention_fwd(qkv, qkv + D, 3 * D, vt, Ns, static_cast<uint16_t*>(ws.o.p), B,
@@ -347,7 +348,8 @@ int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_r
                          JEPA_EPI_STORE, 1, s));
       JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
                   launch_attention_f32(static_cast<const float*>(ws.qkv.p),
-                                       static_cast<float*>(ws.o.p), B, N, n_head, hd, ids, rs, s));
+                                       static_cast<float*>(ws.o.p), B, N, n_head, hd, ids,
+                                       ids_stride, rs, s));
     }
     JEPA_LAUNCH(JEPA_KC_GEMM_OUT, s,
                 linear(compute, ws.o.p, ts.dev(b.outw), ts.devf(b.outb), x, M, D, D,
@@ -484,7 +486,7 @@ int jepa_encode(jepa_encoder* enc, const uint8_t* clip_dev, int B, int T, int H,
                      JEPA_EPI_STORE, 1, s));
   const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, c.rope_ref_grid};
   JEPA_TRY(run_blocks(enc->ts, enc->blocks, c.n_layer, enc->ws, out_dev, B, static_cast<int>(N), D,
-                      c.ffn_dim, c.n_head, c.ln_eps, nullptr, rs, s));
+                      c.ffn_dim, c.n_head, c.ln_eps, nullptr, 0, rs, s));
   if (c.final_norm)
     JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
                 launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M,
@@ -511,7 +513,42 @@ int jepa_encode_tokens(jepa_encoder* enc, const float* x_dev, int B, int N,
                                hipMemcpyDeviceToDevice, s));
   const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, c.rope_ref_grid};
   JEPA_TRY(run_blocks(enc->ts, enc->blocks, c.n_layer, enc->ws, out_dev, B, N, D, c.ffn_dim,
-                      c.n_head, c.ln_eps, ids_dev, rs, s));
+                      c.n_head, c.ln_eps, ids_dev, 0, rs, s));
+  if (c.final_norm)
+    JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
+                launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M,
+                                 D, c.ln_eps, out_dev, 0, s));
+  return JEPA_OK;
+}
+
+int jepa_encode_masked(jepa_encoder* enc, const uint8_t* clip_dev, int B, int T, int H, int W,
+                       const int32_t* ids_dev, int K, float* out_dev, void* stream) {
+  if (!enc || !clip_dev || !ids_dev || !out_dev) return JEPA_ERR_ARG;
+  const jepa_encoder_config& c = enc->cfg;
+  if (B < 1 || T < 2 || T % 2 || H < 16 || W < 16 || H % 16 || W % 16) return JEPA_ERR_SHAPE;
+  const int gt = T / 2, gh = H / 16, gw = W / 16;
+  JEPA_TRY(check_grid(gt, gh, gw, c.rope_ref_grid));
+  const long long N = static_cast<long long>(gt) * gh * gw;
+  if (K < 1 || K > N) return JEPA_ERR_SHAPE;
+  if (static_cast<long long>(B) * K > c.max_rows) return JEPA_ERR_SHAPE;
+  if (!enc->ts.all_set()) return JEPA_ERR_STATE;
+  JEPA_TRY(refresh_pe_bias(enc));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int M = B * K;
+  const int D = c.embed_dim, bf = c.compute == JEPA_BF16 ? 1 : 0;
+  const int feat = c.in_chans * c.tubelet * c.patch * c.patch;
+  // [HFport "Usage"]: the tokens outside the context are dropped before the blocks.  The
+  // patch embedding acts on each row alone, so only the K context tubelets of each clip
+  // are patchified and embedded.
+  JEPA_LAUNCH(JEPA_KC_PATCHIFY, s,
+              launch_patchify(clip_dev, B, T, H, W, enc->ws.a.p, bf, s, ids_dev, K));
+  JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
+              linear(c.compute, enc->ws.a.p, enc->ts.dev(enc->pe_w),
+                     static_cast<const float*>(enc->pe_bias_eff.p), out_dev, M, D, feat,
+                     JEPA_EPI_STORE, 1, s));
+  const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, c.rope_ref_grid};
+  JEPA_TRY(run_blocks(enc->ts, enc->blocks, c.n_layer, enc->ws, out_dev, B, K, D, c.ffn_dim,
+                      c.n_head, c.ln_eps, ids_dev, K, rs, s));
   if (c.final_norm)
     JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
                 launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M,
@@ -624,7 +661,7 @@ int jepa_predict(jepa_predictor* pred, const float* z_dev, int n_enc,
                              hipMemcpyDeviceToDevice, s));
   const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, 0};
   JEPA_TRY(run_blocks(pred->ts, pred->blocks, c.n_layer, pred->ws, x, 1, M, E, c.ffn_dim,
-                      c.n_head, c.ln_eps, ids, rs, s));
+                      c.n_head, c.ln_eps, ids, 0, rs, s));
   // final norm and output projection on the target rows only
   float* xt = x + static_cast<size_t>(n_ctx) * E;
   JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
@@ -726,7 +763,7 @@ int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, 
   if (dtype == JEPA_F32)
     return hip_status(launch_attention_f32(static_cast<const float*>(qkv_dev),
                                            static_cast<float*>(out_dev), B, N, n_head, head_dim,
-                                           ids_dev, rs, s));
+                                           ids_dev, 0, rs, s));
   const int D = n_head * head_dim;
   if (D % 32) return JEPA_ERR_SHAPE;
   size_t off_qk, off_vt;

@@ -496,7 +496,7 @@ hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, i
   if (B <= 0 || N <= 0) return hipSuccess;
   if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N)) return hipErrorInvalidValue;
   const int D = n_head * head_dim;
-  const RopeArgs ra{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw};
+  const RopeArgs ra{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw, 0};
   const long long M = static_cast<long long>(B) * N;
   const long long total = M * (3 * D / 4);
   const dim3 grid(static_cast<unsigned>(min(total, 256LL * 2048) / 256 + 1));
@@ -520,7 +520,8 @@ static RopeFreq make_freq(int head_dim, float theta) {
 template <int HD>
 __global__ __launch_bounds__(64)
 void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out, int N, int H,
-                     const int32_t* __restrict__ ids, RopeSpec r, RopeFreq fr, float scale) {
+                     const int32_t* __restrict__ ids_all, int ids_stride, RopeSpec r, RopeFreq fr,
+                     float scale) {
   constexpr int D3 = 2 * ((HD / 3) / 2);
   constexpr int MF = D3 / 2;
   constexpr int BKV = 64;
@@ -528,6 +529,7 @@ void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out, int
   __shared__ float Ks[BKV][HD];
   __shared__ float Vs[BKV][HD];
   const int tid = threadIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const int32_t* ids = ids_all ? ids_all + static_cast<size_t>(b) * ids_stride : nullptr;
   const int D = H * HD, ld = 3 * D;
   const int ntot = r.gt * r.gh * r.gw;
   const float* base = qkv + static_cast<size_t>(b) * N * ld + head * HD;
@@ -592,16 +594,16 @@ void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out, int
 }
 
 hipError_t launch_attention_f32(const float* qkv, float* out, int B, int N, int n_head,
-                                int head_dim, const int32_t* ids, const RopeSpec& r,
-                                hipStream_t s) {
+                                int head_dim, const int32_t* ids, int ids_stride,
+                                const RopeSpec& r, hipStream_t s) {
   if (B <= 0 || N <= 0) return hipSuccess;
   const RopeFreq fr = make_freq(head_dim, r.theta);
   const float scale = static_cast<float>(1.0 / sqrt(static_cast<double>(head_dim)));
   const dim3 grid((N + 63) / 64, n_head, B);
   if (head_dim == 64)
-    attn_f32_kernel<64><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, r, fr, scale);
+    attn_f32_kernel<64><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, ids_stride, r, fr, scale);
   else if (head_dim == 32)
-    attn_f32_kernel<32><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, r, fr, scale);
+    attn_f32_kernel<32><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, ids_stride, r, fr, scale);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

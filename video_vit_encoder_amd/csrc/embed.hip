@@ -10,20 +10,24 @@ namespace jepa {
 // (px - 255*mean)/(255*std) with the ImageNet statistics ([Parity "Preprocessing
 // parity"]).  One thread per (token, dt, dy): it reads the 16 pixels x 3 channels of one
 // image row segment (48 contiguous bytes of THWC input) and writes the three 16-wide
-// feature runs c*512 + dt*256 + dy*16 + [0, 16).
+// feature runs c*512 + dt*256 + dy*16 + [0, 16).  With ids, output row b*K + k is the
+// tubelet of token ids[b*K + k] of clip b (the context tokens of the masked forward,
+// [HFport "Usage"]); ids outside [0, N) are clamped.
 template <bool BF16>
 __global__ __launch_bounds__(256)
 void patchify_kernel(const uint8_t* __restrict__ clip, int B, int T, int H, int W,
-                     void* __restrict__ out) {
+                     void* __restrict__ out, const int32_t* __restrict__ ids, int K) {
   const int gt = T / 2, gh = H / 16, gw = W / 16;
-  const long long ntok = static_cast<long long>(B) * gt * gh * gw;
+  const int per_clip = gt * gh * gw;
+  const int rows = ids ? K : per_clip;   // output rows per clip
+  const long long ntok = static_cast<long long>(B) * rows;
   const long long gid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gid >= ntok * 32) return;
   const long long tokg = gid >> 5;
   const int sub = static_cast<int>(gid & 31), dt = sub >> 4, dy = sub & 15;
-  const int per_clip = gt * gh * gw;
-  const int b = static_cast<int>(tokg / per_clip);
-  const int n = static_cast<int>(tokg - static_cast<long long>(b) * per_clip);
+  const int b = static_cast<int>(tokg / rows);
+  int n = static_cast<int>(tokg - static_cast<long long>(b) * rows);
+  if (ids) n = min(max(ids[tokg], 0), per_clip - 1);
   const int tp = n / (gh * gw), rem = n - tp * gh * gw, hp = rem / gw, wp = rem - hp * gw;
   const int t = 2 * tp + dt, y = 16 * hp + dy, x0 = 16 * wp;
   const uint32_t* src = reinterpret_cast<const uint32_t*>(
@@ -63,14 +67,15 @@ void patchify_kernel(const uint8_t* __restrict__ clip, int B, int T, int H, int 
 }
 
 hipError_t launch_patchify(const uint8_t* clip, int B, int T, int H, int W, void* A, int bf16,
-                           hipStream_t s) {
-  const long long threads = static_cast<long long>(B) * (T / 2) * (H / 16) * (W / 16) * 32;
+                           hipStream_t s, const int32_t* ids, int K) {
+  const long long rows = ids ? static_cast<long long>(K) : static_cast<long long>(T / 2) * (H / 16) * (W / 16);
+  const long long threads = static_cast<long long>(B) * rows * 32;
   if (threads <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
   if (bf16)
-    patchify_kernel<true><<<grid, 256, 0, s>>>(clip, B, T, H, W, A);
+    patchify_kernel<true><<<grid, 256, 0, s>>>(clip, B, T, H, W, A, ids, K);
   else
-    patchify_kernel<false><<<grid, 256, 0, s>>>(clip, B, T, H, W, A);
+    patchify_kernel<false><<<grid, 256, 0, s>>>(clip, B, T, H, W, A, ids, K);
   return hipGetLastError();
 }
 

@@ -544,8 +544,8 @@ static hipError_t gemm_qkv_dispatch(const uint16_t* A, const uint16_t* W, const 
 
 hipError_t launch_gemm_bf16_qkv(const uint16_t* A, const uint16_t* W, const float* bias,
                                 uint16_t* C, uint16_t* vt, int Ns, int M, int D, int K,
-                                int head_dim, const int32_t* ids, int N, const RopeSpec& r,
-                                const void* tab, float qscale, hipStream_t s) {
+                                int head_dim, const int32_t* ids, int ids_stride, int N,
+                                const RopeSpec& r, const void* tab, float qscale, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const int Ncol = 3 * D;
   if (!gemm_shape_ok(M, Ncol, K) || (head_dim != 64 && head_dim != 32) || D % head_dim ||
@@ -553,7 +553,8 @@ hipError_t launch_gemm_bf16_qkv(const uint16_t* A, const uint16_t* W, const floa
     return hipErrorInvalidValue;
   QkvEpi qe;
   qe.vt = vt;
-  qe.ra = RopeArgs{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw};
+  qe.ra = RopeArgs{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw,
+                   ids_stride};
   qe.D = D;
   qe.H = D / head_dim;
   qe.Ns = Ns;

@@ -36,8 +36,8 @@ hipError_t launch_rope_table(void* tab, const RopeSpec& r, int head_dim, hipStre
 // transposed: q, k into C [M, 3D] (columns [0, 2D)), v into vt [B][H][hd][Ns].
 hipError_t launch_gemm_bf16_qkv(const uint16_t* A, const uint16_t* W, const float* bias,
                                 uint16_t* C, uint16_t* vt, int Ns, int M, int D, int K,
-                                int head_dim, const int32_t* ids, int N, const RopeSpec& r,
-                                const void* tab, float qscale, hipStream_t s);
+                                int head_dim, const int32_t* ids, int ids_stride, int N,
+                                const RopeSpec& r, const void* tab, float qscale, hipStream_t s);
 // The same preparation from a projection already in memory: qkv [M, 3D] bf16 ->
 // q', k' into qk [M, 2D] and v into vt [B][H][hd][Ns].
 hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, int Ns, int B,
@@ -55,12 +55,14 @@ inline int vt_stride(int N) { return (N + 15) / 16 * 16; }
 inline float attn_qscale(int head_dim) {
   return static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(head_dim)));
 }
+// ids: grid ids of clip b at ids + b * ids_stride (NULL: 0..N-1).
 hipError_t launch_attention_f32(const float* qkv, float* out, int B, int N, int n_head,
-                                int head_dim, const int32_t* ids, const RopeSpec& r,
-                                hipStream_t s);
-// uint8 [B,T,H,W,3] -> normalised patch rows [B*N, 1536] (bf16 or fp32).
+                                int head_dim, const int32_t* ids, int ids_stride,
+                                const RopeSpec& r, hipStream_t s);
+// uint8 [B,T,H,W,3] -> normalised patch rows (bf16 or fp32): all B*N tokens ([B*N, 1536],
+// ids NULL), or the K tokens ids[b*K + k] of each clip ([B*K, 1536], ids clamped to [0, N)).
 hipError_t launch_patchify(const uint8_t* clip, int B, int T, int H, int W, void* A, int bf16,
-                           hipStream_t s);
+                           hipStream_t s, const int32_t* ids = nullptr, int K = 0);
 // dst[i, :] = src[clamp(ids[i]), :] (fp32 -> bf16 or fp32), i < n.
 hipError_t launch_gather_rows(const float* src, int n_src, int D, const int32_t* ids, int n,
                               void* dst, int bf16, hipStream_t s);

@@ -24,13 +24,14 @@ struct RopeArgs {
   int N;                // tokens per clip: row r is token r % N of clip r / N
   int layout;           // 0 tiled, 1 interleaved
   int ntot, gh, gw;     // grid size gt*gh*gw and its last two sides
+  int ids_stride;       // ids of clip b start at ids + b * ids_stride (0: shared by all)
 };
 
 // Grid coordinates of the token of row r.
 __device__ __forceinline__ Thw rope_token(int r, const RopeArgs& ra, int* clip) {
   const int b = r / ra.N, n = r - b * ra.N;
   *clip = b;
-  int id = ra.ids ? ra.ids[n] : n;
+  int id = ra.ids ? ra.ids[b * ra.ids_stride + n] : n;
   id = min(max(id, 0), ra.ntot - 1);
   return decode_id(id, ra.gh, ra.gw);
 }
