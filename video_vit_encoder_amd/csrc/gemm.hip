@@ -118,6 +118,10 @@ using Cfg256x192 = GemmCfg<256, 192, 2, 4, 2>;
 using Cfg256x128 = GemmCfg<256, 128, 3, 4, 2>;
 // 256 x 128 with a 2-buffer ring: leaves LDS for the RoPE table of the QKV epilogue
 using Cfg256x128q = GemmCfg<256, 128, 2, 4, 2>;
+// 128 x 128 (waves of 64 x 32): for outputs whose 256-row tiling leaves CUs idle (few
+// token rows, as in the masked forward, or narrow outputs such as N = 384)
+using Cfg128x128 = GemmCfg<128, 128, 4, 2, 4>;
+using Cfg128x128q = GemmCfg<128, 128, 3, 2, 4>;
 
 template <class C, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(C::NT)
@@ -517,6 +521,12 @@ static int tile_width(int M, int N) {
   return 128;
 }
 
+// Whether 256 x 128 tiles would be fewer than the CUs: then 128-row tiles are used.  The
+// tile shape does not change the order in which an output element sums over K.
+static bool short_rows(int M, int N) {
+  return static_cast<long long>((M + 255) / 256) * (N / 128) < num_cus();
+}
+
 static bool gemm_shape_ok(int M, int N, int K) {
   // N in whole 128-column tiles, K in whole slabs; the DMA addressing uses 32-bit byte
   // offsets
@@ -528,6 +538,7 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* b
                             int M, int N, int K, int epi, int out_f32, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (!gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
+  if (short_rows(M, N)) return gemm_dispatch<Cfg128x128>(A, W, bias, C, M, N, K, epi, out_f32, s);
   const int tw = tile_width(M, N);
   if (tw == 256) return gemm_dispatch<Cfg256x256>(A, W, bias, C, M, N, K, epi, out_f32, s);
   if (tw == 192) return gemm_dispatch<Cfg256x192>(A, W, bias, C, M, N, K, epi, out_f32, s);
@@ -561,6 +572,7 @@ hipError_t launch_gemm_bf16_qkv(const uint16_t* A, const uint16_t* W, const floa
   qe.ts = max(r.gt, max(r.gh, r.gw));
   qe.qscale = qscale;
   if (qe.ts > kMaxGridSide) return hipErrorInvalidValue;
+  if (short_rows(M, Ncol)) return gemm_qkv_dispatch<Cfg128x128q>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
   // the 256 x 256 tile leaves too few registers for the RoPE epilogue
   const int tw = tile_width(M, Ncol);
   if (tw == 192) return gemm_qkv_dispatch<Cfg256x192>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
