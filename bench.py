@@ -1,6 +1,6 @@
 """Throughput of the V-JEPA 2 ViT-L/16 encoder forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--masked]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--masked | --predictor]
 
 One step is one jepa_encode call on a batch of 4 synthetic clips of 16 frames x 256x256
 uint8 (2048 tokens per clip, 8192 token rows), already resident in HBM: patch
@@ -23,6 +23,11 @@ on the stream the library launches on, bracketed by device synchronisation).  Be
 pre-training path): the same clips, each with the context of a seeded tube mask (an 8x8
 block of patches in every temporal slot, 512 of the 2048 tokens); ``value`` is context
 tokens/s and the oracle baseline runs oracle.masked_encoder_forward.
+
+``--predictor`` measures the V-JEPA 2 masked predictor (jepa_predict) on its workload: an
+8192-token ViT-L token map (N(0,1) rows standing in for the encoder output), the seeded tube
+mask's 2048 context and 6144 target ids, 12 blocks at width 384 (head dim 32); ``value`` is
+target tokens/s.
 """
 from __future__ import annotations
 
@@ -164,6 +169,112 @@ def cpu_baseline(w, W, clips, budget_layers=12, ids0=None):
                        f"scaled to 24 blocks = {t_clip:.1f} s/clip")}
 
 
+def predictor_work(n_ctx, n_tgt, Denc, E, F, L, Dout):
+    """Algorithmic work per predictor forward by kernel class (as kernel_work)."""
+    M = n_ctx + n_tgt
+    ln_bytes = 2 * L * (M * E * (4 + 2) + 2 * E * 4) + (n_tgt * E * (4 + 2) + 2 * E * 4)
+    return {
+        "gemm_embed": ("mfma", 2 * n_ctx * Denc * E + 2 * n_tgt * E * Dout),   # embed + output proj
+        "layernorm": ("hbm", ln_bytes),
+        "gemm_qkv": ("mfma", L * 2 * M * E * 3 * E),
+        "attention": ("mfma", L * 4 * M * M * E),
+        "gemm_out": ("mfma", L * 2 * M * E * E),
+        "gemm_up": ("mfma", L * 2 * M * E * F),
+        "gemm_down": ("mfma", L * 2 * M * F * E),
+    }
+
+
+def bench_predictor(args):
+    import torch
+    import synth
+    import video_vit_encoder_amd as J
+
+    w = synth.workload("vitl16_64f256_pred")
+    p, grid = w["pred"], w["grid"]
+    N = grid[0] * grid[1] * grid[2]
+    log(f"predictor workload: {N} encoder tokens, width {p.embed_dim}, {p.n_layer} blocks; drawing weights")
+    Wp = synth.predictor_weights(p, seed=args.seed, dtype="bf16")
+    ids_ctx, ids_tgt = synth.tube_mask(args.seed, *grid)
+    z = synth.tokens_normal(5, 1, N, p.enc_dim)[0]
+    dev = torch.device("cuda:0")
+    pred = J.Predictor(p.enc_dim, p.embed_dim, p.n_layer, p.n_head, p.ffn_dim, p.n_mask_tokens,
+                       p.out_dim, dtype="bf16", max_rows=N)
+    pred.set_weights(Wp)
+    z_d = torch.from_numpy(z).to(dev)
+    ic = torch.from_numpy(ids_ctx.astype(np.int32)).to(dev)
+    it = torch.from_numpy(ids_tgt.astype(np.int32)).to(dev)
+    out = torch.empty((len(ids_tgt), p.out_dim), dtype=torch.float32, device=dev)
+
+    def step():
+        pred.predict(z_d, ic, it, w["mask_index"], grid, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("non-finite predictor output")
+    n_ctx, n_tgt = len(ids_ctx), len(ids_tgt)
+    work = predictor_work(n_ctx, n_tgt, p.enc_dim, p.embed_dim, p.ffn_dim, p.n_layer, p.out_dim)
+    flops = sum(v for b, v in work.values() if b == "mfma")
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{ms:.3f} ms/forward, {n_tgt / (ms * 1e-3):,.0f} target tokens/s, {tflops:.1f} TFLOP/s")
+    roof, kernels = None, None
+    if not args.no_kernels:
+        kernels, _ = kernel_timing(J, step, args.steps, work)
+        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+        k = kernels[dom]
+        roof = {"kernel": dom, "bound": k["bound"], "achieved": k.get("tflops", k.get("gbs")),
+                "peak": PEAK_BF16_TFLOPS if k["bound"] == "mfma" else PEAK_HBM_GBS,
+                "unit": "TFLOP/s" if k["bound"] == "mfma" else "GB/s", "frac": k["frac"],
+                "traffic": None, "launch_ms": k["avg_ms"]}
+        log(f"dominant kernel {dom}: {k['avg_ms'] * 1e3:.1f} us/launch, frac {k['frac']:.3f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline (oracle predictor, 0 and 1 blocks, scaled to 12)")
+
+        def spec(n):
+            return oracle.PredictorSpec(p.enc_dim, p.embed_dim, n, p.n_head, p.ffn_dim,
+                                        p.n_mask_tokens, p.out_dim)
+        t0 = time.perf_counter()
+        oracle.predictor_forward(z, Wp, spec(0), ids_ctx, ids_tgt, w["mask_index"], grid)
+        t_fixed = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.predictor_forward(z, Wp, spec(1), ids_ctx, ids_tgt, w["mask_index"], grid)
+        t_layer = max(time.perf_counter() - t0 - t_fixed, 1e-9)
+        t_fwd = t_fixed + p.n_layer * t_layer
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([q.get("num_threads", 1) for q in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        cpu = {"value": n_tgt / t_fwd, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+               "sample": (f"float64 numpy oracle predictor, embedding+norm+projection {t_fixed:.2f} s, "
+                          f"1 block {t_layer:.2f} s; scaled to {p.n_layer} blocks = {t_fwd:.1f} s")}
+    res = {
+        "metric": "predictor target tokens/sec at 1 GPU (V-JEPA 2 ViT-L predictor, 2048 context + "
+                  "6144 targets); % bf16 MFMA peak",
+        "value": round(n_tgt / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) encoder tokens, random N(0,0.02) bf16 weights, seeded tube mask)",
+        "config": {"workload": "V-JEPA 2 ViT-L masked predictor on a 32x16x16 grid (8192 tokens): "
+                               "2048 context + 6144 target rows, width 384, 12 heads of 32, 12 blocks, bf16 MFMA",
+                   "context_tokens": n_ctx, "target_tokens": n_tgt, "embed_dim": p.embed_dim,
+                   "layers": p.n_layer, "heads": p.n_head, "ffn_dim": p.ffn_dim},
+        "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": flops, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +283,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--predictor", action="store_true",
+                    help="time the masked predictor (jepa_predict) on its 8192-token workload")
     ap.add_argument("--masked", action="store_true",
                     help="time the masked-encoder forward on tube-mask contexts (512 of 2048 "
                          "tokens per clip) instead of the full forward")
@@ -183,6 +296,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.predictor:
+        bench_predictor(args)
+        return
 
     import torch
     import synth
