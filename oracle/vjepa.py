@@ -19,7 +19,8 @@ __all__ = [
     "normalize_frames", "patchify", "id_to_thw", "rope_positions", "rope_axis_dim",
     "rope_omegas", "rope_angle_index", "rope_angles", "rope_rotate", "rope_rotate_with_angles",
     "layer_norm", "gelu_erf", "linear", "attention", "block", "encoder_forward",
-    "encode_tokens", "encoder_forward_batch", "masked_encoder_forward", "predictor_forward",
+    "encode_tokens", "encoder_forward_batch", "encoder_forward_image", "masked_encoder_forward",
+    "predictor_forward",
 ]
 
 # [Notes §1 "pre.mean / std / rescale": ImageNet, 1/255]; values as given on [HFport
@@ -64,6 +65,8 @@ class PredictorSpec:
     layout: str = "tiled"
     ln_eps: float = 1e-6
     theta: float = 10000.0
+    has_mod_embed: bool = False      # V-JEPA 2.1: a modality vector on every row
+    has_proj_context: bool = False   # V-JEPA 2.1: projection of the context rows
 
     @property
     def head_dim(self) -> int:
@@ -346,6 +349,25 @@ def masked_encoder_forward(clip: np.ndarray, W: Dict[str, np.ndarray], spec: Enc
     return encode_tokens(x[ids], W, spec, ids, grid)
 
 
+def encoder_forward_image(img: np.ndarray, W: Dict[str, np.ndarray], spec: EncoderSpec) -> np.ndarray:
+    """V-JEPA 2.1 native image path, one uint8 image [H, W, 3] -> [N, D] float64
+    ([Notes §3] "2.1 encoder forward", image line; [Notes §2] patch_embed_img with
+    tubelet 1; [Notes §5]: fed as one frame).
+
+    tokens = patchify(x, 1, 16) Wpe_img^T + bpe_img (+ mod_embed_img), features in C, T, H, W
+    order with T = 1; then the blocks with 3-D RoPE on the grid (1, H/16, W/16) and the
+    final norm, as for a clip.
+    """
+    X = normalize_frames(img[None])
+    p = patchify(X, 1, spec.patch)
+    Wd = _f64(W)
+    x = linear(p, Wd["enc.patch_embed_img.weight"], Wd["enc.patch_embed_img.bias"])
+    if spec.has_mod_embed:
+        x = x + Wd["enc.mod_embed_img"]
+    grid = (1, img.shape[0] // spec.patch, img.shape[1] // spec.patch)
+    return encode_tokens(x, W, spec, np.arange(grid[1] * grid[2]), grid)
+
+
 def encoder_forward_batch(clips: np.ndarray, W, spec: EncoderSpec) -> np.ndarray:
     """[B, T, H, W, 3] -> [B, N, D]; each clip is encoded on its own."""
     return np.stack([encoder_forward(c, W, spec) for c in clips])
@@ -354,7 +376,8 @@ def encoder_forward_batch(clips: np.ndarray, W, spec: EncoderSpec) -> np.ndarray
 def predictor_forward(z: np.ndarray, W: Dict[str, np.ndarray], spec: PredictorSpec,
                       ids_ctx: np.ndarray, ids_tgt: np.ndarray, mask_index: int,
                       grid: Tuple[int, int, int],
-                      last_rows: Optional[np.ndarray] = None) -> np.ndarray:
+                      last_rows: Optional[np.ndarray] = None, modality: str = "video",
+                      return_context: bool = False):
     """Masked predictor: encoder token map z [N, D_enc] -> predictions [len(ids_tgt), out].
 
     ctx = z[ids_ctx] Wemb^T + b; every target row is mask_tokens[mask_index mod n];
@@ -365,6 +388,11 @@ def predictor_forward(z: np.ndarray, W: Dict[str, np.ndarray], spec: PredictorSp
     are not sorted by id: attention is permutation-equivariant ([Notes §3]).
     ``last_rows`` (indices into the targets) restricts the last block, the norm and the
     projection to those target rows.
+
+    V-JEPA 2.1 ([Notes §3] "2.1 predictor forward"): with ``spec.has_mod_embed`` every row
+    (context and mask tokens) takes ``pred.mod_embed_{modality}`` after the concatenation;
+    with ``return_context`` the normed context rows are projected by ``pred.proj_context``
+    and (predictions, context output) is returned.
     """
     W = _f64(W)
     ids_ctx = np.asarray(ids_ctx, dtype=np.int64)
@@ -373,6 +401,10 @@ def predictor_forward(z: np.ndarray, W: Dict[str, np.ndarray], spec: PredictorSp
     tok = W["pred.mask_tokens"][mask_index % spec.n_mask_tokens]
     tgt = np.broadcast_to(tok, (len(ids_tgt), spec.embed_dim))
     x = np.concatenate([ctx, tgt], axis=0)
+    if spec.has_mod_embed:
+        x = x + W[f"pred.mod_embed_{modality}"]
+    if return_context:
+        assert spec.has_proj_context and last_rows is None
     _, gh, gw = grid
     pos = rope_positions(np.concatenate([ids_ctx, ids_tgt]), gh, gw, 0)
     n_ctx = len(ids_ctx)
@@ -382,6 +414,10 @@ def predictor_forward(z: np.ndarray, W: Dict[str, np.ndarray], spec: PredictorSp
         rows = tgt_rows if (i == L - 1 and last_rows is not None) else None
         x = block(x, W, f"pred.blk.{i}", spec.n_head, pos, spec.layout, spec.theta, spec.ln_eps,
                   rows=rows)
+    if return_context:
+        x = layer_norm(x, W["pred.norm.weight"], W["pred.norm.bias"], spec.ln_eps)
+        return (linear(x[n_ctx:], W["pred.proj.weight"], W["pred.proj.bias"]),
+                linear(x[:n_ctx], W["pred.proj_context.weight"], W["pred.proj_context.bias"]))
     if not (L > 0 and last_rows is not None):
         x = x[tgt_rows]
     x = layer_norm(x, W["pred.norm.weight"], W["pred.norm.bias"], spec.ln_eps)

@@ -57,6 +57,7 @@ class EncoderShape:
     in_chans: int = 3
     has_mod_embed: bool = False
     final_norm: bool = True
+    has_image_embed: bool = False   # V-JEPA 2.1 image path: patch_embed_img (+ mod_embed_img)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -68,6 +69,8 @@ class PredictorShape:
     ffn_dim: int
     n_mask_tokens: int
     out_dim: int
+    has_mod_embed: bool = False      # V-JEPA 2.1: pred.mod_embed_video / _img
+    has_proj_context: bool = False   # V-JEPA 2.1: pred.proj_context
 
 
 def _block_tensors(prefix: str, d: int, f: int) -> List[Tuple[str, Tuple[int, ...], str]]:
@@ -98,6 +101,12 @@ def encoder_tensor_list(s: EncoderShape) -> List[Tuple[str, Tuple[int, ...], str
         out += _block_tensors(f"enc.blk.{i}", s.embed_dim, s.ffn_dim)
     if s.final_norm:
         out += [("enc.norm.weight", (s.embed_dim,), "lnw"), ("enc.norm.bias", (s.embed_dim,), "lnb")]
+    # appended last, so the tensors above keep their streams
+    if s.has_image_embed:
+        out += [("enc.patch_embed_img.weight", (s.embed_dim, s.in_chans * s.patch * s.patch), "w"),
+                ("enc.patch_embed_img.bias", (s.embed_dim,), "b")]
+        if s.has_mod_embed:
+            out.append(("enc.mod_embed_img", (s.embed_dim,), "tok"))
     return out
 
 
@@ -110,6 +119,12 @@ def predictor_tensor_list(s: PredictorShape) -> List[Tuple[str, Tuple[int, ...],
     out += [("pred.norm.weight", (s.embed_dim,), "lnw"), ("pred.norm.bias", (s.embed_dim,), "lnb"),
             ("pred.proj.weight", (s.out_dim, s.embed_dim), "w"),
             ("pred.proj.bias", (s.out_dim,), "b")]
+    # appended last, so the tensors above keep their streams
+    if s.has_mod_embed:
+        out += [("pred.mod_embed_video", (s.embed_dim,), "tok"), ("pred.mod_embed_img", (s.embed_dim,), "tok")]
+    if s.has_proj_context:
+        out += [("pred.proj_context.weight", (s.out_dim, s.embed_dim), "w"),
+                ("pred.proj_context.bias", (s.out_dim,), "b")]
     return out
 
 

@@ -151,7 +151,9 @@ def encoder(clip, Wnp: Dict, n_layer, n_head, layout, ref_grid=0, mod_embed=Fals
 
 
 def predictor(z, Wnp: Dict, ids_ctx, ids_tgt, mask_index, grid, n_layer, n_head, n_mask,
-              layout="tiled", theta=10000.0, eps=1e-6):
+              layout="tiled", theta=10000.0, eps=1e-6, mod=None, context=False):
+    """mod: name of a modality vector added to every row after the concatenation;
+    context: also return the context rows projected by pred.proj_context."""
     W = {k: to_list(v) for k, v in Wnp.items()}
     z = to_list(z)
     ids_ctx = [int(i) for i in ids_ctx]
@@ -159,9 +161,14 @@ def predictor(z, Wnp: Dict, ids_ctx, ids_tgt, mask_index, grid, n_layer, n_head,
     ctx = matvec_rows([z[i] for i in ids_ctx], W["pred.embed.weight"], W["pred.embed.bias"])
     tok = W["pred.mask_tokens"][mask_index % n_mask]
     x = ctx + [list(tok) for _ in ids_tgt]
+    if mod is not None:
+        x = [[r[i] + W[mod][i] for i in range(len(r))] for r in x]
     _, gh, gw = grid
     pos = [positions(i, gh, gw, 0) for i in ids_ctx + ids_tgt]
     for li in range(n_layer):
         x = block(x, W, f"pred.blk.{li}", n_head, pos, layout, theta, eps)
     x = layer_norm_rows(x, W["pred.norm.weight"], W["pred.norm.bias"], eps)
-    return matvec_rows(x[len(ids_ctx):], W["pred.proj.weight"], W["pred.proj.bias"])
+    pred = matvec_rows(x[len(ids_ctx):], W["pred.proj.weight"], W["pred.proj.bias"])
+    if not context:
+        return pred
+    return pred, matvec_rows(x[:len(ids_ctx)], W["pred.proj_context.weight"], W["pred.proj_context.bias"])
