@@ -53,6 +53,11 @@ enum jepa_status {
  * V-JEPA 2.1). */
 enum jepa_rope_layout { JEPA_ROPE_TILED = 0, JEPA_ROPE_INTERLEAVED = 1 };
 
+/* Modality vector of the V-JEPA 2.1 predictor ([Notes §3] "2.1 predictor forward"):
+ * pred.mod_embed_video or pred.mod_embed_img; AUTO takes the image one when the grid has
+ * a single temporal slot (gt = 1). */
+enum jepa_modality { JEPA_MODALITY_VIDEO = 0, JEPA_MODALITY_IMAGE = 1, JEPA_MODALITY_AUTO = 2 };
+
 /* Element types.  JEPA_F32 also selects the fp32 compute path (plain fp32 FMA
  * kernels); JEPA_BF16 selects bf16 MFMA operands with fp32 accumulation. */
 enum jepa_dtype { JEPA_F32 = 0, JEPA_BF16 = 1 };
@@ -93,6 +98,9 @@ typedef struct jepa_encoder_config {
   int32_t max_rows;       /* largest B*N a call may use (sizes the workspace)    */
   float ln_eps;           /* 1e-6                                                */
   float rope_theta;       /* 10000                                               */
+  int32_t has_image_embed; /* 1: the V-JEPA 2.1 image path (jepa_encode_image) with
+                              enc.patch_embed_img (+ enc.mod_embed_img when
+                              has_mod_embed) ([Notes §2] key map, [Notes §3])    */
 } jepa_encoder_config;
 
 typedef struct jepa_encoder jepa_encoder;
@@ -112,7 +120,9 @@ void jepa_encoder_free(jepa_encoder* enc);
  *   enc.blk.{i}.ln1.weight/bias [D], enc.blk.{i}.attn_qkv.weight [3D, D] (rows q; k; v),
  *   enc.blk.{i}.attn_qkv.bias [3D], enc.blk.{i}.attn_out.weight [D, D] / .bias [D],
  *   enc.blk.{i}.ln2.weight/bias [D], enc.blk.{i}.ffn_up.weight [F, D] / .bias [F],
- *   enc.blk.{i}.ffn_down.weight [D, F] / .bias [D], enc.norm.weight/bias [D].
+ *   enc.blk.{i}.ffn_down.weight [D, F] / .bias [D], enc.norm.weight/bias [D];
+ *   with has_image_embed: enc.patch_embed_img.weight [D, 768] / .bias [D] and, when
+ *   has_mod_embed, enc.mod_embed_img [D].
  * `host` holds numel(shape) values of src_dtype (JEPA_F32 floats or JEPA_BF16 bit
  * patterns), row-major.  Matrices are stored on the device in the compute dtype
  * (fp32 -> bf16 by round-to-nearest-even); vectors stay fp32.  Synchronous.
@@ -162,6 +172,18 @@ int jepa_encode_tokens(jepa_encoder* enc, const float* x_dev, int B, int N,
 int jepa_encode_masked(jepa_encoder* enc, const uint8_t* clip_dev, int B, int T, int H, int W,
                        const int32_t* ids_dev, int K, float* out_dev, void* stream);
 
+/* V-JEPA 2.1 native image path ([Notes §3] "2.1 encoder forward", image line; [Notes §2]
+ * patch_embed_img with tubelet 1): each image is one frame, patchified into 1x16x16x3
+ * patches (features in C, T, H, W order with T = 1, 768 of them) and embedded with
+ * enc.patch_embed_img [D, 768] / .bias (+ enc.mod_embed_img when has_mod_embed), then the
+ * blocks and the final norm on the grid (1, H/16, W/16).
+ *   img_dev: uint8 [B, H, W, 3]; out_dev: fp32 [B, N, D], N = (H/16)(W/16), row-major.
+ * Needs has_image_embed.  Errors: JEPA_ERR_ARG (null pointer, no image path);
+ * JEPA_ERR_SHAPE (H or W not a multiple of 16, a grid side above 64, interpolation with a
+ * side of 1, B*N > max_rows); JEPA_ERR_STATE (a tensor never set). */
+int jepa_encode_image(jepa_encoder* enc, const uint8_t* img_dev, int B, int H, int W,
+                      float* out_dev, void* stream);
+
 /* ------------------------------------------------------------------ predictor */
 
 /* V-JEPA 2 masked predictor ([Notes §1]: 384 / 12 / 12 / 1536, 10 mask tokens, output
@@ -179,6 +201,9 @@ typedef struct jepa_predictor_config {
   int32_t max_rows;       /* largest n_ctx + n_tgt */
   float ln_eps;
   float rope_theta;
+  int32_t has_mod_embed;  /* 1: V-JEPA 2.1 modality vectors pred.mod_embed_video/_img [E]
+                             added to every row ([Notes §3] "2.1 predictor forward") */
+  int32_t has_proj_context; /* 1: pred.proj_context [Dout, E] projects the context rows */
 } jepa_predictor_config;
 
 typedef struct jepa_predictor jepa_predictor;
@@ -188,7 +213,9 @@ void jepa_predictor_free(jepa_predictor* pred);
 
 /* Names ([Notes §2]): pred.embed.weight [E, Denc] / .bias [E], pred.mask_tokens [n, E],
  * pred.blk.{i}.* as the encoder blocks at width E, pred.norm.weight/bias [E],
- * pred.proj.weight [Dout, E] / .bias [Dout].  Same rules as jepa_encoder_set_tensor. */
+ * pred.proj.weight [Dout, E] / .bias [Dout]; with has_mod_embed pred.mod_embed_video and
+ * pred.mod_embed_img [E]; with has_proj_context pred.proj_context.weight [Dout, E] /
+ * .bias [Dout].  Same rules as jepa_encoder_set_tensor. */
 int jepa_predictor_set_tensor(jepa_predictor* pred, const char* name, const void* host,
                               int src_dtype, const int64_t* shape, int ndim);
 
@@ -205,6 +232,19 @@ int jepa_predictor_set_tensor(jepa_predictor* pred, const char* name, const void
 int jepa_predict(jepa_predictor* pred, const float* z_dev, int n_enc,
                  const int32_t* ids_ctx_dev, int n_ctx, const int32_t* ids_tgt_dev, int n_tgt,
                  int mask_index, int gt, int gh, int gw, float* out_dev, void* stream);
+
+/* jepa_predict with the V-JEPA 2.1 options ([Notes §3] "2.1 predictor forward"):
+ *   modality: jepa_modality, which of pred.mod_embed_video / _img is added to every row
+ *             after the concatenation (ignored without has_mod_embed; jepa_predict
+ *             uses the video one);
+ *   ctx_out_dev: NULL, or fp32 [n_ctx, Dout] = pred.proj_context of the normed context
+ *             rows (needs has_proj_context).
+ * Errors as jepa_predict, plus JEPA_ERR_ARG for a bad modality or ctx_out_dev without
+ * has_proj_context. */
+int jepa_predict_mod(jepa_predictor* pred, const float* z_dev, int n_enc,
+                     const int32_t* ids_ctx_dev, int n_ctx, const int32_t* ids_tgt_dev, int n_tgt,
+                     int mask_index, int modality, int gt, int gh, int gw, float* out_dev,
+                     float* ctx_out_dev, void* stream);
 
 /* ------------------------------------------------------------------ stand-alone ops */
 

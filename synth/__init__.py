@@ -231,6 +231,15 @@ WORKLOADS = {
         enc=EncoderShape(1024, 24, 16, 4096), layout="tiled", ref_grid=0, dtype="bf16",
         B=1, frames=64, size=256, grid=(32, 16, 16),
         pred=PredictorShape(1024, 384, 12, 12, 1536, 10, 1024), mask_index=1),
+    "vitb16_img384": dict(
+        desc="V-JEPA 2.1 ViT-B/16 native image path, 1 image 384x384 (576 tokens), bf16",
+        enc=EncoderShape(768, 12, 12, 3072, has_mod_embed=True, has_image_embed=True),
+        layout="interleaved", ref_grid=16, dtype="bf16", B=1, frames=1, size=384, grid=(1, 24, 24)),
+    "vitb16_pred21": dict(
+        desc="V-JEPA 2.1 ViT-B predictor (384 / 12 / 12 / 1536, 8 mask tokens, out 1664, "
+             "modality vectors, context projection) on the grid of 384 px (24 x 24 per slot), bf16",
+        pred=PredictorShape(768, 384, 12, 12, 1536, 8, 1664, has_mod_embed=True, has_proj_context=True),
+        layout="interleaved", dtype="bf16", mask_index=1, grid_video=(8, 24, 24), grid_image=(1, 24, 24)),
 }
 
 

@@ -41,14 +41,15 @@ class jepa_encoder_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "embed_dim", "n_layer", "n_head", "ffn_dim", "patch", "tubelet", "in_chans",
         "rope_layout", "rope_ref_grid", "has_mod_embed", "final_norm", "compute", "max_rows")] + [
-        ("ln_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+        ("ln_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("has_image_embed", ctypes.c_int32)]
 
 
 class jepa_predictor_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "enc_dim", "embed_dim", "n_layer", "n_head", "ffn_dim", "n_mask_tokens", "out_dim",
         "rope_layout", "compute", "max_rows")] + [
-        ("ln_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+        ("ln_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+        ("has_mod_embed", ctypes.c_int32), ("has_proj_context", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -65,10 +66,12 @@ _SIGS = {
     "jepa_encode": ([_P, _P, _I, _I, _I, _I, _P, _P], _I),
     "jepa_encode_tokens": ([_P, _P, _I, _I, _P, _I, _I, _I, _P, _P], _I),
     "jepa_encode_masked": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
+    "jepa_encode_image": ([_P, _P, _I, _I, _I, _P, _P], _I),
     "jepa_predictor_create": ([ctypes.POINTER(jepa_predictor_config), ctypes.POINTER(_P)], _I),
     "jepa_predictor_free": ([_P], None),
     "jepa_predictor_set_tensor": ([_P, ctypes.c_char_p, _P, _I, ctypes.POINTER(_I64), _I], _I),
     "jepa_predict": ([_P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P], _I),
+    "jepa_predict_mod": ([_P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "jepa_rope3d": ([_P, _P, _I, _I, _I, _I, _I, _I64, _P, _I, _I, _I, _I, _F, _I, _P], _I),
     "jepa_layernorm": ([_P, _P, _P, _I, _I, _F, _P, _I, _P], _I),
     "jepa_linear": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
@@ -235,6 +238,17 @@ def jepa_encode_masked(handle: int, clip, ids, out, stream=None) -> None:
                                                            _ptr(out), _stream(stream)))
 
 
+def jepa_encode_image(handle: int, img, out, stream=None) -> None:
+    """img: uint8 device tensor [B, H, W, 3]; out: fp32 device tensor [B, N, D]."""
+    B, H, W, C = img.shape
+    _need(C == 3 and img.dtype == _torch().uint8, "img must be uint8 [B, H, W, 3]")
+    N = (H // 16) * (W // 16)
+    _need(out.dtype == _torch().float32 and out.numel() == B * N * _enc_dim(handle),
+          "out must be fp32 [B, N, D]")
+    _check("jepa_encode_image", load().jepa_encode_image(handle, _ptr(img), B, H, W, _ptr(out),
+                                                         _stream(stream)))
+
+
 def jepa_predictor_create(cfg: jepa_predictor_config) -> int:
     h = _P()
     _check("jepa_predictor_create",
@@ -269,6 +283,31 @@ def jepa_predict(handle: int, z, ids_ctx, ids_tgt, mask_index: int, grid: Sequen
            load().jepa_predict(handle, _ptr(z), z.shape[0], _ptr(ids_ctx), ids_ctx.numel(),
                                _ptr(ids_tgt), ids_tgt.numel(), mask_index, gt, gh, gw, _ptr(out),
                                _stream(stream)))
+
+
+MODALITIES = {"video": 0, "image": 1, "auto": 2}
+
+
+def jepa_predict_mod(handle: int, z, ids_ctx, ids_tgt, mask_index: int, modality: str,
+                     grid: Sequence[int], out, ctx_out=None, stream=None) -> None:
+    """jepa_predict with the 2.1 modality vector ('video', 'image' or 'auto') and, when
+    ctx_out (fp32 [n_ctx, Dout]) is given, the context projection."""
+    c = _PRED_CFG[handle]
+    _need(z.dim() == 2 and z.shape[1] == c.enc_dim and z.dtype == _torch().float32,
+          "z must be fp32 [n_enc, enc_dim]")
+    for t in (ids_ctx, ids_tgt):
+        _need(t.dtype == _torch().int32, "ids must be int32")
+    _need(out.dtype == _torch().float32 and out.numel() == ids_tgt.numel() * c.out_dim,
+          "out must be fp32 [n_tgt, out_dim]")
+    _need(ctx_out is None or (ctx_out.dtype == _torch().float32 and
+                              ctx_out.numel() == ids_ctx.numel() * c.out_dim),
+          "ctx_out must be fp32 [n_ctx, out_dim]")
+    _need(modality in MODALITIES, "modality must be 'video', 'image' or 'auto'")
+    gt, gh, gw = grid
+    _check("jepa_predict_mod",
+           load().jepa_predict_mod(handle, _ptr(z), z.shape[0], _ptr(ids_ctx), ids_ctx.numel(),
+                                   _ptr(ids_tgt), ids_tgt.numel(), mask_index, MODALITIES[modality],
+                                   gt, gh, gw, _ptr(out), _ptr(ctx_out), _stream(stream)))
 
 
 def jepa_rope3d(x, y, B: int, N: int, n_head: int, head_dim: int, row_stride: int, ids,

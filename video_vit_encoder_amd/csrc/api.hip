@@ -375,7 +375,9 @@ struct jepa_encoder {
   TensorSet ts;
   std::vector<BlockIdx> blocks;
   int pe_w = -1, pe_b = -1, mod = -1, norm_w = -1, norm_b = -1;
-  DevBuf pe_bias_eff;  // bpe + mod_embed_video (when has_mod_embed), fp32 [D]
+  int img_w = -1, img_b = -1, img_mod = -1;   // 2.1 image path (has_image_embed)
+  DevBuf pe_bias_eff;   // bpe + mod_embed_video (when has_mod_embed), fp32 [D]
+  DevBuf img_bias_eff;  // bpe_img + mod_embed_img (when has_mod_embed), fp32 [D]
   bool pe_bias_dirty = true;
   Workspace ws;
 };
@@ -405,6 +407,7 @@ int jepa_encoder_create(const jepa_encoder_config* cfg, jepa_encoder** out) {
   const int hd = c.embed_dim / c.n_head;
   JEPA_TRY(check_widths(c.compute, c.embed_dim, c.ffn_dim, c.n_head, hd));
   if (c.n_layer < 0 || c.patch != 16 || c.tubelet != 2 || c.in_chans != 3) return JEPA_ERR_ARG;
+  if ((c.has_image_embed | c.has_mod_embed | c.final_norm) & ~1) return JEPA_ERR_ARG;
   if (c.rope_layout != JEPA_ROPE_TILED && c.rope_layout != JEPA_ROPE_INTERLEAVED) return JEPA_ERR_ARG;
   if (c.rope_ref_grid < 0 || c.rope_ref_grid == 1) return JEPA_ERR_ARG;
   if (c.max_rows <= 0) return JEPA_ERR_ARG;
@@ -425,8 +428,14 @@ int jepa_encoder_create(const jepa_encoder_config* cfg, jepa_encoder** out) {
     e->norm_w = e->ts.add("enc.norm.weight", {D}, false);
     e->norm_b = e->ts.add("enc.norm.bias", {D}, false);
   }
+  if (c.has_image_embed) {
+    e->img_w = e->ts.add("enc.patch_embed_img.weight", {D, feat / c.tubelet}, true);
+    e->img_b = e->ts.add("enc.patch_embed_img.bias", {D}, false, true);
+    if (c.has_mod_embed) e->img_mod = e->ts.add("enc.mod_embed_img", {D}, false, true);
+  }
   int st = e->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, static_cast<int>(feat), c.compute);
   if (st == JEPA_OK) st = dev_alloc(e->pe_bias_eff, static_cast<size_t>(D) * 4);
+  if (st == JEPA_OK && c.has_image_embed) st = dev_alloc(e->img_bias_eff, static_cast<size_t>(D) * 4);
   if (st != JEPA_OK) {
     delete e;
     return st;
@@ -438,6 +447,7 @@ int jepa_encoder_create(const jepa_encoder_config* cfg, jepa_encoder** out) {
 void jepa_encoder_free(jepa_encoder* enc) {
   if (!enc) return;
   dev_free(enc->pe_bias_eff);
+  dev_free(enc->img_bias_eff);
   delete enc;
 }
 
@@ -449,17 +459,23 @@ int jepa_encoder_set_tensor(jepa_encoder* enc, const char* name, const void* hos
   return st;
 }
 
-// Folds mod_embed_video into the patch-embedding bias on the host (fp32 sum of the two
+// Folds the modality vector into a patch-embedding bias on the host (fp32 sum of the two
 // fp32 vectors, the same value the GPU would form).
-static int refresh_pe_bias(jepa_encoder* e) {
-  if (!e->pe_bias_dirty) return JEPA_OK;
-  const Tensor& b = e->ts.t[e->pe_b];
+static int fold_bias(const TensorSet& ts, int bias, int mod, DevBuf& dst) {
+  const Tensor& b = ts.t[bias];
   std::vector<float> v(b.host);
-  if (e->mod >= 0) {
-    const Tensor& m = e->ts.t[e->mod];
+  if (mod >= 0) {
+    const Tensor& m = ts.t[mod];
     for (size_t i = 0; i < v.size(); ++i) v[i] = v[i] + m.host[i];
   }
-  JEPA_HIP(hipMemcpy(e->pe_bias_eff.p, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+  JEPA_HIP(hipMemcpy(dst.p, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+  return JEPA_OK;
+}
+
+static int refresh_pe_bias(jepa_encoder* e) {
+  if (!e->pe_bias_dirty) return JEPA_OK;
+  JEPA_TRY(fold_bias(e->ts, e->pe_b, e->mod, e->pe_bias_eff));
+  if (e->img_b >= 0) JEPA_TRY(fold_bias(e->ts, e->img_b, e->img_mod, e->img_bias_eff));
   e->pe_bias_dirty = false;
   return JEPA_OK;
 }
@@ -521,6 +537,38 @@ int jepa_encode_tokens(jepa_encoder* enc, const float* x_dev, int B, int N,
   return JEPA_OK;
 }
 
+int jepa_encode_image(jepa_encoder* enc, const uint8_t* img_dev, int B, int H, int W,
+                      float* out_dev, void* stream) {
+  if (!enc || !img_dev || !out_dev || !enc->cfg.has_image_embed) return JEPA_ERR_ARG;
+  const jepa_encoder_config& c = enc->cfg;
+  if (B < 1 || H < 16 || W < 16 || H % 16 || W % 16) return JEPA_ERR_SHAPE;
+  const int gh = H / 16, gw = W / 16;
+  JEPA_TRY(check_grid(1, gh, gw, c.rope_ref_grid));
+  const long long N = static_cast<long long>(gh) * gw;
+  if (static_cast<long long>(B) * N > c.max_rows) return JEPA_ERR_SHAPE;
+  if (!enc->ts.all_set()) return JEPA_ERR_STATE;
+  JEPA_TRY(refresh_pe_bias(enc));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int M = static_cast<int>(B * N);
+  const int D = c.embed_dim, bf = c.compute == JEPA_BF16 ? 1 : 0;
+  const int feat = c.in_chans * c.patch * c.patch;
+  // [Notes §3] "2.1 encoder forward", image line: tubelet-1 patches, the image embedding
+  // and modality vector, then the blocks on the one-slot grid.
+  JEPA_LAUNCH(JEPA_KC_PATCHIFY, s, launch_patchify_image(img_dev, B, H, W, enc->ws.a.p, bf, s));
+  JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
+              linear(c.compute, enc->ws.a.p, enc->ts.dev(enc->img_w),
+                     static_cast<const float*>(enc->img_bias_eff.p), out_dev, M, D, feat,
+                     JEPA_EPI_STORE, 1, s));
+  const RopeSpec rs{1, gh, gw, c.rope_layout, c.rope_theta, c.rope_ref_grid};
+  JEPA_TRY(run_blocks(enc->ts, enc->blocks, c.n_layer, enc->ws, out_dev, B, static_cast<int>(N), D,
+                      c.ffn_dim, c.n_head, c.ln_eps, nullptr, 0, rs, s));
+  if (c.final_norm)
+    JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
+                launch_layernorm(out_dev, enc->ts.devf(enc->norm_w), enc->ts.devf(enc->norm_b), M,
+                                 D, c.ln_eps, out_dev, 0, s));
+  return JEPA_OK;
+}
+
 int jepa_encode_masked(jepa_encoder* enc, const uint8_t* clip_dev, int B, int T, int H, int W,
                        const int32_t* ids_dev, int K, float* out_dev, void* stream) {
   if (!enc || !clip_dev || !ids_dev || !out_dev) return JEPA_ERR_ARG;
@@ -565,9 +613,13 @@ struct jepa_predictor {
   TensorSet ts;
   std::vector<BlockIdx> blocks;
   int emb_w = -1, emb_b = -1, mask = -1, norm_w = -1, norm_b = -1, proj_w = -1, proj_b = -1;
+  int mod_v = -1, mod_i = -1, pctx_w = -1, pctx_b = -1;   // V-JEPA 2.1 options
   Workspace ws;
-  DevBuf x;     // fp32 [max_rows, E] residual stream
-  DevBuf ids;   // int32 [max_rows] concat(ids_ctx, ids_tgt)
+  DevBuf x;          // fp32 [max_rows, E] residual stream
+  DevBuf ids;        // int32 [max_rows] concat(ids_ctx, ids_tgt)
+  DevBuf emb_bias;   // fp32 [2, E]: bemb + mod_embed_video, bemb + mod_embed_img
+  DevBuf mask_row;   // fp32 [E]: the mask token plus the modality vector
+  bool bias_dirty = true;
 };
 
 extern "C" {
@@ -585,6 +637,7 @@ int jepa_predictor_create(const jepa_predictor_config* cfg, jepa_predictor** out
   if (c.rope_layout != JEPA_ROPE_TILED && c.rope_layout != JEPA_ROPE_INTERLEAVED) return JEPA_ERR_ARG;
   if (c.max_rows <= 0) return JEPA_ERR_ARG;
   if (!(c.ln_eps > 0.f) || !(c.rope_theta > 1.f)) return JEPA_ERR_ARG;
+  if ((c.has_mod_embed | c.has_proj_context) & ~1) return JEPA_ERR_ARG;
 
   jepa_predictor* p = new (std::nothrow) jepa_predictor();
   if (!p) return JEPA_ERR_OOM;
@@ -592,7 +645,7 @@ int jepa_predictor_create(const jepa_predictor_config* cfg, jepa_predictor** out
   p->ts.compute = c.compute;
   const int64_t E = c.embed_dim, F = c.ffn_dim;
   p->emb_w = p->ts.add("pred.embed.weight", {E, c.enc_dim}, true);
-  p->emb_b = p->ts.add("pred.embed.bias", {E}, false);
+  p->emb_b = p->ts.add("pred.embed.bias", {E}, false, true);
   p->mask = p->ts.add("pred.mask_tokens", {c.n_mask_tokens, E}, false);
   for (int i = 0; i < c.n_layer; ++i)
     p->blocks.push_back(add_block(p->ts, "pred.blk." + std::to_string(i), E, F));
@@ -600,12 +653,24 @@ int jepa_predictor_create(const jepa_predictor_config* cfg, jepa_predictor** out
   p->norm_b = p->ts.add("pred.norm.bias", {E}, false);
   p->proj_w = p->ts.add("pred.proj.weight", {c.out_dim, E}, true);
   p->proj_b = p->ts.add("pred.proj.bias", {c.out_dim}, false);
+  if (c.has_mod_embed) {
+    p->mod_v = p->ts.add("pred.mod_embed_video", {E}, false, true);
+    p->mod_i = p->ts.add("pred.mod_embed_img", {E}, false, true);
+  }
+  if (c.has_proj_context) {
+    p->pctx_w = p->ts.add("pred.proj_context.weight", {c.out_dim, E}, true);
+    p->pctx_b = p->ts.add("pred.proj_context.bias", {c.out_dim}, false);
+  }
   int st = p->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, c.enc_dim, c.compute);
   if (st == JEPA_OK) st = dev_alloc(p->x, static_cast<size_t>(c.max_rows) * E * 4);
   if (st == JEPA_OK) st = dev_alloc(p->ids, static_cast<size_t>(c.max_rows) * 4);
+  if (st == JEPA_OK) st = dev_alloc(p->emb_bias, static_cast<size_t>(2) * E * 4);
+  if (st == JEPA_OK) st = dev_alloc(p->mask_row, static_cast<size_t>(E) * 4);
   if (st != JEPA_OK) {
     dev_free(p->x);
     dev_free(p->ids);
+    dev_free(p->emb_bias);
+    dev_free(p->mask_row);
     delete p;
     return st;
   }
@@ -617,20 +682,36 @@ void jepa_predictor_free(jepa_predictor* pred) {
   if (!pred) return;
   dev_free(pred->x);
   dev_free(pred->ids);
+  dev_free(pred->emb_bias);
+  dev_free(pred->mask_row);
   delete pred;
 }
 
 int jepa_predictor_set_tensor(jepa_predictor* pred, const char* name, const void* host,
                               int src_dtype, const int64_t* shape, int ndim) {
   if (!pred) return JEPA_ERR_ARG;
-  return pred->ts.set_tensor(name, host, src_dtype, shape, ndim);
+  const int st = pred->ts.set_tensor(name, host, src_dtype, shape, ndim);
+  if (st == JEPA_OK) pred->bias_dirty = true;
+  return st;
 }
 
 int jepa_predict(jepa_predictor* pred, const float* z_dev, int n_enc,
                  const int32_t* ids_ctx_dev, int n_ctx, const int32_t* ids_tgt_dev, int n_tgt,
                  int mask_index, int gt, int gh, int gw, float* out_dev, void* stream) {
+  return jepa_predict_mod(pred, z_dev, n_enc, ids_ctx_dev, n_ctx, ids_tgt_dev, n_tgt, mask_index,
+                          JEPA_MODALITY_VIDEO, gt, gh, gw, out_dev, nullptr, stream);
+}
+
+int jepa_predict_mod(jepa_predictor* pred, const float* z_dev, int n_enc,
+                     const int32_t* ids_ctx_dev, int n_ctx, const int32_t* ids_tgt_dev, int n_tgt,
+                     int mask_index, int modality, int gt, int gh, int gw, float* out_dev,
+                     float* ctx_out_dev, void* stream) {
   if (!pred || !z_dev || !ids_ctx_dev || !ids_tgt_dev || !out_dev) return JEPA_ERR_ARG;
+  if (modality != JEPA_MODALITY_VIDEO && modality != JEPA_MODALITY_IMAGE &&
+      modality != JEPA_MODALITY_AUTO)
+    return JEPA_ERR_ARG;
   const jepa_predictor_config& c = pred->cfg;
+  if (ctx_out_dev && !c.has_proj_context) return JEPA_ERR_ARG;
   if (n_ctx < 1 || n_tgt < 1 || n_enc < 1) return JEPA_ERR_SHAPE;
   if (static_cast<long long>(n_ctx) + n_tgt > c.max_rows) return JEPA_ERR_SHAPE;
   JEPA_TRY(check_grid(gt, gh, gw, 0));
@@ -641,18 +722,38 @@ int jepa_predict(jepa_predictor* pred, const float* z_dev, int n_enc,
   const int M = n_ctx + n_tgt;
   float* x = static_cast<float*>(pred->x.p);
   int32_t* ids = static_cast<int32_t*>(pred->ids.p);
+  // V-JEPA 2.1: the modality vector goes onto every row.  On the context rows it is folded
+  // into the embedding bias (host fp32 sums, refreshed after set_tensor), on the mask rows
+  // it is added to the mask token before the fill.
+  const bool mod = c.has_mod_embed != 0;
+  const bool img = mod && (modality == JEPA_MODALITY_IMAGE || (modality == JEPA_MODALITY_AUTO && gt == 1));
+  if (mod && pred->bias_dirty) {
+    DevBuf v{pred->emb_bias.p, static_cast<size_t>(E) * 4};
+    DevBuf i{static_cast<float*>(pred->emb_bias.p) + E, static_cast<size_t>(E) * 4};
+    JEPA_TRY(fold_bias(pred->ts, pred->emb_b, pred->mod_v, v));
+    JEPA_TRY(fold_bias(pred->ts, pred->emb_b, pred->mod_i, i));
+    pred->bias_dirty = false;
+  }
+  const float* emb_bias = mod ? static_cast<const float*>(pred->emb_bias.p) + (img ? E : 0)
+                              : pred->ts.devf(pred->emb_b);
   // [Notes §3] "2.1 predictor forward": embed the context rows, mask tokens at the
   // targets, concatenate; positions from the concatenated ids ([Notes §4.4]).
   JEPA_LAUNCH(JEPA_KC_OTHER, s,
               launch_gather_rows(z_dev, n_enc, c.enc_dim, ids_ctx_dev, n_ctx, pred->ws.a.p, bf, s));
   JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
-              linear(c.compute, pred->ws.a.p, pred->ts.dev(pred->emb_w), pred->ts.devf(pred->emb_b),
+              linear(c.compute, pred->ws.a.p, pred->ts.dev(pred->emb_w), emb_bias,
                      x, n_ctx, E, c.enc_dim, JEPA_EPI_STORE, 1, s));
   int mi = mask_index % c.n_mask_tokens;
   if (mi < 0) mi += c.n_mask_tokens;
+  const float* mask_row = pred->ts.devf(pred->mask) + static_cast<size_t>(mi) * E;
+  if (mod) {
+    JEPA_LAUNCH(JEPA_KC_OTHER, s,
+                launch_add_vec(static_cast<float*>(pred->mask_row.p), mask_row,
+                               pred->ts.devf(img ? pred->mod_i : pred->mod_v), E, s));
+    mask_row = static_cast<const float*>(pred->mask_row.p);
+  }
   JEPA_LAUNCH(JEPA_KC_OTHER, s,
-              launch_fill_rows(x + static_cast<size_t>(n_ctx) * E,
-                               pred->ts.devf(pred->mask) + static_cast<size_t>(mi) * E, n_tgt, E, s));
+              launch_fill_rows(x + static_cast<size_t>(n_ctx) * E, mask_row, n_tgt, E, s));
   JEPA_LAUNCH(JEPA_KC_OTHER, s,
               hipMemcpyAsync(ids, ids_ctx_dev, static_cast<size_t>(n_ctx) * 4,
                              hipMemcpyDeviceToDevice, s));
@@ -662,15 +763,22 @@ int jepa_predict(jepa_predictor* pred, const float* z_dev, int n_enc,
   const RopeSpec rs{gt, gh, gw, c.rope_layout, c.rope_theta, 0};
   JEPA_TRY(run_blocks(pred->ts, pred->blocks, c.n_layer, pred->ws, x, 1, M, E, c.ffn_dim,
                       c.n_head, c.ln_eps, ids, 0, rs, s));
-  // final norm and output projection on the target rows only
-  float* xt = x + static_cast<size_t>(n_ctx) * E;
+  // final norm and output projection: of the target rows only, or of all rows when the
+  // context rows also go through pred.proj_context
+  const size_t es = bf ? 2 : 4;
+  const int first = ctx_out_dev ? 0 : n_ctx;
   JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
-              launch_layernorm(xt, pred->ts.devf(pred->norm_w), pred->ts.devf(pred->norm_b), n_tgt,
-                               E, c.ln_eps, pred->ws.h.p, bf, s));
+              launch_layernorm(x + static_cast<size_t>(first) * E, pred->ts.devf(pred->norm_w),
+                               pred->ts.devf(pred->norm_b), M - first, E, c.ln_eps, pred->ws.h.p, bf, s));
+  const unsigned char* ht = static_cast<const unsigned char*>(pred->ws.h.p) +
+                            static_cast<size_t>(n_ctx - first) * E * es;
   JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
-              linear(c.compute, pred->ws.h.p, pred->ts.dev(pred->proj_w),
-                     pred->ts.devf(pred->proj_b), out_dev, n_tgt, c.out_dim, E, JEPA_EPI_STORE, 1,
-                     s));
+              linear(c.compute, ht, pred->ts.dev(pred->proj_w), pred->ts.devf(pred->proj_b), out_dev,
+                     n_tgt, c.out_dim, E, JEPA_EPI_STORE, 1, s));
+  if (ctx_out_dev)
+    JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
+                linear(c.compute, pred->ws.h.p, pred->ts.dev(pred->pctx_w), pred->ts.devf(pred->pctx_b),
+                       ctx_out_dev, n_ctx, c.out_dim, E, JEPA_EPI_STORE, 1, s));
   return JEPA_OK;
 }
 

@@ -5,31 +5,32 @@
 
 namespace jepa {
 
-// Patch rows ([Notes §2]: feature order C, T, H, W of the 2x16x16x3 tubelet;
-// [Notes §4]: tokens T-major).  Pixels are normalised in the fused float32 form
-// (px - 255*mean)/(255*std) with the ImageNet statistics ([Parity "Preprocessing
-// parity"]).  One thread per (token, dt, dy): it reads the 16 pixels x 3 channels of one
-// image row segment (48 contiguous bytes of THWC input) and writes the three 16-wide
-// feature runs c*512 + dt*256 + dy*16 + [0, 16).  With ids, output row b*K + k is the
-// tubelet of token ids[b*K + k] of clip b (the context tokens of the masked forward,
-// [HFport "Usage"]); ids outside [0, N) are clamped.
-template <bool BF16>
+// Patch rows ([Notes §2]: feature order C, T, H, W of the TUBx16x16x3 tubelet, TUB = 2
+// for clips and 1 for the 2.1 image path; [Notes §4]: tokens T-major).  Pixels are
+// normalised in the fused float32 form (px - 255*mean)/(255*std) with the ImageNet
+// statistics ([Parity "Preprocessing parity"]).  One thread per (token, dt, dy): it reads
+// the 16 pixels x 3 channels of one image row segment (48 contiguous bytes of THWC input)
+// and writes the three 16-wide feature runs c*TUB*256 + dt*256 + dy*16 + [0, 16).  With
+// ids, output row b*K + k is the tubelet of token ids[b*K + k] of clip b (the context
+// tokens of the masked forward, [HFport "Usage"]); ids outside [0, N) are clamped.
+template <bool BF16, int TUB>
 __global__ __launch_bounds__(256)
 void patchify_kernel(const uint8_t* __restrict__ clip, int B, int T, int H, int W,
                      void* __restrict__ out, const int32_t* __restrict__ ids, int K) {
-  const int gt = T / 2, gh = H / 16, gw = W / 16;
+  constexpr int FEAT = 3 * TUB * 256, TPT = TUB * 16;   // features, threads per token
+  const int gt = T / TUB, gh = H / 16, gw = W / 16;
   const int per_clip = gt * gh * gw;
   const int rows = ids ? K : per_clip;   // output rows per clip
   const long long ntok = static_cast<long long>(B) * rows;
   const long long gid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= ntok * 32) return;
-  const long long tokg = gid >> 5;
-  const int sub = static_cast<int>(gid & 31), dt = sub >> 4, dy = sub & 15;
+  if (gid >= ntok * TPT) return;
+  const long long tokg = gid / TPT;
+  const int sub = static_cast<int>(gid - tokg * TPT), dt = sub >> 4, dy = sub & 15;
   const int b = static_cast<int>(tokg / rows);
   int n = static_cast<int>(tokg - static_cast<long long>(b) * rows);
   if (ids) n = min(max(ids[tokg], 0), per_clip - 1);
   const int tp = n / (gh * gw), rem = n - tp * gh * gw, hp = rem / gw, wp = rem - hp * gw;
-  const int t = 2 * tp + dt, y = 16 * hp + dy, x0 = 16 * wp;
+  const int t = TUB * tp + dt, y = 16 * hp + dy, x0 = 16 * wp;
   const uint32_t* src = reinterpret_cast<const uint32_t*>(
       clip + ((((static_cast<long long>(b) * T + t) * H + y) * W + x0) * 3));
   uint32_t raw[12];
@@ -48,7 +49,7 @@ void patchify_kernel(const uint8_t* __restrict__ clip, int B, int T, int H, int 
       const float px = static_cast<float>((raw[byte >> 2] >> (8 * (byte & 3))) & 0xFF);
       v[dx] = (px - mu255[c]) / sd255[c];
     }
-    const long long o = tokg * 1536 + c * 512 + dt * 256 + dy * 16;
+    const long long o = tokg * FEAT + c * (TUB * 256) + dt * 256 + dy * 16;
     if constexpr (BF16) {
       u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + o);
 #pragma unroll
@@ -73,9 +74,21 @@ hipError_t launch_patchify(const uint8_t* clip, int B, int T, int H, int W, void
   if (threads <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
   if (bf16)
-    patchify_kernel<true><<<grid, 256, 0, s>>>(clip, B, T, H, W, A, ids, K);
+    patchify_kernel<true, 2><<<grid, 256, 0, s>>>(clip, B, T, H, W, A, ids, K);
   else
-    patchify_kernel<false><<<grid, 256, 0, s>>>(clip, B, T, H, W, A, ids, K);
+    patchify_kernel<false, 2><<<grid, 256, 0, s>>>(clip, B, T, H, W, A, ids, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_patchify_image(const uint8_t* img, int B, int H, int W, void* A, int bf16,
+                                 hipStream_t s) {
+  const long long threads = static_cast<long long>(B) * (H / 16) * (W / 16) * 16;
+  if (threads <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (bf16)
+    patchify_kernel<true, 1><<<grid, 256, 0, s>>>(img, B, 1, H, W, A, nullptr, 0);
+  else
+    patchify_kernel<false, 1><<<grid, 256, 0, s>>>(img, B, 1, H, W, A, nullptr, 0);
   return hipGetLastError();
 }
 

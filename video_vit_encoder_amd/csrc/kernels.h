@@ -63,6 +63,9 @@ hipError_t launch_attention_f32(const float* qkv, float* out, int B, int N, int 
 // ids NULL), or the K tokens ids[b*K + k] of each clip ([B*K, 1536], ids clamped to [0, N)).
 hipError_t launch_patchify(const uint8_t* clip, int B, int T, int H, int W, void* A, int bf16,
                            hipStream_t s, const int32_t* ids = nullptr, int K = 0);
+// uint8 images [B,H,W,3] -> normalised 1x16x16x3 patch rows [B*N, 768] (2.1 image path).
+hipError_t launch_patchify_image(const uint8_t* img, int B, int H, int W, void* A, int bf16,
+                                 hipStream_t s);
 // dst[i, :] = src[clamp(ids[i]), :] (fp32 -> bf16 or fp32), i < n.
 hipError_t launch_gather_rows(const float* src, int n_src, int D, const int32_t* ids, int n,
                               void* dst, int bf16, hipStream_t s);
