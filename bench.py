@@ -1,6 +1,7 @@
 """Throughput of the V-JEPA 2 ViT-L/16 encoder forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--masked | --predictor]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--masked | --image | --predictor [--v21]]
 
 One step is one jepa_encode call on a batch of 4 synthetic clips of 16 frames x 256x256
 uint8 (2048 tokens per clip, 8192 token rows), already resident in HBM: patch
@@ -27,7 +28,13 @@ tokens/s and the oracle baseline runs oracle.masked_encoder_forward.
 ``--predictor`` measures the V-JEPA 2 masked predictor (jepa_predict) on its workload: an
 8192-token ViT-L token map (N(0,1) rows standing in for the encoder output), the seeded tube
 mask's 2048 context and 6144 target ids, 12 blocks at width 384 (head dim 32); ``value`` is
-target tokens/s.
+target tokens/s.  ``--predictor --v21`` runs the V-JEPA 2.1 ViT-B predictor instead (768 -> 384,
+8 mask tokens, output 1664, interleaved RoPE, modality vector on every row, context rows
+projected too) on the 8x24x24 grid of a 16-frame 384-px clip with the tube mask's 512
+context and 4096 target ids.
+
+``--image`` measures the V-JEPA 2.1 ViT-B/16 native image path (jepa_encode_image) on 16
+uniform uint8 images of 384x384 (576 tokens each, 12 layers); ``value`` is image tokens/s.
 """
 from __future__ import annotations
 
@@ -189,8 +196,10 @@ def bench_predictor(args):
     import synth
     import video_vit_encoder_amd as J
 
-    w = synth.workload("vitl16_64f256_pred")
-    p, grid = w["pred"], w["grid"]
+    v21 = args.v21
+    w = synth.workload("vitb16_pred21" if v21 else "vitl16_64f256_pred")
+    p = w["pred"]
+    grid = w["grid_video"] if v21 else w["grid"]
     N = grid[0] * grid[1] * grid[2]
     log(f"predictor workload: {N} encoder tokens, width {p.embed_dim}, {p.n_layer} blocks; drawing weights")
     Wp = synth.predictor_weights(p, seed=args.seed, dtype="bf16")
@@ -198,15 +207,21 @@ def bench_predictor(args):
     z = synth.tokens_normal(5, 1, N, p.enc_dim)[0]
     dev = torch.device("cuda:0")
     pred = J.Predictor(p.enc_dim, p.embed_dim, p.n_layer, p.n_head, p.ffn_dim, p.n_mask_tokens,
-                       p.out_dim, dtype="bf16", max_rows=N)
+                       p.out_dim, dtype="bf16", max_rows=len(ids_ctx) + len(ids_tgt),
+                       layout=w.get("layout", "tiled"), has_mod_embed=p.has_mod_embed,
+                       has_proj_context=p.has_proj_context)
     pred.set_weights(Wp)
     z_d = torch.from_numpy(z).to(dev)
     ic = torch.from_numpy(ids_ctx.astype(np.int32)).to(dev)
     it = torch.from_numpy(ids_tgt.astype(np.int32)).to(dev)
     out = torch.empty((len(ids_tgt), p.out_dim), dtype=torch.float32, device=dev)
+    ctx = torch.empty((len(ids_ctx), p.out_dim), dtype=torch.float32, device=dev)
 
     def step():
-        pred.predict(z_d, ic, it, w["mask_index"], grid, out=out)
+        if v21:
+            J.jepa_predict_mod(pred.handle, z_d, ic, it, w["mask_index"], "video", grid, out, ctx)
+        else:
+            pred.predict(z_d, ic, it, w["mask_index"], grid, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -222,6 +237,9 @@ def bench_predictor(args):
         raise RuntimeError("non-finite predictor output")
     n_ctx, n_tgt = len(ids_ctx), len(ids_tgt)
     work = predictor_work(n_ctx, n_tgt, p.enc_dim, p.embed_dim, p.ffn_dim, p.n_layer, p.out_dim)
+    if v21:   # the context rows are normed and projected as well
+        b, f = work["gemm_embed"]
+        work["gemm_embed"] = (b, f + 2 * n_ctx * p.embed_dim * p.out_dim)
     flops = sum(v for b, v in work.values() if b == "mfma")
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{ms:.3f} ms/forward, {n_tgt / (ms * 1e-3):,.0f} target tokens/s, {tflops:.1f} TFLOP/s")
@@ -242,12 +260,17 @@ def bench_predictor(args):
 
         def spec(n):
             return oracle.PredictorSpec(p.enc_dim, p.embed_dim, n, p.n_head, p.ffn_dim,
-                                        p.n_mask_tokens, p.out_dim)
+                                        p.n_mask_tokens, p.out_dim, layout=w.get("layout", "tiled"),
+                                        has_mod_embed=p.has_mod_embed, has_proj_context=p.has_proj_context)
+
+        def run(n):
+            return oracle.predictor_forward(z, Wp, spec(n), ids_ctx, ids_tgt, w["mask_index"], grid,
+                                            return_context=v21)
         t0 = time.perf_counter()
-        oracle.predictor_forward(z, Wp, spec(0), ids_ctx, ids_tgt, w["mask_index"], grid)
+        run(0)
         t_fixed = time.perf_counter() - t0
         t0 = time.perf_counter()
-        oracle.predictor_forward(z, Wp, spec(1), ids_ctx, ids_tgt, w["mask_index"], grid)
+        run(1)
         t_layer = max(time.perf_counter() - t0 - t_fixed, 1e-9)
         t_fwd = t_fixed + p.n_layer * t_layer
         try:
@@ -258,17 +281,116 @@ def bench_predictor(args):
         cpu = {"value": n_tgt / t_fwd, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
                "sample": (f"float64 numpy oracle predictor, embedding+norm+projection {t_fixed:.2f} s, "
                           f"1 block {t_layer:.2f} s; scaled to {p.n_layer} blocks = {t_fwd:.1f} s")}
+    metric = ("predictor target tokens/sec at 1 GPU (V-JEPA 2 ViT-L predictor, 2048 context + "
+              "6144 targets); % bf16 MFMA peak")
+    wl = ("V-JEPA 2 ViT-L masked predictor on a 32x16x16 grid (8192 tokens): 2048 context + 6144 "
+          "target rows, width 384, 12 heads of 32, 12 blocks, bf16 MFMA")
+    if v21:
+        metric = ("predictor target tokens/sec at 1 GPU (V-JEPA 2.1 ViT-B predictor, 512 context + "
+                  "4096 targets on 8x24x24); % bf16 MFMA peak")
+        wl = ("V-JEPA 2.1 ViT-B predictor on the 8x24x24 grid of a 16-frame 384-px clip: 512 context + "
+              "4096 target rows, width 384, 12 heads of 32, 12 blocks, interleaved RoPE, video modality "
+              "vector, targets and context projected to 1664, bf16 MFMA")
     res = {
-        "metric": "predictor target tokens/sec at 1 GPU (V-JEPA 2 ViT-L predictor, 2048 context + "
-                  "6144 targets); % bf16 MFMA peak",
+        "metric": metric,
         "value": round(n_tgt / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (N(0,1) encoder tokens, random N(0,0.02) bf16 weights, seeded tube mask)",
-        "config": {"workload": "V-JEPA 2 ViT-L masked predictor on a 32x16x16 grid (8192 tokens): "
-                               "2048 context + 6144 target rows, width 384, 12 heads of 32, 12 blocks, bf16 MFMA",
+        "config": {"workload": wl,
                    "context_tokens": n_ctx, "target_tokens": n_tgt, "embed_dim": p.embed_dim,
                    "layers": p.n_layer, "heads": p.n_head, "ffn_dim": p.ffn_dim},
+        "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": flops, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_image(args, B=16):
+    import torch
+    import synth
+    import video_vit_encoder_amd as J
+
+    w = synth.workload("vitb16_img384")
+    e = w["enc"]
+    S = w["size"]
+    N = w["grid"][1] * w["grid"][2]
+    D, F, L, H = e.embed_dim, e.ffn_dim, e.n_layer, e.n_head
+    log(f"image workload: {B} images {S}x{S}, N={N}, D={D}, L={L}; drawing weights")
+    W = synth.encoder_weights(e, seed=args.seed, dtype="bf16")
+    imgs = synth.clip_u8(args.seed, B, 1, S, S)[:, 0]
+    dev = torch.device("cuda:0")
+    enc = J.Encoder(D, L, H, F, layout=w["layout"], ref_grid=w["ref_grid"], has_mod_embed=True,
+                    dtype="bf16", max_rows=B * N, has_image_embed=True)
+    enc.set_weights(W)
+    img_d = torch.from_numpy(imgs).to(dev)
+    out = torch.empty((B, N, D), dtype=torch.float32, device=dev)
+
+    def step():
+        enc.encode_image(img_d, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("non-finite encoder output")
+    feat = 768
+    flops = forward_flops(B, N, D, F, L, feat=feat)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{ms:.3f} ms/step, {B * N / (ms * 1e-3):,.0f} tokens/s, {tflops:.1f} TFLOP/s")
+    roof, kernels = None, None
+    if not args.no_kernels:
+        work = kernel_work(B, N, D, F, L, feat=feat)
+        kernels, _ = kernel_timing(J, step, args.steps, work)
+        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+        k = kernels[dom]
+        roof = {"kernel": dom, "bound": k["bound"], "achieved": k.get("tflops", k.get("gbs")),
+                "peak": PEAK_BF16_TFLOPS if k["bound"] == "mfma" else PEAK_HBM_GBS,
+                "unit": "TFLOP/s" if k["bound"] == "mfma" else "GB/s", "frac": k["frac"],
+                "traffic": None, "launch_ms": k["avg_ms"]}
+        log(f"dominant kernel {dom}: {k['avg_ms'] * 1e3:.1f} us/launch, frac {k['frac']:.3f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline (oracle image path, 0 and 2 blocks, scaled to 12)")
+
+        def spec(n):
+            return oracle.EncoderSpec(D, n, H, F, has_mod_embed=True, layout=w["layout"],
+                                      ref_grid=w["ref_grid"])
+        t0 = time.perf_counter()
+        oracle.encoder_forward_image(imgs[0], W, spec(0))
+        t_fixed = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.encoder_forward_image(imgs[0], W, spec(2))
+        t_layer = max(time.perf_counter() - t0 - t_fixed, 1e-9) / 2
+        t_img = t_fixed + L * t_layer
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([q.get("num_threads", 1) for q in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        cpu = {"value": N / t_img, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+               "sample": (f"float64 numpy oracle image path, image 0 ({N} tokens): embedding+norm "
+                          f"{t_fixed:.2f} s, 2 blocks {2 * t_layer:.2f} s; scaled to {L} blocks = {t_img:.1f} s")}
+    res = {
+        "metric": "image tokens/sec at 1 GPU (V-JEPA 2.1 ViT-B/16 image path, 384px); % bf16 MFMA peak",
+        "value": round(B * N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (uniform uint8 images, random N(0,0.02) bf16 weights)",
+        "config": {"workload": f"V-JEPA 2.1 ViT-B/16 native image path, {B} images x 384x384 (576 tokens "
+                               "each), tubelet-1 patches, image modality vector, interleaved RoPE "
+                               "interpolated to 16, 12 layers, bf16 MFMA",
+                   "batch_images": B, "tokens_per_image": N, "embed_dim": D, "layers": L, "heads": H,
+                   "ffn_dim": F},
+        "images_per_s": round(B / (ms * 1e-3), 2),
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "flops_per_step": flops, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
     }
@@ -285,6 +407,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--predictor", action="store_true",
                     help="time the masked predictor (jepa_predict) on its 8192-token workload")
+    ap.add_argument("--v21", action="store_true",
+                    help="with --predictor: the V-JEPA 2.1 ViT-B predictor (jepa_predict_mod)")
+    ap.add_argument("--image", action="store_true",
+                    help="time the V-JEPA 2.1 ViT-B/16 image path on 16 images of 384x384")
     ap.add_argument("--masked", action="store_true",
                     help="time the masked-encoder forward on tube-mask contexts (512 of 2048 "
                          "tokens per clip) instead of the full forward")
@@ -299,6 +425,9 @@ def main():
 
     if args.predictor:
         bench_predictor(args)
+        return
+    if args.image:
+        bench_image(args)
         return
 
     import torch
