@@ -20,7 +20,7 @@ __all__ = [
     "rope_omegas", "rope_angle_index", "rope_angles", "rope_rotate", "rope_rotate_with_angles",
     "layer_norm", "gelu_erf", "linear", "attention", "block", "encoder_forward",
     "encode_tokens", "encoder_forward_batch", "encoder_forward_image", "masked_encoder_forward",
-    "predictor_forward",
+    "predictor_forward", "mean_pool", "attentive_pool_head",
 ]
 
 # [Notes §1 "pre.mean / std / rescale": ImageNet, 1/255]; values as given on [HFport
@@ -366,6 +366,45 @@ def encoder_forward_image(img: np.ndarray, W: Dict[str, np.ndarray], spec: Encod
         x = x + Wd["enc.mod_embed_img"]
     grid = (1, img.shape[0] // spec.patch, img.shape[1] // spec.patch)
     return encode_tokens(x, W, spec, np.arange(grid[1] * grid[2]), grid)
+
+
+def mean_pool(x: np.ndarray) -> np.ndarray:
+    """Mean of a token map [N, D] over its tokens -> [D] ([Card] "Run it": ``--pool mean``
+    turns the token map into one pooled feature)."""
+    return np.asarray(x, dtype=np.float64).mean(axis=0)
+
+
+def attentive_pool_head(x: np.ndarray, W: Dict[str, np.ndarray], n_layer: int, n_head: int,
+                        eps: float = 1e-6) -> np.ndarray:
+    """Attentive-pool classifier head on one token map x [N, D] (the encoder output after
+    its final norm) -> logits [n_classes] ([Notes §2] "Attentive-pool head — exact
+    forward" and the head.* rows of its key map).
+
+    ``n_layer`` self-attention blocks head.blk.{i} as the encoder's but without RoPE (every
+    position 0, i.e. no rotation); then one cross-attention: the raw learned query
+    head.query takes q from it, the normed tokens (head.xattn.ln_kv) give k and v through
+    their own projections, softmax(q k^T / sqrt(hd)) v per head with the heads
+    concatenated and no output projection; the raw query is the residual; a GELU MLP
+    after head.xattn.ln2 with its own residual; the linear classifier head.cls, no final
+    norm.
+    """
+    W = _f64(W)
+    x = np.asarray(x, dtype=np.float64)
+    N = x.shape[0]
+    pos0 = np.zeros((N, 3))
+    for i in range(n_layer):
+        x = block(x, W, f"head.blk.{i}", n_head, pos0, "tiled", eps=eps)
+    q0 = W["head.query"]                                                  # [1, D]
+    kv = layer_norm(x, W["head.xattn.ln_kv.weight"], W["head.xattn.ln_kv.bias"], eps)
+    q = linear(q0, W["head.xattn.q.weight"], W["head.xattn.q.bias"])
+    k = linear(kv, W["head.xattn.k.weight"], W["head.xattn.k.bias"])
+    v = linear(kv, W["head.xattn.v.weight"], W["head.xattn.v.bias"])
+    o = attention(q, k, v, n_head, np.zeros((1, 3)), pos0, "tiled")
+    y = q0 + o
+    h = layer_norm(y, W["head.xattn.ln2.weight"], W["head.xattn.ln2.bias"], eps)
+    g = gelu_erf(linear(h, W["head.xattn.ffn_up.weight"], W["head.xattn.ffn_up.bias"]))
+    y = y + linear(g, W["head.xattn.ffn_down.weight"], W["head.xattn.ffn_down.bias"])
+    return linear(y, W["head.cls.weight"], W["head.cls.bias"])[0]
 
 
 def encoder_forward_batch(clips: np.ndarray, W, spec: EncoderSpec) -> np.ndarray:

@@ -73,6 +73,16 @@ class PredictorShape:
     has_proj_context: bool = False   # V-JEPA 2.1: pred.proj_context
 
 
+@dataclasses.dataclass(frozen=True)
+class HeadShape:
+    """Attentive-pool classifier head: width, pool blocks, heads, FFN width, classes."""
+    embed_dim: int
+    n_layer: int
+    n_head: int
+    ffn_dim: int
+    n_classes: int
+
+
 def _block_tensors(prefix: str, d: int, f: int) -> List[Tuple[str, Tuple[int, ...], str]]:
     return [
         (f"{prefix}.ln1.weight", (d,), "lnw"),
@@ -128,6 +138,21 @@ def predictor_tensor_list(s: PredictorShape) -> List[Tuple[str, Tuple[int, ...],
     return out
 
 
+def head_tensor_list(s: HeadShape) -> List[Tuple[str, Tuple[int, ...], str]]:
+    d, f = s.embed_dim, s.ffn_dim
+    out = [("head.query", (1, d), "tok")]
+    for i in range(s.n_layer):
+        out += _block_tensors(f"head.blk.{i}", d, f)
+    out += [("head.xattn.ln_kv.weight", (d,), "lnw"), ("head.xattn.ln_kv.bias", (d,), "lnb")]
+    for p in ("q", "k", "v"):
+        out += [(f"head.xattn.{p}.weight", (d, d), "w"), (f"head.xattn.{p}.bias", (d,), "b")]
+    out += [("head.xattn.ln2.weight", (d,), "lnw"), ("head.xattn.ln2.bias", (d,), "lnb"),
+            ("head.xattn.ffn_up.weight", (f, d), "w"), ("head.xattn.ffn_up.bias", (f,), "b"),
+            ("head.xattn.ffn_down.weight", (d, f), "w"), ("head.xattn.ffn_down.bias", (d,), "b"),
+            ("head.cls.weight", (s.n_classes, d), "w"), ("head.cls.bias", (s.n_classes,), "b")]
+    return out
+
+
 def _draw(kind: str, shape, g: np.random.Generator, ln: str) -> np.ndarray:
     if kind == "w":
         a = g.standard_normal(shape) * 0.02
@@ -159,6 +184,10 @@ def make_weights(tensors, seed: int, dtype: str = "bf16", ln: str = "identity",
 
 def encoder_weights(s: EncoderShape, seed: int = 0, dtype: str = "bf16", ln: str = "identity"):
     return make_weights(encoder_tensor_list(s), seed, dtype, ln, base_index=1000)
+
+
+def head_weights(s: HeadShape, seed: int = 0, dtype: str = "bf16", ln: str = "identity"):
+    return make_weights(head_tensor_list(s), seed, dtype, ln, base_index=9000)
 
 
 def predictor_weights(s: PredictorShape, seed: int = 0, dtype: str = "bf16", ln: str = "identity"):

@@ -172,3 +172,33 @@ def predictor(z, Wnp: Dict, ids_ctx, ids_tgt, mask_index, grid, n_layer, n_head,
     if not context:
         return pred
     return pred, matvec_rows(x[:len(ids_ctx)], W["pred.proj_context.weight"], W["pred.proj_context.bias"])
+
+
+def head(x, Wnp: Dict, n_layer, n_head, eps=1e-6):
+    """Attentive-pool head on one token map x [N][D] -> logits, element by element."""
+    W = {k: to_list(v) for k, v in Wnp.items()}
+    x = to_list(x)
+    N, D = len(x), len(x[0])
+    hd = D // n_head
+    pos = [(0.0, 0.0, 0.0)] * N
+    for li in range(n_layer):
+        x = block(x, W, f"head.blk.{li}", n_head, pos, "tiled", 10000.0, eps)
+    q0 = W["head.query"][0]
+    kv = layer_norm_rows(x, W["head.xattn.ln_kv.weight"], W["head.xattn.ln_kv.bias"], eps)
+    q = matvec_rows([q0], W["head.xattn.q.weight"], W["head.xattn.q.bias"])[0]
+    k = matvec_rows(kv, W["head.xattn.k.weight"], W["head.xattn.k.bias"])
+    v = matvec_rows(kv, W["head.xattn.v.weight"], W["head.xattn.v.bias"])
+    y = list(q0)
+    for e in range(n_head):
+        c0 = e * hd
+        s = [sum(q[c0 + j] * k[n][c0 + j] for j in range(hd)) / math.sqrt(hd) for n in range(N)]
+        mx = max(s)
+        ex = [math.exp(t - mx) for t in s]
+        tot = sum(ex)
+        for j in range(hd):
+            y[c0 + j] += sum(ex[n] * v[n][c0 + j] for n in range(N)) / tot
+    h = layer_norm_rows([y], W["head.xattn.ln2.weight"], W["head.xattn.ln2.bias"], eps)
+    g = [[gelu(z) for z in r] for r in matvec_rows(h, W["head.xattn.ffn_up.weight"], W["head.xattn.ffn_up.bias"])]
+    f = matvec_rows(g, W["head.xattn.ffn_down.weight"], W["head.xattn.ffn_down.bias"])[0]
+    y = [y[i] + f[i] for i in range(D)]
+    return matvec_rows([y], W["head.cls.weight"], W["head.cls.bias"])[0]
