@@ -9,6 +9,8 @@
  *            LeVJEPA)" (aselimc.github.io/jepa.cpp/parity/)
  *   [HFport] "V-JEPA 2.1 ViT-B/16 384 -- HuggingFace port"
  *            (aimarketly.com/model/apiantonio/vjepa2.1-vit-base-384)
+ *   [Card]   jepa.cpp V-JEPA 2 ViT-L/16 GGUF model card
+ *            (graysoft.dev/models/jep/jepacpp-vjepa2-vitl-fpc64-256-gguf.html)
  *
  * Conventions shared by every entry point
  *   - Pointers named *_dev are device memory (HIP), allocated and owned by the caller;
@@ -245,6 +247,52 @@ int jepa_predict_mod(jepa_predictor* pred, const float* z_dev, int n_enc,
                      const int32_t* ids_ctx_dev, int n_ctx, const int32_t* ids_tgt_dev, int n_tgt,
                      int mask_index, int modality, int gt, int gh, int gw, float* out_dev,
                      float* ctx_out_dev, void* stream);
+
+/* ------------------------------------------------------------------ pooled outputs */
+
+/* Mean over the tokens of each clip ([Card] "Run it", --pool mean):
+ *   x_dev fp32 [B, N, D] -> out_dev fp32 [B, D], accumulated in fp64 in a fixed order.
+ * Errors: JEPA_ERR_ARG (null pointer), JEPA_ERR_SHAPE (B < 0, N < 1, D < 1). */
+int jepa_pool_mean(const float* x_dev, int B, int N, int D, float* out_dev, void* stream);
+
+/* Attentive-pool classifier head ([Notes §2] "Attentive-pool head — exact forward"; the
+ * V-JEPA 2 SSv2 classifier: D 1024, 3 pool blocks, 16 heads, FFN 4096, 174 classes). */
+typedef struct jepa_head_config {
+  int32_t embed_dim;      /* D, as the encoder; head_dim = D / n_head must be 64 or 32 */
+  int32_t n_layer;        /* pool blocks (self-attention without RoPE), >= 0          */
+  int32_t n_head;
+  int32_t ffn_dim;
+  int32_t n_classes;      /* >= 1, any width                                          */
+  int32_t compute;        /* jepa_dtype of the blocks and the k / v / MLP projections */
+  int32_t max_rows;       /* largest B*N a call may use                               */
+  float ln_eps;           /* 1e-6                                                     */
+} jepa_head_config;
+
+typedef struct jepa_head jepa_head;
+
+int jepa_head_create(const jepa_head_config* cfg, jepa_head** out);
+void jepa_head_free(jepa_head* head);
+
+/* Names ([Notes §2] key map): head.query [1, D]; head.blk.{i}.* as the encoder blocks;
+ * head.xattn.ln_kv.weight/bias [D]; head.xattn.{q,k,v}.weight [D, D] / .bias [D];
+ * head.xattn.ln2.weight/bias [D]; head.xattn.ffn_up.weight [F, D] / .bias [F];
+ * head.xattn.ffn_down.weight [D, F] / .bias [D]; head.cls.weight [C, D] / .bias [C].
+ * The query projection and the classifier stay fp32 (they see one row per clip); the
+ * other matrices follow the compute dtype.  Same rules as jepa_encoder_set_tensor. */
+int jepa_head_set_tensor(jepa_head* head, const char* name, const void* host, int src_dtype,
+                         const int64_t* shape, int ndim);
+
+/* Logits of B token maps:
+ *   x_dev: fp32 [B, N, D] encoder output after its final norm (not modified);
+ *   logits_dev: fp32 [B, C].
+ * The pool blocks run on each clip's N tokens without RoPE; the learned query (raw, not
+ * normed) attends over the normed tokens with fp32 k and v, heads concatenated, no output
+ * projection; the raw query is the residual; then the MLP with its residual and the
+ * classifier, no final norm.
+ * Errors: JEPA_ERR_ARG (null pointer); JEPA_ERR_SHAPE (B < 1, N < 1, N > 16384,
+ * B*N > max_rows); JEPA_ERR_STATE (a tensor never set). */
+int jepa_head_forward(jepa_head* head, const float* x_dev, int B, int N, float* logits_dev,
+                      void* stream);
 
 /* ------------------------------------------------------------------ stand-alone ops */
 

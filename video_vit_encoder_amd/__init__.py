@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     DTYPES, JEPA_BF16, JEPA_EPI_GELU, JEPA_EPI_RESIDUAL, JEPA_EPI_STORE, JEPA_F32, LAYOUTS,
     KERNEL_CLASSES, JepaError, header_functions, jepa_attention, jepa_attention_workspace_size,
     jepa_encode, jepa_encode_image, jepa_encode_masked, jepa_encode_tokens, jepa_predict_mod,
+    jepa_head_config, jepa_head_create, jepa_head_forward, jepa_head_free, jepa_head_set_tensor,
+    jepa_pool_mean,
     jepa_encoder_config, jepa_encoder_create, jepa_encoder_free, jepa_encoder_set_tensor,
     jepa_layernorm, jepa_linear, jepa_predict, jepa_predictor_config, jepa_predictor_create,
     jepa_predictor_free, jepa_predictor_set_tensor, jepa_rope3d, jepa_status_str,
@@ -91,6 +93,42 @@ class Encoder:
         try:
             self.close()
         except Exception:
+            pass
+
+
+class Head:
+    """Owner of a jepa_head handle (attentive-pool classifier head)."""
+
+    def __init__(self, embed_dim: int, n_layer: int, n_head: int, ffn_dim: int, n_classes: int, *,
+                 dtype: str = "bf16", max_rows: int = 8192, ln_eps: float = 1e-6):
+        cfg = jepa_head_config(embed_dim=embed_dim, n_layer=n_layer, n_head=n_head, ffn_dim=ffn_dim,
+                               n_classes=n_classes, compute=DTYPES[dtype], max_rows=max_rows,
+                               ln_eps=ln_eps)
+        self.cfg = cfg
+        self.n_classes = n_classes
+        self.handle = jepa_head_create(cfg)
+
+    def set_weights(self, weights: Dict[str, np.ndarray]) -> None:
+        for name, arr in weights.items():
+            jepa_head_set_tensor(self.handle, name, arr)
+
+    def forward(self, x, out=None, stream=None):
+        """x: fp32 device tensor [B, N, D] -> fp32 logits [B, n_classes]."""
+        import torch
+        if out is None:
+            out = torch.empty((x.shape[0], self.n_classes), dtype=torch.float32, device=x.device)
+        jepa_head_forward(self.handle, x, out, stream)
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            jepa_head_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover
             pass
 
 

@@ -52,6 +52,12 @@ class jepa_predictor_config(ctypes.Structure):
         ("has_mod_embed", ctypes.c_int32), ("has_proj_context", ctypes.c_int32)]
 
 
+class jepa_head_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "embed_dim", "n_layer", "n_head", "ffn_dim", "n_classes", "compute", "max_rows")] + [
+        ("ln_eps", ctypes.c_float)]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _I64 = ctypes.c_int64
@@ -72,6 +78,11 @@ _SIGS = {
     "jepa_predictor_set_tensor": ([_P, ctypes.c_char_p, _P, _I, ctypes.POINTER(_I64), _I], _I),
     "jepa_predict": ([_P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P], _I),
     "jepa_predict_mod": ([_P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "jepa_pool_mean": ([_P, _I, _I, _I, _P, _P], _I),
+    "jepa_head_create": ([ctypes.POINTER(jepa_head_config), ctypes.POINTER(_P)], _I),
+    "jepa_head_free": ([_P], None),
+    "jepa_head_set_tensor": ([_P, ctypes.c_char_p, _P, _I, ctypes.POINTER(_I64), _I], _I),
+    "jepa_head_forward": ([_P, _P, _I, _I, _P, _P], _I),
     "jepa_rope3d": ([_P, _P, _I, _I, _I, _I, _I, _I64, _P, _I, _I, _I, _I, _F, _I, _P], _I),
     "jepa_layernorm": ([_P, _P, _P, _I, _I, _F, _P, _I, _P], _I),
     "jepa_linear": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
@@ -283,6 +294,46 @@ def jepa_predict(handle: int, z, ids_ctx, ids_tgt, mask_index: int, grid: Sequen
            load().jepa_predict(handle, _ptr(z), z.shape[0], _ptr(ids_ctx), ids_ctx.numel(),
                                _ptr(ids_tgt), ids_tgt.numel(), mask_index, gt, gh, gw, _ptr(out),
                                _stream(stream)))
+
+
+def jepa_pool_mean(x, out, stream=None) -> None:
+    """x: fp32 device tensor [B, N, D]; out: fp32 device tensor [B, D]."""
+    B, N, D = x.shape
+    _need(x.dtype == _torch().float32 and out.dtype == x.dtype and out.numel() == B * D,
+          "x must be fp32 [B, N, D] and out fp32 [B, D]")
+    _check("jepa_pool_mean", load().jepa_pool_mean(_ptr(x), B, N, D, _ptr(out), _stream(stream)))
+
+
+_HEAD_CFG = {}
+
+
+def jepa_head_create(cfg: jepa_head_config) -> int:
+    h = _P()
+    _check("jepa_head_create", load().jepa_head_create(ctypes.byref(cfg), ctypes.byref(h)))
+    _HEAD_CFG[h.value] = cfg
+    return h.value
+
+
+def jepa_head_free(handle: int) -> None:
+    load().jepa_head_free(handle)
+    _HEAD_CFG.pop(handle, None)
+
+
+def jepa_head_set_tensor(handle: int, name: str, arr: np.ndarray) -> None:
+    p, code, shape, keep = _host_tensor(arr)
+    _check("jepa_head_set_tensor",
+           load().jepa_head_set_tensor(handle, name.encode(), p, code, shape, keep.ndim))
+
+
+def jepa_head_forward(handle: int, x, logits, stream=None) -> None:
+    """x: fp32 device tensor [B, N, D]; logits: fp32 device tensor [B, n_classes]."""
+    c = _HEAD_CFG[handle]
+    B, N, D = x.shape
+    _need(D == c.embed_dim and x.dtype == _torch().float32, "x must be fp32 [B, N, D]")
+    _need(logits.dtype == _torch().float32 and logits.numel() == B * c.n_classes,
+          "logits must be fp32 [B, n_classes]")
+    _check("jepa_head_forward", load().jepa_head_forward(handle, _ptr(x), B, N, _ptr(logits),
+                                                         _stream(stream)))
 
 
 MODALITIES = {"video": 0, "image": 1, "auto": 2}

@@ -782,6 +782,144 @@ int jepa_predict_mod(jepa_predictor* pred, const float* z_dev, int n_enc,
   return JEPA_OK;
 }
 
+// ==================================================================== pooled outputs
+
+struct jepa_head {
+  jepa_head_config cfg;
+  TensorSet ts;
+  std::vector<BlockIdx> blocks;
+  int query = -1, lnkv_w = -1, lnkv_b = -1, q_w = -1, q_b = -1, k_w = -1, k_b = -1, v_w = -1,
+      v_b = -1, ln2_w = -1, ln2_b = -1, up_w = -1, up_b = -1, down_w = -1, down_b = -1,
+      cls_w = -1, cls_b = -1;
+  Workspace ws;
+  DevBuf x;    // fp32 [max_rows, D] token rows through the pool blocks
+  DevBuf kv;   // fp32 [2, max_rows, D]: k, then v of the cross-attention
+  DevBuf q;    // fp32 [D] projected query
+  DevBuf y;    // fp32 [max_rows, D] pooled rows (one per clip)
+};
+
+int jepa_head_create(const jepa_head_config* cfg, jepa_head** out) {
+  if (!cfg || !out) return JEPA_ERR_ARG;
+  *out = nullptr;
+  const jepa_head_config& c = *cfg;
+  if (c.n_head <= 0 || c.embed_dim <= 0 || c.n_layer < 0 || c.n_classes < 1) return JEPA_ERR_ARG;
+  const int hd = c.embed_dim / c.n_head;
+  JEPA_TRY(check_widths(c.compute, c.embed_dim, c.ffn_dim, c.n_head, hd));
+  if (c.max_rows <= 0 || !(c.ln_eps > 0.f)) return JEPA_ERR_ARG;
+  jepa_head* h = new (std::nothrow) jepa_head();
+  if (!h) return JEPA_ERR_OOM;
+  h->cfg = c;
+  h->ts.compute = c.compute;
+  const int64_t D = c.embed_dim, F = c.ffn_dim;
+  h->query = h->ts.add("head.query", {1, D}, false);
+  for (int i = 0; i < c.n_layer; ++i)
+    h->blocks.push_back(add_block(h->ts, "head.blk." + std::to_string(i), D, F));
+  h->lnkv_w = h->ts.add("head.xattn.ln_kv.weight", {D}, false);
+  h->lnkv_b = h->ts.add("head.xattn.ln_kv.bias", {D}, false);
+  // q sees one row and the classifier has any width: both stay fp32 for the fp32 GEMM
+  h->q_w = h->ts.add("head.xattn.q.weight", {D, D}, false);
+  h->q_b = h->ts.add("head.xattn.q.bias", {D}, false);
+  h->k_w = h->ts.add("head.xattn.k.weight", {D, D}, true);
+  h->k_b = h->ts.add("head.xattn.k.bias", {D}, false);
+  h->v_w = h->ts.add("head.xattn.v.weight", {D, D}, true);
+  h->v_b = h->ts.add("head.xattn.v.bias", {D}, false);
+  h->ln2_w = h->ts.add("head.xattn.ln2.weight", {D}, false);
+  h->ln2_b = h->ts.add("head.xattn.ln2.bias", {D}, false);
+  h->up_w = h->ts.add("head.xattn.ffn_up.weight", {F, D}, true);
+  h->up_b = h->ts.add("head.xattn.ffn_up.bias", {F}, false);
+  h->down_w = h->ts.add("head.xattn.ffn_down.weight", {D, F}, true);
+  h->down_b = h->ts.add("head.xattn.ffn_down.bias", {D}, false);
+  h->cls_w = h->ts.add("head.cls.weight", {c.n_classes, D}, false);
+  h->cls_b = h->ts.add("head.cls.bias", {c.n_classes}, false);
+  const size_t m = static_cast<size_t>(c.max_rows);
+  int st = h->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, 0, c.compute);
+  if (st == JEPA_OK) st = dev_alloc(h->x, m * D * 4);
+  if (st == JEPA_OK) st = dev_alloc(h->kv, m * 2 * D * 4);
+  if (st == JEPA_OK) st = dev_alloc(h->q, static_cast<size_t>(D) * 4);
+  if (st == JEPA_OK) st = dev_alloc(h->y, m * D * 4);
+  if (st != JEPA_OK) {
+    jepa_head_free(h);
+    return st;
+  }
+  *out = h;
+  return JEPA_OK;
+}
+
+void jepa_head_free(jepa_head* head) {
+  if (!head) return;
+  dev_free(head->x);
+  dev_free(head->kv);
+  dev_free(head->q);
+  dev_free(head->y);
+  delete head;
+}
+
+int jepa_head_set_tensor(jepa_head* head, const char* name, const void* host, int src_dtype,
+                         const int64_t* shape, int ndim) {
+  if (!head) return JEPA_ERR_ARG;
+  return head->ts.set_tensor(name, host, src_dtype, shape, ndim);
+}
+
+int jepa_head_forward(jepa_head* head, const float* x_dev, int B, int N, float* logits_dev,
+                      void* stream) {
+  if (!head || !x_dev || !logits_dev) return JEPA_ERR_ARG;
+  const jepa_head_config& c = head->cfg;
+  if (B < 1 || N < 1 || N > kXattnMaxTokens) return JEPA_ERR_SHAPE;
+  if (static_cast<long long>(B) * N > c.max_rows) return JEPA_ERR_SHAPE;
+  if (!head->ts.all_set()) return JEPA_ERR_STATE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = c.embed_dim, M = B * N, hd = D / c.n_head, bf = c.compute == JEPA_BF16 ? 1 : 0;
+  float* x = static_cast<float*>(head->x.p);
+  float* kv = static_cast<float*>(head->kv.p);
+  float* q = static_cast<float*>(head->q.p);
+  float* y = static_cast<float*>(head->y.p);
+  // [Notes §2] "Attentive-pool head": the pool blocks run without RoPE.  On the grid 1 x 1 x 1
+  // every token sits at position 0, whose table entries are (cos, sin) = (1, 0) exactly.
+  JEPA_LAUNCH(JEPA_KC_OTHER, s,
+              hipMemcpyAsync(x, x_dev, static_cast<size_t>(M) * D * 4, hipMemcpyDeviceToDevice, s));
+  const RopeSpec rs{1, 1, 1, JEPA_ROPE_TILED, 10000.f, 0};
+  JEPA_TRY(run_blocks(head->ts, head->blocks, c.n_layer, head->ws, x, B, N, D, c.ffn_dim, c.n_head,
+                      c.ln_eps, nullptr, 0, rs, s));
+  // cross-attention: k, v (fp32) from the normed tokens, q from the raw query
+  JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
+              launch_layernorm(x, head->ts.devf(head->lnkv_w), head->ts.devf(head->lnkv_b), M, D,
+                               c.ln_eps, head->ws.h.p, bf, s));
+  float* kk = kv;
+  float* vv = kv + static_cast<size_t>(c.max_rows) * D;
+  JEPA_LAUNCH(JEPA_KC_GEMM_QKV, s,
+              linear(c.compute, head->ws.h.p, head->ts.dev(head->k_w), head->ts.devf(head->k_b), kk, M,
+                     D, D, JEPA_EPI_STORE, 1, s));
+  JEPA_LAUNCH(JEPA_KC_GEMM_QKV, s,
+              linear(c.compute, head->ws.h.p, head->ts.dev(head->v_w), head->ts.devf(head->v_b), vv, M,
+                     D, D, JEPA_EPI_STORE, 1, s));
+  JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
+              launch_gemm_f32(head->ts.devf(head->query), head->ts.devf(head->q_w),
+                              head->ts.devf(head->q_b), q, 1, D, D, JEPA_EPI_STORE, s));
+  JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
+              launch_xattn_query(q, kk, vv, D, head->ts.devf(head->query), y, B, N, c.n_head, hd, s));
+  // y += ffn_down(gelu(ffn_up(ln2(y)))), then the classifier (no final norm)
+  JEPA_LAUNCH(JEPA_KC_LAYERNORM, s,
+              launch_layernorm(y, head->ts.devf(head->ln2_w), head->ts.devf(head->ln2_b), B, D,
+                               c.ln_eps, head->ws.h.p, bf, s));
+  JEPA_LAUNCH(JEPA_KC_GEMM_UP, s,
+              linear(c.compute, head->ws.h.p, head->ts.dev(head->up_w), head->ts.devf(head->up_b),
+                     head->ws.g.p, B, c.ffn_dim, D, JEPA_EPI_GELU, !bf, s));
+  JEPA_LAUNCH(JEPA_KC_GEMM_DOWN, s,
+              linear(c.compute, head->ws.g.p, head->ts.dev(head->down_w), head->ts.devf(head->down_b),
+                     y, B, D, c.ffn_dim, JEPA_EPI_RESIDUAL, 1, s));
+  JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
+              launch_gemm_f32(y, head->ts.devf(head->cls_w), head->ts.devf(head->cls_b), logits_dev, B,
+                              c.n_classes, D, JEPA_EPI_STORE, s));
+  return JEPA_OK;
+}
+
+int jepa_pool_mean(const float* x_dev, int B, int N, int D, float* out_dev, void* stream) {
+  if (!x_dev || !out_dev) return JEPA_ERR_ARG;
+  if (B < 0 || N < 1 || D < 1) return JEPA_ERR_SHAPE;
+  if (B == 0) return JEPA_OK;
+  return hip_status(launch_mean_pool(x_dev, B, N, D, out_dev, static_cast<hipStream_t>(stream)));
+}
+
 // ==================================================================== stand-alone ops
 
 int jepa_rope3d(const void* x_dev, void* y_dev, int dtype, int B, int N, int n_head,

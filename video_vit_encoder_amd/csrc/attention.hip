@@ -610,3 +610,108 @@ hipError_t launch_attention_f32(const float* qkv, float* out, int B, int N, int 
 }
 
 }  // namespace jepa
+
+namespace jepa {
+
+// ---------------------------------------------------------------- single-query pooling
+
+// The cross-attention of the attentive-pool head ([Notes §2] "Attentive-pool head"): one
+// learned query row q (projected, fp32 [D]) attends over the N tokens of each clip, with
+// k and v fp32 (rows of leading dimension ld: k at kv, v at kv + D), softmax(q k^T /
+// sqrt(hd)) v per head, heads concatenated, no output projection; the raw query q0 is the
+// residual: y[b] = q0 + o[b].  k and v are separate row blocks of leading dimension ld.
+// One workgroup per (head, clip): scores in LDS (N floats),
+// the block max and sum, then the weighted sum of v split over 4 key groups (n mod 4) and
+// added in that order, so the result does not depend on the launch.
+template <int HD>
+__global__ __launch_bounds__(256)
+void xattn_query_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                        const float* __restrict__ v, int ld, const float* __restrict__ q0,
+                        float* __restrict__ y, int N, int D, float scale) {
+  extern __shared__ float sc[];   // [N] scores, then probabilities
+  __shared__ float red[256];
+  __shared__ float part[4][HD];
+  const int tid = threadIdx.x, head = blockIdx.x, b = blockIdx.y;
+  const float* qh = q + head * HD;
+  const float* kb = k + static_cast<size_t>(b) * N * ld + head * HD;
+  const float* vb = v + static_cast<size_t>(b) * N * ld + head * HD;
+  float mx = -INFINITY;
+  for (int n = tid; n < N; n += 256) {
+    const f32x4* kr = reinterpret_cast<const f32x4*>(kb + static_cast<size_t>(n) * ld);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < HD / 4; ++c) {
+      const f32x4 k4 = kr[c];
+      s = fmaf(qh[4 * c], k4[0], s);
+      s = fmaf(qh[4 * c + 1], k4[1], s);
+      s = fmaf(qh[4 * c + 2], k4[2], s);
+      s = fmaf(qh[4 * c + 3], k4[3], s);
+    }
+    s *= scale;
+    sc[n] = s;
+    mx = fmaxf(mx, s);
+  }
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  float sum = 0.f;
+  for (int n = tid; n < N; n += 256) {
+    const float p = expf(sc[n] - mx);
+    sc[n] = p;
+    sum += p;
+  }
+  red[tid] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  sum = red[0];
+  // o[d] over the keys n = g, g + 4, ... of group g = tid / 64 (HD <= 64 lanes per group)
+  const int g = tid >> 6, d = tid & 63;
+  if (d < HD) {
+    float acc = 0.f;
+    for (int n = g; n < N; n += 4) acc = fmaf(sc[n], vb[static_cast<size_t>(n) * ld + d], acc);
+    part[g][d] = acc;
+  }
+  __syncthreads();
+  if (tid < HD) {
+    const float o = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+    y[static_cast<size_t>(b) * D + head * HD + tid] = q0[head * HD + tid] + o / sum;
+  }
+}
+
+hipError_t launch_xattn_query(const float* q, const float* k, const float* v, int ld,
+                              const float* q0, float* y, int B, int N, int n_head, int head_dim,
+                              hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  if (N <= 0 || N > kXattnMaxTokens || ld % 4) return hipErrorInvalidValue;
+  const int D = n_head * head_dim;
+  const float scale = static_cast<float>(1.0 / sqrt(static_cast<double>(head_dim)));
+  const dim3 grid(n_head, B);
+  const size_t lds = static_cast<size_t>(N) * 4;
+  static bool configured = false;   // up to 64 KB of dynamic LDS for the scores
+  if (!configured) {
+    for (const void* f : {reinterpret_cast<const void*>(&xattn_query_kernel<64>),
+                          reinterpret_cast<const void*>(&xattn_query_kernel<32>)}) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               kXattnMaxTokens * 4);
+      if (e != hipSuccess) return e;
+    }
+    configured = true;
+  }
+  if (head_dim == 64)
+    xattn_query_kernel<64><<<grid, 256, lds, s>>>(q, k, v, ld, q0, y, N, D, scale);
+  else if (head_dim == 32)
+    xattn_query_kernel<32><<<grid, 256, lds, s>>>(q, k, v, ld, q0, y, N, D, scale);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace jepa

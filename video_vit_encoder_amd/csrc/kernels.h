@@ -71,6 +71,15 @@ hipError_t launch_gather_rows(const float* src, int n_src, int D, const int32_t*
                               void* dst, int bf16, hipStream_t s);
 // dst[i, :] = vec[:] for i < n (fp32).
 hipError_t launch_fill_rows(float* dst, const float* vec, int n, int D, hipStream_t s);
+// Single learned query over the N tokens of each clip (attentive-pool cross-attention):
+// q fp32 [D] (projected), k and v fp32 rows of leading dimension ld (ld >= D, a multiple of 4),
+// y[b] = q0 + concat_h softmax(q_h k_h^T / sqrt(hd)) v_h, fp32 [B, D].  N <= kXattnMaxTokens.
+constexpr int kXattnMaxTokens = 16384;
+hipError_t launch_xattn_query(const float* q, const float* k, const float* v, int ld,
+                              const float* q0, float* y, int B, int N, int n_head, int head_dim,
+                              hipStream_t s);
+// Mean over the tokens of each clip: x fp32 [B, N, D] -> out fp32 [B, D].
+hipError_t launch_mean_pool(const float* x, int B, int N, int D, float* out, hipStream_t s);
 // dst[i] = a[i] + b[i] (fp32), i < n.
 hipError_t launch_add_vec(float* dst, const float* a, const float* b, int n, hipStream_t s);
 

@@ -117,3 +117,39 @@ hipError_t launch_layernorm(const float* x, const float* w, const float* b, int 
 }
 
 }  // namespace jepa
+
+namespace jepa {
+
+// Mean over the N tokens of each clip ([Card] "Run it", --pool mean): x fp32 [B, N, D] ->
+// out fp32 [B, D].  One workgroup of 1024 threads per (64 columns, clip): 16 row groups
+// (n mod 16) accumulate in fp64, added in group order, so the result does not depend on
+// the launch.
+__global__ __launch_bounds__(1024)
+void mean_pool_kernel(const float* __restrict__ x, int N, int D, float* __restrict__ out) {
+  __shared__ double part[16][64];
+  const int tid = threadIdx.x, g = tid >> 6, c = tid & 63;
+  const int col = blockIdx.x * 64 + c, b = blockIdx.y;
+  double acc = 0.0;
+  if (col < D) {
+    const float* xb = x + static_cast<size_t>(b) * N * D + col;
+    for (int n = g; n < N; n += 16) acc += static_cast<double>(xb[static_cast<size_t>(n) * D]);
+  }
+  part[g][c] = acc;
+  __syncthreads();
+  if (g == 0 && col < D) {
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += part[i][c];
+    out[static_cast<size_t>(b) * D + col] = static_cast<float>(s / N);
+  }
+}
+
+hipError_t launch_mean_pool(const float* x, int B, int N, int D, float* out, hipStream_t s) {
+  if (B <= 0 || D <= 0) return hipSuccess;
+  if (N <= 0) return hipErrorInvalidValue;
+  const dim3 grid((D + 63) / 64, B);
+  mean_pool_kernel<<<grid, 1024, 0, s>>>(x, N, D, out);
+  return hipGetLastError();
+}
+
+}  // namespace jepa
