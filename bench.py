@@ -1,7 +1,7 @@
 """Throughput of the V-JEPA 2 ViT-L/16 encoder forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--masked | --image | --predictor [--v21]]
+                    [--masked | --image | --head | --predictor [--v21]]
 
 One step is one jepa_encode call on a batch of 4 synthetic clips of 16 frames x 256x256
 uint8 (2048 tokens per clip, 8192 token rows), already resident in HBM: patch
@@ -32,6 +32,10 @@ target tokens/s.  ``--predictor --v21`` runs the V-JEPA 2.1 ViT-B predictor inst
 8 mask tokens, output 1664, interleaved RoPE, modality vector on every row, context rows
 projected too) on the 8x24x24 grid of a 16-frame 384-px clip with the tube mask's 512
 context and 4096 target ids.
+
+``--head`` measures the attentive-pool classifier head of the V-JEPA 2 SSv2 classifier (3
+pool blocks, 16 heads, 174 classes) on 4 token maps of 2048 x 1024 (N(0,1) rows standing in
+for the encoder output); ``value`` is clips/s.
 
 ``--image`` measures the V-JEPA 2.1 ViT-B/16 native image path (jepa_encode_image) on 16
 uniform uint8 images of 384x384 (576 tokens each, 12 layers); ``value`` is image tokens/s.
@@ -306,6 +310,91 @@ def bench_predictor(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_head(args, B=4, N=2048):
+    import torch
+    import synth
+    import video_vit_encoder_amd as J
+
+    s = synth.HeadShape(1024, 3, 16, 4096, 174)
+    D, F, L, C = s.embed_dim, s.ffn_dim, s.n_layer, s.n_classes
+    log(f"head workload: {B} token maps of {N} x {D}, {L} pool blocks, {C} classes")
+    W = synth.head_weights(s, seed=args.seed, dtype="bf16")
+    x = synth.tokens_normal(5, B, N, D)
+    dev = torch.device("cuda:0")
+    head = J.Head(D, L, s.n_head, F, C, dtype="bf16", max_rows=B * N)
+    head.set_weights(W)
+    x_d = torch.from_numpy(x).to(dev)
+    out = torch.empty((B, C), dtype=torch.float32, device=dev)
+
+    def step():
+        head.forward(x_d, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("non-finite logits")
+    M = B * N
+    work = kernel_work(B, N, D, F, L, feat=0)
+    work.pop("patchify"); work.pop("gemm_embed")
+    b_, f_ = work["gemm_qkv"]; work["gemm_qkv"] = (b_, f_ + 2 * 2 * M * D * D)      # + k, v
+    b_, f_ = work["attention"]; work["attention"] = (b_, f_ + 4 * B * N * D)         # + 1-query
+    b_, f_ = work["gemm_up"]; work["gemm_up"] = (b_, f_ + 2 * B * D * F)
+    b_, f_ = work["gemm_down"]; work["gemm_down"] = (b_, f_ + 2 * B * F * D)
+    work["gemm_embed"] = ("mfma", 2 * D * D + 2 * B * D * C)                         # q, classifier
+    work["layernorm"] = ("hbm", 2 * L * (M * D * 6 + 8 * D) + (M * D * 6 + 8 * D) + (B * D * 6 + 8 * D))
+    flops = sum(v for b, v in work.values() if b == "mfma")
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{ms:.3f} ms/step, {B / (ms * 1e-3):,.0f} clips/s, {tflops:.1f} TFLOP/s")
+    roof, kernels = None, None
+    if not args.no_kernels:
+        kernels, _ = kernel_timing(J, step, args.steps, work)
+        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+        k = kernels[dom]
+        roof = {"kernel": dom, "bound": k["bound"], "achieved": k.get("tflops", k.get("gbs")),
+                "peak": PEAK_BF16_TFLOPS if k["bound"] == "mfma" else PEAK_HBM_GBS,
+                "unit": "TFLOP/s" if k["bound"] == "mfma" else "GB/s", "frac": k["frac"],
+                "traffic": None, "launch_ms": k["avg_ms"]}
+        log(f"dominant kernel {dom}: {k['avg_ms'] * 1e3:.1f} us/launch, frac {k['frac']:.3f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline (oracle head on one token map)")
+        t0 = time.perf_counter()
+        oracle.attentive_pool_head(x[0], W, L, s.n_head)
+        t1 = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([q.get("num_threads", 1) for q in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        cpu = {"value": 1.0 / t1, "unit": "clips/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"float64 numpy oracle head on token map 0 ({N} tokens): {t1:.2f} s"}
+    res = {
+        "metric": "attentive-pool head clips/sec at 1 GPU (V-JEPA 2 SSv2 head on ViT-L token maps); "
+                  "% bf16 MFMA peak",
+        "value": round(B / (ms * 1e-3), 2), "unit": "clips/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) token maps, random N(0,0.02) bf16 weights)",
+        "config": {"workload": f"attentive-pool head: {B} token maps of {N} x {D}, {L} pool blocks "
+                               "(no RoPE), 16 heads, FFN 4096, single-query cross-attention with fp32 "
+                               f"k/v, {C} classes, bf16 MFMA",
+                   "batch_clips": B, "tokens_per_clip": N, "embed_dim": D, "pool_layers": L,
+                   "classes": C},
+        "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": flops, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_image(args, B=16):
     import torch
     import synth
@@ -409,6 +498,8 @@ def main():
                     help="time the masked predictor (jepa_predict) on its 8192-token workload")
     ap.add_argument("--v21", action="store_true",
                     help="with --predictor: the V-JEPA 2.1 ViT-B predictor (jepa_predict_mod)")
+    ap.add_argument("--head", action="store_true",
+                    help="time the attentive-pool classifier head on 4 ViT-L token maps")
     ap.add_argument("--image", action="store_true",
                     help="time the V-JEPA 2.1 ViT-B/16 image path on 16 images of 384x384")
     ap.add_argument("--masked", action="store_true",
@@ -428,6 +519,9 @@ def main():
         return
     if args.image:
         bench_image(args)
+        return
+    if args.head:
+        bench_head(args)
         return
 
     import torch

@@ -893,8 +893,8 @@ int jepa_head_forward(jepa_head* head, const float* x_dev, int B, int N, float* 
               linear(c.compute, head->ws.h.p, head->ts.dev(head->v_w), head->ts.devf(head->v_b), vv, M,
                      D, D, JEPA_EPI_STORE, 1, s));
   JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
-              launch_gemm_f32(head->ts.devf(head->query), head->ts.devf(head->q_w),
-                              head->ts.devf(head->q_b), q, 1, D, D, JEPA_EPI_STORE, s));
+              launch_gemv_f32(head->ts.devf(head->query), head->ts.devf(head->q_w),
+                              head->ts.devf(head->q_b), q, 1, D, D, s));
   JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
               launch_xattn_query(q, kk, vv, D, head->ts.devf(head->query), y, B, N, c.n_head, hd, s));
   // y += ffn_down(gelu(ffn_up(ln2(y)))), then the classifier (no final norm)
@@ -908,8 +908,8 @@ int jepa_head_forward(jepa_head* head, const float* x_dev, int B, int N, float* 
               linear(c.compute, head->ws.g.p, head->ts.dev(head->down_w), head->ts.devf(head->down_b),
                      y, B, D, c.ffn_dim, JEPA_EPI_RESIDUAL, 1, s));
   JEPA_LAUNCH(JEPA_KC_GEMM_EMBED, s,
-              launch_gemm_f32(y, head->ts.devf(head->cls_w), head->ts.devf(head->cls_b), logits_dev, B,
-                              c.n_classes, D, JEPA_EPI_STORE, s));
+              launch_gemv_f32(y, head->ts.devf(head->cls_w), head->ts.devf(head->cls_b), logits_dev, B,
+                              c.n_classes, D, s));
   return JEPA_OK;
 }
 

@@ -620,23 +620,24 @@ namespace jepa {
 // k and v fp32 (rows of leading dimension ld: k at kv, v at kv + D), softmax(q k^T /
 // sqrt(hd)) v per head, heads concatenated, no output projection; the raw query q0 is the
 // residual: y[b] = q0 + o[b].  k and v are separate row blocks of leading dimension ld.
-// One workgroup per (head, clip): scores in LDS (N floats),
-// the block max and sum, then the weighted sum of v split over 4 key groups (n mod 4) and
-// added in that order, so the result does not depend on the launch.
+// One workgroup of 1024 threads per (head, clip): scores in LDS (N floats), the block max
+// and sum, then the weighted sum of v split over 1024 / 64 = 16 key groups (n mod 16) and
+// added in group order, so the result does not depend on the launch.
 template <int HD>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(1024)
 void xattn_query_kernel(const float* __restrict__ q, const float* __restrict__ k,
                         const float* __restrict__ v, int ld, const float* __restrict__ q0,
                         float* __restrict__ y, int N, int D, float scale) {
+  constexpr int NT = 1024, G = NT / 64;
   extern __shared__ float sc[];   // [N] scores, then probabilities
-  __shared__ float red[256];
-  __shared__ float part[4][HD];
+  __shared__ float red[NT];
+  __shared__ float part[G][HD];
   const int tid = threadIdx.x, head = blockIdx.x, b = blockIdx.y;
   const float* qh = q + head * HD;
   const float* kb = k + static_cast<size_t>(b) * N * ld + head * HD;
   const float* vb = v + static_cast<size_t>(b) * N * ld + head * HD;
   float mx = -INFINITY;
-  for (int n = tid; n < N; n += 256) {
+  for (int n = tid; n < N; n += NT) {
     const f32x4* kr = reinterpret_cast<const f32x4*>(kb + static_cast<size_t>(n) * ld);
     float s = 0.f;
 #pragma unroll
@@ -653,35 +654,37 @@ void xattn_query_kernel(const float* __restrict__ q, const float* __restrict__ k
   }
   red[tid] = mx;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = NT / 2; w > 0; w >>= 1) {
     if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
     __syncthreads();
   }
   mx = red[0];
   __syncthreads();
   float sum = 0.f;
-  for (int n = tid; n < N; n += 256) {
+  for (int n = tid; n < N; n += NT) {
     const float p = expf(sc[n] - mx);
     sc[n] = p;
     sum += p;
   }
   red[tid] = sum;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = NT / 2; w > 0; w >>= 1) {
     if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
   sum = red[0];
-  // o[d] over the keys n = g, g + 4, ... of group g = tid / 64 (HD <= 64 lanes per group)
+  // o[d] over the keys n = g, g + G, ... of group g = tid / 64 (HD <= 64 lanes per group)
   const int g = tid >> 6, d = tid & 63;
   if (d < HD) {
     float acc = 0.f;
-    for (int n = g; n < N; n += 4) acc = fmaf(sc[n], vb[static_cast<size_t>(n) * ld + d], acc);
+    for (int n = g; n < N; n += G) acc = fmaf(sc[n], vb[static_cast<size_t>(n) * ld + d], acc);
     part[g][d] = acc;
   }
   __syncthreads();
   if (tid < HD) {
-    const float o = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) o += part[i][tid];
     y[static_cast<size_t>(b) * D + head * HD + tid] = q0[head * HD + tid] + o / sum;
   }
 }
@@ -706,9 +709,9 @@ hipError_t launch_xattn_query(const float* q, const float* k, const float* v, in
     configured = true;
   }
   if (head_dim == 64)
-    xattn_query_kernel<64><<<grid, 256, lds, s>>>(q, k, v, ld, q0, y, N, D, scale);
+    xattn_query_kernel<64><<<grid, 1024, lds, s>>>(q, k, v, ld, q0, y, N, D, scale);
   else if (head_dim == 32)
-    xattn_query_kernel<32><<<grid, 256, lds, s>>>(q, k, v, ld, q0, y, N, D, scale);
+    xattn_query_kernel<32><<<grid, 1024, lds, s>>>(q, k, v, ld, q0, y, N, D, scale);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -643,4 +643,34 @@ hipError_t launch_gemm_f32(const float* A, const float* W, const float* bias, fl
   return hipGetLastError();
 }
 
+// C[m, n] = A[m, :] . W[n, :] + bias[n] (fp32) for a few rows of A: one wavefront per output,
+// lanes stride over K (coalesced rows of W), four partial sums per lane added in order and
+// a butterfly over the wave, so every output sums in a fixed order whatever M is.
+__global__ __launch_bounds__(64)
+void gemv_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
+                     const float* __restrict__ bias, float* __restrict__ C, int N, int K) {
+  const int n = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
+  const float* a = A + static_cast<size_t>(m) * K;
+  const float* w = W + static_cast<size_t>(n) * K;
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+  int k = lane;
+  for (; k + 192 < K; k += 256) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fmaf(a[k + 64 * i], w[k + 64 * i], p[i]);
+  }
+  for (int i = 0; k < K; k += 64, ++i) p[i & 3] = fmaf(a[k], w[k], p[i & 3]);
+  float s = (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) C[static_cast<size_t>(m) * N + n] = s + (bias ? bias[n] : 0.f);
+}
+
+hipError_t launch_gemv_f32(const float* A, const float* W, const float* bias, float* C, int M,
+                           int N, int K, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (M > 65535) return hipErrorInvalidValue;
+  gemv_f32_kernel<<<dim3(N, M), 64, 0, s>>>(A, W, bias, C, N, K);
+  return hipGetLastError();
+}
+
 }  // namespace jepa

@@ -25,6 +25,9 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* b
                             int M, int N, int K, int epi, int out_f32, hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, const float* W, const float* bias, float* C,
                            int M, int N, int K, int epi, hipStream_t s);
+// C = A W^T + bias (fp32) with one wavefront per output, for few rows (M <= 65535).
+hipError_t launch_gemv_f32(const float* A, const float* W, const float* bias, float* C, int M,
+                           int N, int K, hipStream_t s);
 hipError_t launch_layernorm(const float* x, const float* w, const float* b, int M, int D,
                             float eps, void* out, int out_bf16, hipStream_t s);
 hipError_t launch_rope3d(const void* x, void* y, int bf16, int B, int N, int n_head,
