@@ -18,7 +18,7 @@ __all__ = [
     "IMAGENET_MEAN", "IMAGENET_STD", "EncoderSpec", "PredictorSpec",
     "normalize_frames", "patchify", "id_to_thw", "rope_positions", "rope_axis_dim",
     "rope_omegas", "rope_angle_index", "rope_angles", "rope_rotate", "rope_rotate_with_angles",
-    "layer_norm", "gelu_erf", "linear", "attention", "block", "encoder_forward",
+    "layer_norm", "gelu_erf", "linear", "attention", "block_causal_mask", "block", "encoder_forward",
     "encode_tokens", "encoder_forward_batch", "encoder_forward_image", "masked_encoder_forward",
     "predictor_forward", "mean_pool", "attentive_pool_head",
 ]
@@ -221,9 +221,23 @@ def linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
     return y
 
 
+def block_causal_mask(N: int, n_cls: int, slot: int) -> np.ndarray:
+    """Visibility [N, N] (query row, key column) of the block-causal attention of
+    [Parity] "LeVJEPA ViT-L/16 — CLS, block-causal attention, tubelet 1": rows [0, n_cls)
+    are CLS rows, open to every key; the patch tokens that follow sit in temporal slots of
+    ``slot`` tokens, and a patch query sees every patch key of its own and earlier slots
+    (bidirectional inside a slot, causal across slots) and no CLS key."""
+    idx = np.arange(N)
+    slot_of = np.where(idx >= n_cls, (idx - n_cls) // slot, -1)
+    vis = (slot_of[None, :] <= slot_of[:, None]) & (idx[None, :] >= n_cls)
+    vis[:n_cls, :] = True
+    return vis
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_head: int,
               pos_q: np.ndarray, pos_k: np.ndarray, layout: str, theta: float = 10000.0,
-              rows: Optional[np.ndarray] = None, slab: int = 1024) -> np.ndarray:
+              rows: Optional[np.ndarray] = None, slab: int = 1024,
+              visible: Optional[np.ndarray] = None) -> np.ndarray:
     """Multi-head softmax attention with 3-D RoPE on q and k.
 
     q [Nq, D], k, v [Nk, D]; head e owns columns [e*hd, (e+1)*hd) (contiguous split of
@@ -231,7 +245,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_head: int,
     before the 1/sqrt(hd) scaling ([Notes §4]); softmax runs over every key, no mask
     ([Notes §2] attentive-pool head uses the same softmax(q k^T / sqrt(hd)) v form).
     ``rows`` selects query rows (default all); each output row depends only on its own
-    query row, so the result is evaluated a slab of rows at a time.
+    query row, so the result is evaluated a slab of rows at a time.  ``visible`` [Nq, Nk]
+    (default all true) hides keys from queries: their scores are -inf before the softmax.
     """
     Nq, D = q.shape
     hd = D // n_head
@@ -246,6 +261,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_head: int,
             r = rows[s0:s0 + slab]
             qh = rope_rotate(q[r, cs], pos_q[r], layout, theta)
             s = qh @ kh.T / math.sqrt(hd)
+            if visible is not None:
+                s = np.where(visible[r], s, -np.inf)
             s = s - s.max(axis=1, keepdims=True)
             p = np.exp(s)
             p = p / p.sum(axis=1, keepdims=True)

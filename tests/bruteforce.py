@@ -80,7 +80,8 @@ def rope_vec(u: List[float], pos, layout: str, theta: float) -> List[float]:
     return out
 
 
-def attention(q, k, v, n_head, pos, layout, theta):
+def attention(q, k, v, n_head, pos, layout, theta, visible=None):
+    """visible(i, n) -> bool hides key n from query i (default: every key visible)."""
     N = len(q)
     D = len(q[0])
     hd = D // n_head
@@ -91,8 +92,9 @@ def attention(q, k, v, n_head, pos, layout, theta):
         ks = [rope_vec(k[n][c0:c0 + hd], pos[n], layout, theta) for n in range(N)]
         for i in range(N):
             s = [sum(qs[i][j] * ks[n][j] for j in range(hd)) / math.sqrt(hd) for n in range(N)]
-            mx = max(s)
-            ex = [math.exp(x - mx) for x in s]
+            keep = [visible is None or visible(i, n) for n in range(N)]
+            mx = max(s[n] for n in range(N) if keep[n])
+            ex = [math.exp(s[n] - mx) if keep[n] else 0.0 for n in range(N)]
             tot = sum(ex)
             for j in range(hd):
                 out[i][c0 + j] = sum(ex[n] * v[n][c0 + j] for n in range(N)) / tot
