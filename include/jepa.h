@@ -345,6 +345,26 @@ int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, 
  * non-positive sizes). */
 size_t jepa_attention_workspace_size(int dtype, int B, int N, int n_head, int head_dim);
 
+/* Block-causal attention with leading CLS rows ([Parity] "LeVJEPA ViT-L/16 -- CLS,
+ * block-causal attention, tubelet 1": the CLS row first, then the patch tokens T-major;
+ * the CLS carries no position, its RoPE row is the identity; the mask is bidirectional
+ * inside a temporal slot, causal across slots, CLS row open, CLS column closed).
+ *   Each clip has N = n_cls + gt*gh*gw rows: rows [0, n_cls) are CLS rows, row
+ *   n_cls + n is grid token n (id n, as jepa_rope3d with ids NULL); a temporal slot is
+ *   one grid slice of gh*gw tokens.
+ *   CLS rows: q and k unrotated; the query sees every key of the clip.
+ *   Patch row of slot t: the query sees the patch keys of slots 0..t and no CLS key.
+ *   qkv_dev [B*N, 3*n_head*head_dim], out_dev [B*N, n_head*head_dim], dtype, layout,
+ *   theta, ref_grid and the workspace (jepa_attention_workspace_size(dtype, B, N, ...))
+ *   as jepa_attention.  0 <= n_cls < 64.
+ * With n_cls = 0 and gt = 1 every row sees every key and the result equals
+ * jepa_attention on the same rows.
+ * Errors: as jepa_attention; JEPA_ERR_SHAPE for n_cls outside [0, 64). */
+int jepa_attention_block_causal(const void* qkv_dev, void* out_dev, int dtype, int B, int n_cls,
+                                int n_head, int head_dim, int gt, int gh, int gw, int layout,
+                                float theta, int ref_grid, void* work_dev, size_t work_bytes,
+                                void* stream);
+
 /* ------------------------------------------------------------------ kernel timing */
 
 /* Kernel classes of the forwards, for jepa_timing_end. */

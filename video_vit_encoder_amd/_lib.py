@@ -89,6 +89,8 @@ _SIGS = {
     "jepa_attention": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t,
                         _P], _I),
     "jepa_attention_workspace_size": ([_I, _I, _I, _I, _I], ctypes.c_size_t),
+    "jepa_attention_block_causal": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P,
+                                     ctypes.c_size_t, _P], _I),
     "jepa_timing_begin": ([_I], _I),
     "jepa_timing_end": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)], _I),
 }
@@ -429,6 +431,28 @@ def jepa_attention(qkv, out, B: int, N: int, n_head: int, head_dim: int, ids,
            load().jepa_attention(_ptr(qkv), _ptr(out), dt, B, N, n_head, head_dim, _ptr(ids),
                                  gt, gh, gw, LAYOUTS[layout], theta, ref_grid, _ptr(work), wbytes,
                                  _stream(stream)))
+
+
+def jepa_attention_block_causal(qkv, out, B: int, n_cls: int, n_head: int, head_dim: int,
+                                grid: Sequence[int], layout: str, theta: float = 10000.0,
+                                ref_grid: int = 0, stream=None, work=None) -> None:
+    """Block-causal attention with n_cls leading CLS rows: qkv [B*N, 3D] and out [B*N, D]
+    device tensors of one dtype, N = n_cls + gt*gh*gw."""
+    import torch
+    dt = JEPA_BF16 if qkv.dtype == torch.bfloat16 else JEPA_F32
+    gt, gh, gw = grid
+    N = n_cls + gt * gh * gw
+    D = n_head * head_dim
+    _need(qkv.numel() == B * N * 3 * D and out.numel() == B * N * D and out.dtype == qkv.dtype,
+          "qkv [B*N, 3D] and out [B*N, D] of one dtype, N = n_cls + gt*gh*gw")
+    nbytes = jepa_attention_workspace_size(dt, B, N, n_head, head_dim)
+    if work is None and nbytes > 0:
+        work = torch.empty(nbytes, dtype=torch.uint8, device=qkv.device)
+    wbytes = 0 if work is None else work.numel() * work.element_size()
+    _check("jepa_attention_block_causal",
+           load().jepa_attention_block_causal(_ptr(qkv), _ptr(out), dt, B, n_cls, n_head, head_dim,
+                                              gt, gh, gw, LAYOUTS[layout], theta, ref_grid,
+                                              _ptr(work), wbytes, _stream(stream)))
 
 
 def jepa_timing_begin(cap: int) -> None:

@@ -992,24 +992,15 @@ size_t jepa_attention_workspace_size(int dtype, int B, int N, int n_head, int he
   return attn_ws_parts(B, N, n_head * head_dim, &a, &b);
 }
 
-int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
-                   int head_dim, const int32_t* ids_dev, int gt, int gh, int gw, int layout,
-                   float theta, int ref_grid, void* work_dev, size_t work_bytes, void* stream) {
-  if (!qkv_dev || !out_dev) return JEPA_ERR_ARG;
-  if (dtype != JEPA_F32 && dtype != JEPA_BF16) return JEPA_ERR_ARG;
-  if (layout != JEPA_ROPE_TILED && layout != JEPA_ROPE_INTERLEAVED) return JEPA_ERR_ARG;
-  if (!(theta > 1.f)) return JEPA_ERR_ARG;
-  if (head_dim != 64 && head_dim != 32) return JEPA_ERR_SHAPE;
-  if (B < 0 || N < 0 || n_head < 1) return JEPA_ERR_SHAPE;
-  JEPA_TRY(check_grid(gt, gh, gw, ref_grid));
-  if (!ids_dev && static_cast<long long>(N) > static_cast<long long>(gt) * gh * gw) return JEPA_ERR_SHAPE;
-  if (B == 0 || N == 0) return JEPA_OK;
-  const RopeSpec rs{gt, gh, gw, layout, theta, ref_grid};
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// Shared by jepa_attention and jepa_attention_block_causal: ids (NULL: row n is grid
+// token n - n_cls, the n_cls leading rows unrotated) and the mask (slot 0: none).
+static int attention_common(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
+                            int head_dim, const int32_t* ids_dev, const RopeSpec& rs, int n_cls,
+                            int slot, void* work_dev, size_t work_bytes, hipStream_t s) {
   if (dtype == JEPA_F32)
     return hip_status(launch_attention_f32(static_cast<const float*>(qkv_dev),
                                            static_cast<float*>(out_dev), B, N, n_head, head_dim,
-                                           ids_dev, 0, rs, s));
+                                           ids_dev, 0, rs, s, n_cls, slot));
   const int D = n_head * head_dim;
   if (D % 32) return JEPA_ERR_SHAPE;
   size_t off_qk, off_vt;
@@ -1021,11 +1012,49 @@ int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, 
   const int Ns = vt_stride(N);
   JEPA_HIP(launch_rope_table(w, rs, head_dim, s));
   JEPA_HIP(launch_qkv_prepare(static_cast<const uint16_t*>(qkv_dev), qk, vt, Ns, B, N, n_head,
-                              head_dim, ids_dev, rs, w, attn_qscale(head_dim), s));
+                              head_dim, ids_dev, rs, w, attn_qscale(head_dim), s, n_cls));
   return hip_status(launch_attention_fwd(qk, qk + D, 2 * D, vt, Ns,
-                                         static_cast<uint16_t*>(out_dev), B, N, n_head, head_dim, s));
+                                         static_cast<uint16_t*>(out_dev), B, N, n_head, head_dim, s,
+                                         n_cls, slot));
 }
 
+static int attention_args(const void* qkv_dev, void* out_dev, int dtype, int n_head, int head_dim,
+                          int layout, float theta) {
+  if (!qkv_dev || !out_dev) return JEPA_ERR_ARG;
+  if (dtype != JEPA_F32 && dtype != JEPA_BF16) return JEPA_ERR_ARG;
+  if (layout != JEPA_ROPE_TILED && layout != JEPA_ROPE_INTERLEAVED) return JEPA_ERR_ARG;
+  if (!(theta > 1.f)) return JEPA_ERR_ARG;
+  if (head_dim != 64 && head_dim != 32) return JEPA_ERR_SHAPE;
+  if (n_head < 1) return JEPA_ERR_SHAPE;
+  return JEPA_OK;
+}
+
+int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
+                   int head_dim, const int32_t* ids_dev, int gt, int gh, int gw, int layout,
+                   float theta, int ref_grid, void* work_dev, size_t work_bytes, void* stream) {
+  JEPA_TRY(attention_args(qkv_dev, out_dev, dtype, n_head, head_dim, layout, theta));
+  if (B < 0 || N < 0) return JEPA_ERR_SHAPE;
+  JEPA_TRY(check_grid(gt, gh, gw, ref_grid));
+  if (!ids_dev && static_cast<long long>(N) > static_cast<long long>(gt) * gh * gw) return JEPA_ERR_SHAPE;
+  if (B == 0 || N == 0) return JEPA_OK;
+  const RopeSpec rs{gt, gh, gw, layout, theta, ref_grid};
+  return attention_common(qkv_dev, out_dev, dtype, B, N, n_head, head_dim, ids_dev, rs, 0, 0,
+                          work_dev, work_bytes, static_cast<hipStream_t>(stream));
+}
+
+int jepa_attention_block_causal(const void* qkv_dev, void* out_dev, int dtype, int B, int n_cls,
+                                int n_head, int head_dim, int gt, int gh, int gw, int layout,
+                                float theta, int ref_grid, void* work_dev, size_t work_bytes,
+                                void* stream) {
+  JEPA_TRY(attention_args(qkv_dev, out_dev, dtype, n_head, head_dim, layout, theta));
+  if (B < 0 || n_cls < 0 || n_cls >= 64) return JEPA_ERR_SHAPE;
+  JEPA_TRY(check_grid(gt, gh, gw, ref_grid));
+  if (B == 0) return JEPA_OK;
+  const int N = n_cls + gt * gh * gw;
+  const RopeSpec rs{gt, gh, gw, layout, theta, ref_grid};
+  return attention_common(qkv_dev, out_dev, dtype, B, N, n_head, head_dim, nullptr, rs, n_cls,
+                          gh * gw, work_dev, work_bytes, static_cast<hipStream_t>(stream));
+}
 
 int jepa_timing_begin(int cap) {
   if (cap < 1 || g_timing.on) return JEPA_ERR_ARG;

@@ -83,8 +83,10 @@ __device__ __forceinline__ void rope_chunk(float* x, int j0, const Thw& g, int l
   }
 }
 
-__device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot) {
-  const int id = ids ? ids[n] : n;
+// grid id of row n: ids[n], else n - lead (rows below lead clamp to id 0, position
+// (0, 0, 0), where the rotation is the identity)
+__device__ __forceinline__ int token_id(const int32_t* ids, int n, int ntot, int lead) {
+  const int id = ids ? ids[n] : n - lead;
   return min(max(id, 0), ntot - 1);
 }
 
@@ -128,11 +130,21 @@ __device__ __forceinline__ float max_halves(float x) {
 //     tile sets the max exactly, so the running sum never underflows;
 //   * the row sum adds the bf16-rounded probabilities (the values the second product
 //     uses) with v_dot2_f32_bf16.
-template <int HD>
+// BC: the block-causal mask of [Parity] "LeVJEPA ViT-L/16 — CLS, block-causal attention,
+// tubelet 1".  Rows [0, n_cls) are CLS rows that see every key; row r >= n_cls is a patch
+// token of temporal slot s = (r - n_cls) / slot and sees the keys [n_cls, lim(r)), lim(r) =
+// n_cls + (s + 1) * slot capped at N: no CLS key, every key of its own and the earlier
+// slots.  The query blocks take the patch rows in order and the CLS rows after them,
+// aligned so that the last block ends on the last row; a block then needs only the key
+// tiles below the limit of its last row (the last block, which holds the CLS rows and the
+// last slot, needs them all), so the work follows the mask's density.  Scores outside
+// [lo, lim) become -inf in the tiles that straddle a limit.  The heaviest blocks start
+// first.
+template <int HD, bool BC>
 __global__ __launch_bounds__(512, 1)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int ld,
                      const uint16_t* __restrict__ vt, int Ns, uint16_t* __restrict__ out, int N,
-                     int H, int nqb) {
+                     int H, int nqb, int n_cls, int slot) {
   constexpr int NW = 8, BQ = NW * 64, BKV = 64, S = 4;
   constexpr int KS = HD / 16;                   // MFMA k-steps over the head dim
   constexpr int DT = HD / 32;                   // 32-dim blocks of the output
@@ -155,9 +167,29 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // blocks of one (clip, head), which read the same keys and values, share an XCD's L2.
   int wg = blockIdx.x;
   if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
-  const int qblk = wg % nqb, bh = wg / nqb;
+  const int qblk = BC ? nqb - 1 - wg % nqb : wg % nqb, bh = wg / nqb;
   const int head = bh % H, b = bh / H;
   const int D = H * HD;
+
+  // query j of the block order and its row: j >= N - n_cls are the CLS rows (BC)
+  const int jbase = (BC ? N - nqb * BQ : 0) + qblk * BQ;
+  auto row_of = [&](int j) { return j < N - n_cls ? j + n_cls : j - (N - n_cls); };
+  auto limit_of = [&](int r) { return r < n_cls ? N : min(N, n_cls + ((r - n_cls) / slot + 1) * slot); };
+  int qrow[2], lo[2], lim[2];
+  bool qok[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int j = jbase + wave * 64 + g * 32 + l32;
+    if (BC) {
+      qok[g] = j >= 0;
+      qrow[g] = row_of(max(j, 0));
+      lo[g] = qrow[g] < n_cls ? 0 : n_cls;
+      lim[g] = limit_of(qrow[g]);
+    } else {
+      qok[g] = j < N;
+      qrow[g] = min(j, N - 1);
+    }
+  }
 
   // K rows are 128 B (hd 64) or 64 B (hd 32), V^T rows 128 B; chunk c of row r sits at
   // c ^ kkey(r) (K) or c ^ lds_key128(r) (V^T)
@@ -167,7 +199,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const uint32_t sbase = lds_addr(smem);
   const uint16_t* kbase = k + static_cast<size_t>(b) * N * ld + head * HD;
   const uint16_t* vbase = vt + static_cast<size_t>(b * H + head) * HD * Ns;
-  const int ntiles = (N + BKV - 1) / BKV;
+  int ntiles = (N + BKV - 1) / BKV;
+  if (BC) {
+    const int jl = jbase + BQ - 1;   // the block's last query, in [0, N)
+    if (jl < N - n_cls) ntiles = (limit_of(row_of(jl)) + BKV - 1) / BKV;
+  }
 
   // Tile t into buffer t % S: instruction i = qd*NW + wave of the tile fills 1 KB of K
   // (i < K_INS) or of V^T.  K rows past N repeat row N - 1 (their scores are masked); V^T
@@ -196,8 +232,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   bf16x8 qf[2][KS];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int qr = min(qblk * BQ + wave * 64 + g * 32 + l32, N - 1);
-    const uint16_t* src = q + (static_cast<size_t>(b) * N + qr) * ld + head * HD;
+    const uint16_t* src = q + (static_cast<size_t>(b) * N + qrow[g]) * ld + head * HD;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) qf[g][kk] = *reinterpret_cast<const bf16x8*>(src + (2 * kk + h) * 8);
   }
@@ -297,7 +332,21 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // Softmax of tile t's scores into pf, updating m_run, l_run (and o on a rescale).
   auto softmax = [&](int t) __attribute__((always_inline)) {
     const int kb = t * BKV;
-    if (kb + BKV > N) {
+    if (BC) {
+      if (__ballot(kb + BKV > lim[0] || kb + BKV > lim[1] || kb < lo[0] || kb < lo[1]) != 0) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const uint32_t span = static_cast<uint32_t>(lim[g] - lo[g]);
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kb + t2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+              if (static_cast<uint32_t>(key - lo[g]) >= span) sc[g][t2][i] = -INFINITY;
+            }
+        }
+      }
+    } else if (kb + BKV > N) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -405,10 +454,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // ---- normalise and store: element i of o[g][dt] is dim 32 dt + 8(i/4) + 4h + i%4
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int qi = qblk * BQ + wave * 64 + g * 32 + l32;
     const float inv = 1.0f / (l_run[g] + __shfl_xor(l_run[g], 32));
-    if (qi < N) {
-      uint16_t* dst = out + (static_cast<size_t>(b) * N + qi) * D + head * HD;
+    if (qok[g]) {
+      uint16_t* dst = out + (static_cast<size_t>(b) * N + qrow[g]) * D + head * HD;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -422,34 +470,41 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 }
 
-template <int HD>
+template <int HD, bool BC>
 static hipError_t attn_launch(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt, int Ns,
-                              uint16_t* out, int B, int N, int n_head, hipStream_t s) {
+                              uint16_t* out, int B, int N, int n_head, int n_cls, int slot,
+                              hipStream_t s) {
   constexpr int LDS = 4 * (64 * HD * 2 + HD * 64 * 2);
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<HD>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<HD, BC>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int nqb = (N + 511) / 512;
   const dim3 grid(nqb * n_head * B);
-  attn_fwd_kernel<HD><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb);
+  attn_fwd_kernel<HD, BC><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb, n_cls, slot);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
                                 int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
-                                hipStream_t s) {
+                                hipStream_t s, int n_cls, int slot) {
   if (B <= 0 || N <= 0) return hipSuccess;
   if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N) || Ns % 16 || ld % 8) return hipErrorInvalidValue;
   // 32-bit DMA offsets: one clip's rows of q/k and one (clip, head)'s V^T rows
   if (static_cast<size_t>(N) * ld * 2 >= (size_t(1) << 31) ||
       static_cast<size_t>(head_dim) * Ns * 2 >= (size_t(1) << 31))
     return hipErrorInvalidValue;
-  if (head_dim == 64) return attn_launch<64>(q, k, ld, vt, Ns, out, B, N, n_head, s);
-  return attn_launch<32>(q, k, ld, vt, Ns, out, B, N, n_head, s);
+  if (slot > 0) {
+    // the first key tile must hold a key every query sees (key n_cls)
+    if (n_cls < 0 || n_cls >= 64 || n_cls >= N) return hipErrorInvalidValue;
+    if (head_dim == 64) return attn_launch<64, true>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, s);
+    return attn_launch<32, true>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, s);
+  }
+  if (head_dim == 64) return attn_launch<64, false>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
+  return attn_launch<32, false>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
 }
 
 // Attention inputs from a projection already in memory (the stand-alone entry point):
@@ -492,11 +547,13 @@ void qkv_prepare_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__
 
 hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, int Ns, int B,
                               int N, int n_head, int head_dim, const int32_t* ids,
-                              const RopeSpec& r, const void* tab, float qscale, hipStream_t s) {
+                              const RopeSpec& r, const void* tab, float qscale, hipStream_t s,
+                              int lead) {
   if (B <= 0 || N <= 0) return hipSuccess;
   if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N)) return hipErrorInvalidValue;
   const int D = n_head * head_dim;
-  const RopeArgs ra{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw, 0};
+  const RopeArgs ra{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw, 0,
+                    lead};
   const long long M = static_cast<long long>(B) * N;
   const long long total = M * (3 * D / 4);
   const dim3 grid(static_cast<unsigned>(min(total, 256LL * 2048) / 256 + 1));
@@ -521,7 +578,7 @@ template <int HD>
 __global__ __launch_bounds__(64)
 void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out, int N, int H,
                      const int32_t* __restrict__ ids_all, int ids_stride, RopeSpec r, RopeFreq fr,
-                     float scale) {
+                     float scale, int n_cls, int slot) {
   constexpr int D3 = 2 * ((HD / 3) / 2);
   constexpr int MF = D3 / 2;
   constexpr int BKV = 64;
@@ -540,7 +597,7 @@ void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out, int
   const int qr = min(q, N - 1);
   float qv[HD], ov[HD];
   {
-    const Thw g = decode_id(token_id(ids, qr, ntot), r.gh, r.gw);
+    const Thw g = decode_id(token_id(ids, qr, ntot, n_cls), r.gh, r.gw);
 #pragma unroll
     for (int j = 0; j < HD; ++j) qv[j] = base[static_cast<size_t>(qr) * ld + j];
     rope_chunk<HD, HD>(qv, 0, g, r.layout, tab);
@@ -550,12 +607,18 @@ void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out, int
       ov[j] = 0.f;
     }
   }
+  // block-causal mask (slot > 0): a patch row sees the keys [n_cls, lim), a CLS row all
+  int lo = 0, lim = N;
+  if (slot > 0 && qr >= n_cls) {
+    lo = n_cls;
+    lim = min(N, n_cls + ((qr - n_cls) / slot + 1) * slot);
+  }
   float m_run = -INFINITY, l_run = 0.f;
   for (int kb = 0; kb < N; kb += BKV) {
     __syncthreads();
     {
       const int kr = min(kb + tid, N - 1);
-      const Thw g = decode_id(token_id(ids, kr, ntot), r.gh, r.gw);
+      const Thw g = decode_id(token_id(ids, kr, ntot, n_cls), r.gh, r.gw);
       float kv[HD];
 #pragma unroll
       for (int j = 0; j < HD; ++j) kv[j] = base[static_cast<size_t>(kr) * ld + D + j];
@@ -569,6 +632,7 @@ void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out, int
     __syncthreads();
     const int nk = min(BKV, N - kb);
     for (int k = 0; k < nk; ++k) {
+      if (kb + k < lo || kb + k >= lim) continue;
       float sc = 0.f;
 #pragma unroll
       for (int j = 0; j < HD; ++j) sc = fmaf(qv[j], Ks[k][j], sc);
@@ -595,15 +659,15 @@ void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out, int
 
 hipError_t launch_attention_f32(const float* qkv, float* out, int B, int N, int n_head,
                                 int head_dim, const int32_t* ids, int ids_stride,
-                                const RopeSpec& r, hipStream_t s) {
+                                const RopeSpec& r, hipStream_t s, int n_cls, int slot) {
   if (B <= 0 || N <= 0) return hipSuccess;
   const RopeFreq fr = make_freq(head_dim, r.theta);
   const float scale = static_cast<float>(1.0 / sqrt(static_cast<double>(head_dim)));
   const dim3 grid((N + 63) / 64, n_head, B);
   if (head_dim == 64)
-    attn_f32_kernel<64><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, ids_stride, r, fr, scale);
+    attn_f32_kernel<64><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, ids_stride, r, fr, scale, n_cls, slot);
   else if (head_dim == 32)
-    attn_f32_kernel<32><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, ids_stride, r, fr, scale);
+    attn_f32_kernel<32><<<grid, 64, 0, s>>>(qkv, out, N, n_head, ids, ids_stride, r, fr, scale, n_cls, slot);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -42,26 +42,31 @@ hipError_t launch_gemm_bf16_qkv(const uint16_t* A, const uint16_t* W, const floa
                                 int head_dim, const int32_t* ids, int ids_stride, int N,
                                 const RopeSpec& r, const void* tab, float qscale, hipStream_t s);
 // The same preparation from a projection already in memory: qkv [M, 3D] bf16 ->
-// q', k' into qk [M, 2D] and v into vt [B][H][hd][Ns].
+// q', k' into qk [M, 2D] and v into vt [B][H][hd][Ns].  Without ids, rows n < lead of a
+// clip (CLS rows) keep q and k unrotated and row n >= lead is grid token n - lead.
 hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, int Ns, int B,
                               int N, int n_head, int head_dim, const int32_t* ids,
-                              const RopeSpec& r, const void* tab, float qscale, hipStream_t s);
+                              const RopeSpec& r, const void* tab, float qscale, hipStream_t s,
+                              int lead = 0);
 // Flash attention on prepared inputs: q (rotated, scaled by log2(e)/sqrt(hd)) and k
 // (rotated) rows of leading dimension ld (elements), v transposed [B][H][hd][Ns];
-// out [B*N, H*hd] bf16.
+// out [B*N, H*hd] bf16.  slot > 0: block-causal mask with n_cls (< 64) leading CLS rows
+// that see every key, the other rows in temporal slots of `slot` tokens that see the
+// non-CLS keys of their own and earlier slots.
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
                                 int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
-                                hipStream_t s);
+                                hipStream_t s, int n_cls = 0, int slot = 0);
 // Row stride (keys) of the transposed V layout for N tokens.
 inline int vt_stride(int N) { return (N + 15) / 16 * 16; }
 // Scale folded into q: log2(e) / sqrt(head_dim).
 inline float attn_qscale(int head_dim) {
   return static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(head_dim)));
 }
-// ids: grid ids of clip b at ids + b * ids_stride (NULL: 0..N-1).
+// ids: grid ids of clip b at ids + b * ids_stride (NULL: row n is token n - n_cls, the
+// n_cls leading CLS rows unrotated); slot > 0 adds the block-causal mask as above.
 hipError_t launch_attention_f32(const float* qkv, float* out, int B, int N, int n_head,
                                 int head_dim, const int32_t* ids, int ids_stride,
-                                const RopeSpec& r, hipStream_t s);
+                                const RopeSpec& r, hipStream_t s, int n_cls = 0, int slot = 0);
 // uint8 [B,T,H,W,3] -> normalised patch rows (bf16 or fp32): all B*N tokens ([B*N, 1536],
 // ids NULL), or the K tokens ids[b*K + k] of each clip ([B*K, 1536], ids clamped to [0, N)).
 hipError_t launch_patchify(const uint8_t* clip, int B, int T, int H, int W, void* A, int bf16,

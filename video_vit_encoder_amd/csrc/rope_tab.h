@@ -25,13 +25,16 @@ struct RopeArgs {
   int layout;           // 0 tiled, 1 interleaved
   int ntot, gh, gw;     // grid size gt*gh*gw and its last two sides
   int ids_stride;       // ids of clip b start at ids + b * ids_stride (0: shared by all)
+  int lead;             // without ids: rows n < lead of a clip take grid position (0, 0, 0),
+                        // where every rotation is the identity, and row n >= lead is token
+                        // n - lead (a leading CLS row)
 };
 
 // Grid coordinates of the token of row r.
 __device__ __forceinline__ Thw rope_token(int r, const RopeArgs& ra, int* clip) {
   const int b = r / ra.N, n = r - b * ra.N;
   *clip = b;
-  int id = ra.ids ? ra.ids[b * ra.ids_stride + n] : n;
+  int id = ra.ids ? ra.ids[b * ra.ids_stride + n] : n - ra.lead;
   id = min(max(id, 0), ra.ntot - 1);
   return decode_id(id, ra.gh, ra.gw);
 }
