@@ -1,7 +1,7 @@
 """Throughput of the V-JEPA 2 ViT-L/16 encoder forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--masked | --image | --head | --predictor [--v21]]
+                    [--masked | --image | --head | --block-causal | --predictor [--v21]]
 
 One step is one jepa_encode call on a batch of 4 synthetic clips of 16 frames x 256x256
 uint8 (2048 tokens per clip, 8192 token rows), already resident in HBM: patch
@@ -39,6 +39,13 @@ for the encoder output); ``value`` is clips/s.
 
 ``--image`` measures the V-JEPA 2.1 ViT-B/16 native image path (jepa_encode_image) on 16
 uniform uint8 images of 384x384 (576 tokens each, 12 layers); ``value`` is image tokens/s.
+
+``--block-causal`` measures the block-causal attention with a CLS row
+(jepa_attention_block_causal) at the LeVJEPA ViT-L/16 shape: 8 clips of 1 + 16 x 14 x 14 =
+3137 rows (16 frames of 224 px at tubelet 1), 16 heads of 64, N(0,1) bf16 q/k/v rows;
+``value`` is rows/s of the whole call (RoPE table, q/k/v preparation, flash kernel), the
+roofline counts the visible (query, key) pairs only, and the unmasked kernel on the same
+rows is timed beside it.
 """
 from __future__ import annotations
 
@@ -395,6 +402,103 @@ def bench_head(args, B=4, N=2048):
     print(json.dumps(res), flush=True)
 
 
+def bench_block_causal(args, B=8, n_cls=1, grid=(16, 14, 14), H=16, hd=64):
+    import torch
+    import video_vit_encoder_amd as J
+
+    slot = grid[1] * grid[2]
+    N = n_cls + grid[0] * slot
+    D = H * hd
+    log(f"block-causal workload: {B} clips of {N} rows ({n_cls} CLS + {grid}), {H} heads of {hd}")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(args.seed)
+    qkv = torch.randn((B * N, 3 * D), generator=g).to(torch.bfloat16).to(dev)
+    out = torch.empty((B * N, D), dtype=torch.bfloat16, device=dev)
+    out_full = torch.empty_like(out)
+    work = torch.empty(J.jepa_attention_workspace_size(J.JEPA_BF16, B, N, H, hd), dtype=torch.uint8,
+                       device=dev)
+    ids = torch.from_numpy(np.r_[np.zeros(n_cls), np.arange(N - n_cls)].astype(np.int32)).to(dev)
+
+    def step():
+        J.jepa_attention_block_causal(qkv, out, B, n_cls, H, hd, grid, "tiled", work=work)
+
+    def step_full():
+        J.jepa_attention(qkv, out_full, B, N, H, hd, ids, grid, "tiled", work=work)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(args.steps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    ms = timed(step)
+    ms_full = timed(step_full)
+    if not bool(torch.isfinite(out.float()).all()):
+        raise RuntimeError("non-finite output")
+    # visible (query, key) pairs: CLS rows see all N keys, a patch row of slot t sees (t+1)*slot
+    pairs = n_cls * N + slot * slot * sum(t + 1 for t in range(grid[0]))
+    flops = 4 * hd * pairs * H * B
+    log(f"{ms:.3f} ms/step ({ms_full:.3f} unmasked), {B * N / (ms * 1e-3):,.0f} rows/s, "
+        f"density {pairs / N / N:.4f}")
+    roof, kernels = None, None
+    if not args.no_kernels:
+        wk = {"attention": ("mfma", flops),
+              "other": ("hbm", B * N * 3 * D * 2 + B * N * 3 * D * 2)}
+        kernels, _ = kernel_timing(J, step, args.steps, wk)
+        full_k, _ = kernel_timing(J, step_full, args.steps, {"attention": ("mfma", 4 * hd * N * N * H * B)})
+        k = kernels["attention"]
+        roof = {"kernel": "attention", "bound": "mfma", "achieved": k["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": k["frac"], "traffic": None, "launch_ms": k["avg_ms"]}
+        kernels["attention_unmasked_same_rows"] = full_k["attention"]
+        log(f"flash kernel: {k['avg_ms'] * 1e3:.1f} us/launch masked, "
+            f"{full_k['attention']['avg_ms'] * 1e3:.1f} us unmasked; frac {k['frac']:.3f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline (oracle block-causal attention, whole clips, all heads, >= 10 s)")
+        pos = np.concatenate([np.zeros((n_cls, 3)),
+                              oracle.rope_positions(np.arange(N - n_cls), grid[1], grid[2], 0)])
+        vis = oracle.block_causal_mask(N, n_cls, slot)
+        done, t1 = 0, 0.0
+        while t1 < 10.0:
+            x = qkv[(done % B) * N:(done % B + 1) * N].float().cpu().numpy().astype(np.float64)
+            t0 = time.perf_counter()
+            oracle.attention(x[:, :D], x[:, D:2 * D], x[:, 2 * D:], H, pos, pos, "tiled", visible=vis)
+            t1 += time.perf_counter() - t0
+            done += 1
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([q.get("num_threads", 1) for q in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        cpu = {"value": round(done * N / t1, 1), "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"float64 numpy oracle attention with the block-causal mask on {done} whole "
+                         f"clips ({N} rows, {H} heads each): {t1:.2f} s"}
+    res = {
+        "metric": "block-causal attention rows/sec at 1 GPU (LeVJEPA ViT-L/16 shape, 16f/224px + CLS); "
+                  "% bf16 MFMA peak",
+        "value": round(B * N / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) q/k/v rows rounded to bf16)",
+        "config": {"workload": f"block-causal attention: {B} clips of {N} rows (CLS + 16 x 14 x 14 patch "
+                               f"tokens, slots of {slot}), {H} heads of {hd}, tiled 3-D RoPE, bf16 MFMA",
+                   "batch_clips": B, "rows_per_clip": N, "n_cls": n_cls, "slot": slot, "heads": H,
+                   "head_dim": hd, "mask_density": round(pairs / N / N, 4)},
+        "ms_per_step_unmasked": round(ms_full, 4),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flops_per_step": flops,
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_image(args, B=16):
     import torch
     import synth
@@ -502,6 +606,8 @@ def main():
                     help="time the attentive-pool classifier head on 4 ViT-L token maps")
     ap.add_argument("--image", action="store_true",
                     help="time the V-JEPA 2.1 ViT-B/16 image path on 16 images of 384x384")
+    ap.add_argument("--block-causal", action="store_true",
+                    help="time the block-causal attention with a CLS row at the LeVJEPA shape")
     ap.add_argument("--masked", action="store_true",
                     help="time the masked-encoder forward on tube-mask contexts (512 of 2048 "
                          "tokens per clip) instead of the full forward")
@@ -522,6 +628,9 @@ def main():
         return
     if args.head:
         bench_head(args)
+        return
+    if args.block_causal:
+        bench_block_causal(args)
         return
 
     import torch

@@ -382,8 +382,9 @@ enum jepa_kernel_class {
 };
 
 /* Per-launch timing of the forwards, for measurement harnesses.  After
- * jepa_timing_begin(cap), every jepa_encode, jepa_encode_tokens and jepa_predict
- * records a HIP event pair on its own stream around each kernel launch, for at most
+ * jepa_timing_begin(cap), every forward (jepa_encode*, jepa_predict*, jepa_head_forward)
+ * and the stand-alone jepa_attention / jepa_attention_block_causal record a HIP event
+ * pair on their own stream around each kernel launch, for at most
  * `cap` launches per class (later launches are not recorded).  Process-wide state, not
  * thread-safe; the events add a small gap between launches, so time throughput with
  * timing off.  Errors: JEPA_ERR_ARG (cap < 1, or timing already on), JEPA_ERR_HIP. */

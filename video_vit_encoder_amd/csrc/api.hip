@@ -997,10 +997,12 @@ size_t jepa_attention_workspace_size(int dtype, int B, int N, int n_head, int he
 static int attention_common(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
                             int head_dim, const int32_t* ids_dev, const RopeSpec& rs, int n_cls,
                             int slot, void* work_dev, size_t work_bytes, hipStream_t s) {
-  if (dtype == JEPA_F32)
-    return hip_status(launch_attention_f32(static_cast<const float*>(qkv_dev),
-                                           static_cast<float*>(out_dev), B, N, n_head, head_dim,
-                                           ids_dev, 0, rs, s, n_cls, slot));
+  if (dtype == JEPA_F32) {
+    JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
+                launch_attention_f32(static_cast<const float*>(qkv_dev), static_cast<float*>(out_dev),
+                                     B, N, n_head, head_dim, ids_dev, 0, rs, s, n_cls, slot));
+    return JEPA_OK;
+  }
   const int D = n_head * head_dim;
   if (D % 32) return JEPA_ERR_SHAPE;
   size_t off_qk, off_vt;
@@ -1010,12 +1012,14 @@ static int attention_common(const void* qkv_dev, void* out_dev, int dtype, int B
   uint16_t* qk = reinterpret_cast<uint16_t*>(w + off_qk);
   uint16_t* vt = reinterpret_cast<uint16_t*>(w + off_vt);
   const int Ns = vt_stride(N);
-  JEPA_HIP(launch_rope_table(w, rs, head_dim, s));
-  JEPA_HIP(launch_qkv_prepare(static_cast<const uint16_t*>(qkv_dev), qk, vt, Ns, B, N, n_head,
-                              head_dim, ids_dev, rs, w, attn_qscale(head_dim), s, n_cls));
-  return hip_status(launch_attention_fwd(qk, qk + D, 2 * D, vt, Ns,
-                                         static_cast<uint16_t*>(out_dev), B, N, n_head, head_dim, s,
-                                         n_cls, slot));
+  JEPA_LAUNCH(JEPA_KC_OTHER, s, launch_rope_table(w, rs, head_dim, s));
+  JEPA_LAUNCH(JEPA_KC_OTHER, s,
+              launch_qkv_prepare(static_cast<const uint16_t*>(qkv_dev), qk, vt, Ns, B, N, n_head,
+                                 head_dim, ids_dev, rs, w, attn_qscale(head_dim), s, n_cls));
+  JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
+              launch_attention_fwd(qk, qk + D, 2 * D, vt, Ns, static_cast<uint16_t*>(out_dev), B, N,
+                                   n_head, head_dim, s, n_cls, slot));
+  return JEPA_OK;
 }
 
 static int attention_args(const void* qkv_dev, void* out_dev, int dtype, int n_head, int head_dim,

@@ -167,7 +167,22 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // blocks of one (clip, head), which read the same keys and values, share an XCD's L2.
   int wg = blockIdx.x;
   if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
-  const int qblk = BC ? nqb - 1 - wg % nqb : wg % nqb, bh = wg / nqb;
+  int qblk = wg % nqb, bh = wg / nqb;
+  if (BC) {
+    // heaviest blocks first: on the XCD it lands on (blockIdx.x % 8), workgroup i takes
+    // rank i / per of one of that XCD's `per` (clip, head) pairs, the latest query block
+    // first, so every XCD starts its longest blocks first and keeps each pair's blocks in
+    // its own L2
+    const int HB = gridDim.x / nqb;
+    if ((HB & 7) == 0) {
+      const int per = HB >> 3, i = blockIdx.x >> 3;
+      qblk = nqb - 1 - i / per;
+      bh = (blockIdx.x & 7) * per + i % per;
+    } else {
+      qblk = nqb - 1 - static_cast<int>(blockIdx.x) / HB;
+      bh = blockIdx.x % HB;
+    }
+  }
   const int head = bh % H, b = bh / H;
   const int D = H * HD;
 
@@ -507,40 +522,80 @@ hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, co
   return attn_launch<32, false>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
 }
 
-// Attention inputs from a projection already in memory (the stand-alone entry point):
-// thread i handles 4 consecutive columns of one row of qkv [M, 3D]: q and k are rotated
-// (q also scaled) into qk [M, 2D], v goes to vt as in the QKV epilogue.
+// Attention inputs from a projection already in memory (the stand-alone entry point): one
+// workgroup per (64-row tile, section x head, clip) of qkv [B*N, 3D].  Four threads per
+// row each take HD/4 consecutive columns (16-byte loads): q and k are rotated (q also
+// scaled) into qk [B*N, 2D]; v goes through LDS and leaves transposed, each thread writing
+// one 16-key group of one dim (the keys in vt_pos order, 32 contiguous bytes), so the four
+// threads of a dim store 128 contiguous bytes.
 template <int HD>
 __global__ __launch_bounds__(256)
 void qkv_prepare_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ qk,
-                        uint16_t* __restrict__ vt, int Ns, long long M, int D, RopeArgs ra,
-                        float qscale) {
-  const int gpr = 3 * D / 4;  // 4-column groups per row
-  const long long total = M * gpr;
-  for (long long e = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-       e += static_cast<long long>(gridDim.x) * blockDim.x) {
-    const int row = static_cast<int>(e / gpr);
-    const int col = static_cast<int>(e - static_cast<long long>(row) * gpr) * 4;
-    const int sec = col / D, cin = col - sec * D;
-    const int head = cin / HD, jj = cin - head * HD;
-    const u32x2 raw = *reinterpret_cast<const u32x2*>(qkv + static_cast<size_t>(row) * 3 * D + col);
-    float v[4] = {bf16_to_f32(static_cast<uint16_t>(raw[0] & 0xFFFF)), bf16_to_f32(static_cast<uint16_t>(raw[0] >> 16)),
-                  bf16_to_f32(static_cast<uint16_t>(raw[1] & 0xFFFF)), bf16_to_f32(static_cast<uint16_t>(raw[1] >> 16))};
+                        uint16_t* __restrict__ vt, int Ns, int N, int H, RopeArgs ra, float qscale) {
+  constexpr int EPT = HD / 4;               // columns per thread
+  __shared__ uint16_t tile[64][HD + 2];
+  const int D = H * HD;
+  const int r0 = blockIdx.x * 64, b = blockIdx.z;
+  const int sec = blockIdx.y / H, head = blockIdx.y - sec * H;
+  const int t = threadIdx.x, rl = t >> 2, c0 = (t & 3) * EPT;
+  const int n = r0 + rl;
+  const int row = b * N + n;
+  uint16_t raw[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) raw[i] = 0;
+  if (n < N) {
+    const uint16_t* src = qkv + static_cast<size_t>(row) * 3 * D + sec * D + head * HD + c0;
+#pragma unroll
+    for (int i = 0; i < EPT / 8; ++i) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(src + 8 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        raw[8 * i + 2 * e] = static_cast<uint16_t>(w[e] & 0xFFFF);
+        raw[8 * i + 2 * e + 1] = static_cast<uint16_t>(w[e] >> 16);
+      }
+    }
+  }
+  if (sec < 2) {   // uniform over the workgroup
+    if (n >= N) return;
     int clip;
     const Thw g = rope_token(row, ra, &clip);
-    if (sec < 2) {
-      rope_pair<HD>(v[0], v[1], jj, g, ra.layout, ra.tab);
-      rope_pair<HD>(v[2], v[3], jj + 2, g, ra.layout, ra.tab);
-      if (sec == 0)
-        for (int i = 0; i < 4; ++i) v[i] *= qscale;
-      u32x2 pk;
-      pk[0] = pack_bf16x2(v[0], v[1]);
-      pk[1] = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<u32x2*>(qk + static_cast<size_t>(row) * 2 * D + col) = pk;
-    } else {
-      const int n = row - clip * ra.N;
-      uint16_t* dst = vt + (static_cast<size_t>(clip * (D / HD) + head) * HD + jj) * Ns + vt_pos(n);
-      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(i) * Ns] = f32_to_bf16(v[i]);
+    uint16_t* dst = qk + static_cast<size_t>(row) * 2 * D + sec * D + head * HD + c0;
+#pragma unroll
+    for (int i = 0; i < EPT / 8; ++i) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 8 * i + 2 * e;
+        float x0 = bf16_to_f32(raw[j]), x1 = bf16_to_f32(raw[j + 1]);
+        rope_pair<HD>(x0, x1, c0 + j, g, ra.layout, ra.tab);
+        if (sec == 0) {
+          x0 *= qscale;
+          x1 *= qscale;
+        }
+        w[e] = pack_bf16x2(x0, x1);
+      }
+      *reinterpret_cast<u32x4*>(dst + 8 * i) = w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) tile[rl][c0 + i] = raw[i];   // rows past N hold 0
+  __syncthreads();
+  for (int e = t; e < HD * 4; e += 256) {
+    const int d = e >> 2, grp = e & 3;
+    const int k0 = r0 + 16 * grp;
+    if (k0 >= N) continue;     // k0 + 16 <= Ns: Ns is at least N rounded up to 16
+    uint16_t w16[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) w16[vt_pos(k)] = tile[16 * grp + k][d];
+    uint16_t* dst = vt + (static_cast<size_t>(b * H + head) * HD + d) * Ns + k0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      u32x4 w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = static_cast<uint32_t>(w16[8 * i + 2 * q]) | (static_cast<uint32_t>(w16[8 * i + 2 * q + 1]) << 16);
+      *reinterpret_cast<u32x4*>(dst + 8 * i) = w;
     }
   }
 }
@@ -550,17 +605,15 @@ hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, i
                               const RopeSpec& r, const void* tab, float qscale, hipStream_t s,
                               int lead) {
   if (B <= 0 || N <= 0) return hipSuccess;
-  if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N)) return hipErrorInvalidValue;
-  const int D = n_head * head_dim;
+  if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N) || Ns % 16) return hipErrorInvalidValue;
+  if (B > 65535 || static_cast<long long>(B) * N >= (1LL << 31)) return hipErrorInvalidValue;
   const RopeArgs ra{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw, 0,
                     lead};
-  const long long M = static_cast<long long>(B) * N;
-  const long long total = M * (3 * D / 4);
-  const dim3 grid(static_cast<unsigned>(min(total, 256LL * 2048) / 256 + 1));
+  const dim3 grid((N + 63) / 64, 3 * n_head, B);
   if (head_dim == 64)
-    qkv_prepare_kernel<64><<<grid, 256, 0, s>>>(qkv, qk, vt, Ns, M, D, ra, qscale);
+    qkv_prepare_kernel<64><<<grid, 256, 0, s>>>(qkv, qk, vt, Ns, N, n_head, ra, qscale);
   else
-    qkv_prepare_kernel<32><<<grid, 256, 0, s>>>(qkv, qk, vt, Ns, M, D, ra, qscale);
+    qkv_prepare_kernel<32><<<grid, 256, 0, s>>>(qkv, qk, vt, Ns, N, n_head, ra, qscale);
   return hipGetLastError();
 }
 
