@@ -606,15 +606,26 @@ hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, i
                               int lead) {
   if (B <= 0 || N <= 0) return hipSuccess;
   if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N) || Ns % 16) return hipErrorInvalidValue;
-  if (B > 65535 || static_cast<long long>(B) * N >= (1LL << 31)) return hipErrorInvalidValue;
-  const RopeArgs ra{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw, 0,
-                    lead};
-  const dim3 grid((N + 63) / 64, 3 * n_head, B);
-  if (head_dim == 64)
-    qkv_prepare_kernel<64><<<grid, 256, 0, s>>>(qkv, qk, vt, Ns, N, n_head, ra, qscale);
-  else
-    qkv_prepare_kernel<32><<<grid, 256, 0, s>>>(qkv, qk, vt, Ns, N, n_head, ra, qscale);
-  return hipGetLastError();
+  if (static_cast<long long>(B) * N >= (1LL << 31)) return hipErrorInvalidValue;
+  const int D = n_head * head_dim;
+  // clips go to grid z, at most 65535 per launch
+  for (int b0 = 0; b0 < B; b0 += 65535) {
+    const int nb = min(B - b0, 65535);
+    const RopeArgs ra{static_cast<const float2*>(tab), ids, N, r.layout, r.gt * r.gh * r.gw, r.gh, r.gw,
+                      0, lead};
+    const size_t rows = static_cast<size_t>(b0) * N;
+    const dim3 grid((N + 63) / 64, 3 * n_head, nb);
+    uint16_t* vtb = vt + static_cast<size_t>(b0) * D * Ns;
+    if (head_dim == 64)
+      qkv_prepare_kernel<64><<<grid, 256, 0, s>>>(qkv + rows * 3 * D, qk + rows * 2 * D, vtb, Ns, N, n_head,
+                                                   ra, qscale);
+    else
+      qkv_prepare_kernel<32><<<grid, 256, 0, s>>>(qkv + rows * 3 * D, qk + rows * 2 * D, vtb, Ns, N, n_head,
+                                                   ra, qscale);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 static RopeFreq make_freq(int head_dim, float theta) {
