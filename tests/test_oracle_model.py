@@ -159,6 +159,22 @@ def test_vitl_tensor_and_parameter_counts():
     assert params == 325_971_328
 
 
+def test_vitb21_tensor_and_parameter_counts():
+    # the 2.1 ViT-B encoder (video and image embeddings, modality vectors) and the 2.1
+    # predictor (modality vectors, context projection) as built here; the checkpoint also
+    # holds three more hierarchical LayerNorms of the encoder (the final norm is the fourth;
+    # the hierarchical taps are not built) and stores each of the 8 mask tokens as its own
+    # tensor (one [8, 384] tensor here)
+    enc = synth.encoder_tensor_list(synth.WORKLOADS["vitb16_img384"]["enc"])
+    pred = synth.predictor_tensor_list(synth.WORKLOADS["vitb16_pred21"]["pred"])
+    g = GOLD["vitb21_counts"]
+    assert len(enc) + 3 * 2 == g["encoder_tensors"]
+    assert len(pred) + (8 - 1) == g["predictor_tensors"]
+    params = sum(int(np.prod(s)) for _, s, _ in enc + pred)
+    assert round(params / 1e6, 1) == g["params_millions_1dp"]
+    assert round((params + 3 * 2 * 768) / 1e6, 1) == g["params_millions_1dp"]
+
+
 @pytest.mark.parametrize("layout,ref_grid", [("tiled", 0), ("interleaved", 16)])
 def test_last_rows_restriction_equals_full_rows(layout, ref_grid):
     # the sampled-row evaluation used by the full-size parity tests returns exactly the
