@@ -5,10 +5,11 @@
 //
 // bf16 path (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //   * a workgroup of 8 wavefronts (2 per SIMD) computes 256 (rows of A) x 256, 192 or
-//     128 (rows of W) output tiles: the widest tile whose count fills whole rounds of
-//     the CUs, since the bytes a CU pulls from L2 per MFMA fall as the tile grows and
-//     the L2 -> LDS path, not the LDS or the MFMAs, limits the main loop; each wave
-//     owns a 128x64, 64x96 or 64x64 part of the tile as 32x32 blocks;
+//     128 (rows of W) output tiles, the width chosen by the rounds of the CUs its tiles
+//     need times the rows a tile streams per K slab: the bytes a CU pulls from L2 per
+//     MFMA fall as the tile grows, and the L2 -> LDS path, not the LDS or the MFMAs,
+//     limits the main loop; each wave owns a 128x64, 64x96 or 64x64 part of the tile as
+//     32x32 blocks;
 //   * the kernel is persistent: one workgroup per CU walks its tiles, and the 64-deep
 //     K-slabs of all its tiles form one stream through a ring of 2 or 3 LDS buffers,
 //     filled by global_load_lds_dwordx4 (HBM/L2 -> LDS, no register staging) up to
@@ -511,14 +512,25 @@ static hipError_t gemm_dispatch(const uint16_t* A, const uint16_t* W, const floa
                  : gemm_launch<C, EPI_STORE, false>(A, W, bias, Cp, M, N, K, s);
 }
 
-// The widest tile whose count still fills whole rounds of the CUs (fewer, larger tiles
-// cut the bytes each CU pulls through L2 per MFMA): 256 = 256 x 256, 192, else 128.
-static int tile_width(int M, int N) {
-  const int cus = num_cus();
-  const int tm = (M + 255) / 256;
-  if (N % 256 == 0 && tm * (N / 256) >= cus && (tm * (N / 256)) % cus == 0) return 256;
-  if (N % 192 == 0 && tm * (N / 192) >= cus && (tm * (N / 192)) % cus == 0) return 192;
-  return 128;
+// Width of the 256-row tile (256, 192 or 128, at most max_w): the one with the least
+// estimated time, taken as the rounds of the CUs the tiles need times the rows a tile
+// streams into LDS per K slab (256 + width), since the L2 -> LDS path bounds the main
+// loop; ties go to the wider tile.
+static int tile_width(int M, int N, int max_w = 256) {
+  const long long cus = num_cus();
+  const long long tm = (M + 255) / 256;
+  int best = 128;
+  long long best_cost = -1;
+  for (int w : {256, 192, 128}) {
+    if (w > max_w || N % w) continue;
+    const long long rounds = (tm * (N / w) + cus - 1) / cus;
+    const long long cost = rounds * (256 + w);
+    if (best_cost < 0 || cost < best_cost) {
+      best = w;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // Whether 256 x 128 tiles would be fewer than the CUs: then 128-row tiles are used.  The
@@ -574,7 +586,7 @@ hipError_t launch_gemm_bf16_qkv(const uint16_t* A, const uint16_t* W, const floa
   if (qe.ts > kMaxGridSide) return hipErrorInvalidValue;
   if (short_rows(M, Ncol)) return gemm_qkv_dispatch<Cfg128x128q>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
   // the 256 x 256 tile leaves too few registers for the RoPE epilogue
-  const int tw = tile_width(M, Ncol);
+  const int tw = tile_width(M, Ncol, 192);
   if (tw == 192) return gemm_qkv_dispatch<Cfg256x192>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
   return gemm_qkv_dispatch<Cfg256x128q>(A, W, bias, C, M, Ncol, K, head_dim, qe, s);
 }
