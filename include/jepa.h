@@ -83,7 +83,9 @@ const char* jepa_status_str(int status);
  * 2.1 ViT-B: 768/12/12/3072; patch 16, tubelet 2, 3 channels, ln_eps 1e-6,
  * rope_theta 10000.  head_dim = embed_dim / n_head must be 64 or 32. */
 typedef struct jepa_encoder_config {
-  int32_t embed_dim;      /* D, a multiple of 128 on the bf16 path, of 64 on fp32 */
+  int32_t embed_dim;      /* D, a multiple of 128 on the bf16 path, of 64 on fp32,
+                             and a LayerNorm width (see jepa_layernorm), else
+                             JEPA_ERR_ARG at creation                            */
   int32_t n_layer;        /* >= 0 (0: patch embedding (+ final norm) only)        */
   int32_t n_head;
   int32_t ffn_dim;        /* F, a multiple of 128 on the bf16 path                */
@@ -312,7 +314,8 @@ int jepa_rope3d(const void* x_dev, void* y_dev, int dtype, int B, int N, int n_h
 /* LayerNorm over rows ([Notes §1] eps; centred variance as the CPU backend of
  * [Parity "Parity on a GPU"]): x_dev fp32 [M, D]; weight/bias fp32 [D] (device);
  * out_dev [M, D] in out_dtype (may alias x_dev when out_dtype is F32).
- * D must be a multiple of 64 and at most 4096. */
+ * D = 64 * v with v in {1..6, 8, 10, 12, 16, 20, 22, 24, 32, 40, 48, 64}, else
+ * JEPA_ERR_SHAPE. */
 int jepa_layernorm(const float* x_dev, const float* weight_dev, const float* bias_dev,
                    int M, int D, float eps, void* out_dev, int out_dtype, void* stream);
 

@@ -12,7 +12,13 @@ tensor's index in a fixed name order):
   * LayerNorm weight 1 and bias 0 (``ln="identity"``), or, for parity tests that must
     see the affine terms, weight 1 + N(0, 0.1) and bias N(0, 0.1) (``ln="random"``);
   * for the bf16 workloads every drawn tensor is rounded once to bf16
-    (round-to-nearest-even) and handed to both sides as the same float32 values.
+    (round-to-nearest-even) and handed to both sides as the same float32 values;
+  * "sharp attention" variants (``qkv_scale`` s > 1) draw the fused q/k/v projection
+    weights with std 0.02 s (the same stream times s, before the bf16 rounding).  With
+    std 0.02 on width-1024 rows the attention scores have a std of about 0.4, the softmax
+    is almost flat and the attention branch is small next to the residual, so a wrong or
+    missing rotation barely moves the output; at s = 2 to 3 the scores spread over several
+    units and such mistakes show.
 """
 from __future__ import annotations
 
@@ -170,28 +176,33 @@ def _draw(kind: str, shape, g: np.random.Generator, ln: str) -> np.ndarray:
 
 
 def make_weights(tensors, seed: int, dtype: str = "bf16", ln: str = "identity",
-                 base_index: int = 1000) -> Dict[str, np.ndarray]:
+                 base_index: int = 1000, qkv_scale: float = 1.0) -> Dict[str, np.ndarray]:
     """Draw every tensor of ``tensors`` (from *_tensor_list).  float32 arrays; bf16-valued
-    when ``dtype == 'bf16'``."""
+    when ``dtype == 'bf16'``.  ``qkv_scale`` multiplies the draws of every
+    ``*.attn_qkv.weight`` before the rounding (sharp-attention variants)."""
     out = {}
     for k, (name, shape, kind) in enumerate(tensors):
         a = _draw(kind, shape, rng(seed, base_index + k), ln)
+        if qkv_scale != 1.0 and name.endswith(".attn_qkv.weight"):
+            a = (a * np.float32(qkv_scale)).astype(np.float32)
         if dtype == "bf16":
             a = round_to_bf16(a)
         out[name] = a
     return out
 
 
-def encoder_weights(s: EncoderShape, seed: int = 0, dtype: str = "bf16", ln: str = "identity"):
-    return make_weights(encoder_tensor_list(s), seed, dtype, ln, base_index=1000)
+def encoder_weights(s: EncoderShape, seed: int = 0, dtype: str = "bf16", ln: str = "identity",
+                    qkv_scale: float = 1.0):
+    return make_weights(encoder_tensor_list(s), seed, dtype, ln, base_index=1000, qkv_scale=qkv_scale)
 
 
 def head_weights(s: HeadShape, seed: int = 0, dtype: str = "bf16", ln: str = "identity"):
     return make_weights(head_tensor_list(s), seed, dtype, ln, base_index=9000)
 
 
-def predictor_weights(s: PredictorShape, seed: int = 0, dtype: str = "bf16", ln: str = "identity"):
-    return make_weights(predictor_tensor_list(s), seed, dtype, ln, base_index=5000)
+def predictor_weights(s: PredictorShape, seed: int = 0, dtype: str = "bf16", ln: str = "identity",
+                      qkv_scale: float = 1.0):
+    return make_weights(predictor_tensor_list(s), seed, dtype, ln, base_index=5000, qkv_scale=qkv_scale)
 
 
 # --------------------------------------------------------------------------- activations

@@ -44,12 +44,27 @@ def _enc_cfg(**kw):
     dict(patch=14), dict(tubelet=1), dict(in_chans=1), dict(rope_layout=2),
     dict(rope_ref_grid=1), dict(rope_ref_grid=-3), dict(max_rows=0), dict(compute=5),
     dict(ln_eps=0.0), dict(rope_theta=1.0), dict(n_layer=-1),
+    # width 896 (14 x 64) fits the GEMM tiles but has no LayerNorm instantiation
+    dict(embed_dim=896, n_head=14),
 ])
 def test_encoder_create_rejects_bad_config(bad):
     lib = J.load()
     h = ctypes.c_void_p()
     cfg = _enc_cfg(**bad)
     assert lib.jepa_encoder_create(ctypes.byref(cfg), ctypes.byref(h)) == _lib.JEPA_ERR_ARG
+    assert h.value is None
+
+
+def test_predictor_and_head_create_reject_unnormable_width():
+    lib = J.load()
+    h = ctypes.c_void_p()
+    pc = _lib.jepa_predictor_config(enc_dim=1024, embed_dim=896, n_layer=2, n_head=14, ffn_dim=1536,
+                                    n_mask_tokens=10, out_dim=1024, rope_layout=0, compute=1,
+                                    max_rows=64, ln_eps=1e-6, rope_theta=10000.0)
+    assert lib.jepa_predictor_create(ctypes.byref(pc), ctypes.byref(h)) == _lib.JEPA_ERR_ARG
+    hc = _lib.jepa_head_config(embed_dim=896, n_layer=1, n_head=14, ffn_dim=1536, n_classes=10,
+                               compute=1, max_rows=64, ln_eps=1e-6)
+    assert lib.jepa_head_create(ctypes.byref(hc), ctypes.byref(h)) == _lib.JEPA_ERR_ARG
     assert h.value is None
 
 
@@ -82,6 +97,9 @@ def test_standalone_ops_validate_before_launch():
     assert lib.jepa_layernorm(fake, fake, fake, 4, 100, 1e-6, fake, 0, None) == _lib.JEPA_ERR_SHAPE
     assert lib.jepa_layernorm(fake, fake, fake, 4, 8192, 1e-6, fake, 0, None) == _lib.JEPA_ERR_SHAPE
     assert lib.jepa_layernorm(fake, fake, fake, 4, 64 * 7, 1e-6, fake, 0, None) == _lib.JEPA_ERR_SHAPE
+    assert lib.jepa_layernorm(fake, fake, fake, 4, 896, 1e-6, fake, 0, None) == _lib.JEPA_ERR_SHAPE
+    # the ViT-g width (1408 = 22 x 64) is instantiated
+    assert lib.jepa_layernorm(fake, fake, fake, 0, 1408, 1e-6, fake, 0, None) == _lib.JEPA_OK
     # linear: bf16 tiles need N % 128 and K % 64; residual needs fp32 output
     assert lib.jepa_linear(fake, fake, None, fake, 4, 100, 64, 1, 0, 1, None) == _lib.JEPA_ERR_SHAPE
     assert lib.jepa_linear(fake, fake, None, fake, 4, 128, 60, 1, 0, 1, None) == _lib.JEPA_ERR_SHAPE

@@ -249,7 +249,7 @@ int check_widths(int compute, int D, int F, int n_head, int head_dim) {
   if (D <= 0 || F <= 0 || n_head <= 0) return JEPA_ERR_ARG;
   if (head_dim * n_head != D) return JEPA_ERR_ARG;
   if (head_dim != 64 && head_dim != 32) return JEPA_ERR_ARG;
-  if (D % 64 != 0 || D > 4096) return JEPA_ERR_ARG;  // LayerNorm kernel
+  if (!layernorm_width_ok(D)) return JEPA_ERR_ARG;  // LayerNorm kernel instantiations
   if (compute == JEPA_BF16 && (D % 128 != 0 || F % 128 != 0)) return JEPA_ERR_ARG;  // GEMM tiles
   if (compute == JEPA_F32 && (F % 4 != 0)) return JEPA_ERR_ARG;
   return JEPA_OK;
@@ -946,13 +946,7 @@ int jepa_layernorm(const float* x_dev, const float* weight_dev, const float* bia
   if (!x_dev || !weight_dev || !bias_dev || !out_dev) return JEPA_ERR_ARG;
   if (out_dtype != JEPA_F32 && out_dtype != JEPA_BF16) return JEPA_ERR_ARG;
   if (!(eps > 0.f)) return JEPA_ERR_ARG;
-  if (M < 0 || D <= 0 || D % 64 || D > 4096) return JEPA_ERR_SHAPE;
-  const int vpt = D / 64;
-  // the kernel is instantiated for these row lengths
-  static const int ok_vpt[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 40, 48, 64};
-  bool ok = false;
-  for (int v : ok_vpt) ok = ok || v == vpt;
-  if (!ok) return JEPA_ERR_SHAPE;
+  if (M < 0 || !layernorm_width_ok(D)) return JEPA_ERR_SHAPE;
   if (M == 0) return JEPA_OK;
   return hip_status(launch_layernorm(x_dev, weight_dev, bias_dev, M, D, eps, out_dev,
                                      out_dtype == JEPA_BF16, static_cast<hipStream_t>(stream)));

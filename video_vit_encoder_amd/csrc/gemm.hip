@@ -105,9 +105,14 @@ struct GemmCfg {
   static constexpr int B_LOADS = B_BYTES / 1024 / NWAVES;
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int LDS = STAGES * STAGE_BYTES;
+  // 1 KB bias slots, one per tile in flight: tile i's slot is rewritten for tile
+  // i + NBIAS, whose first slab is issued (NBIAS - 1) * K/64 >= STAGES slabs after tile
+  // i's last one, i.e. after a barrier that follows tile i's epilogue, for every K.
+  static constexpr int NBIAS = STAGES + 1;
+  static constexpr int BIAS_BYTES = NBIAS * 1024;
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && B_LOADS * NWAVES * 1024 == B_BYTES, "DMA split");
   static_assert(FI * 32 == WM && FJ * 32 == WN, "wave tile");
-  static_assert(STAGES >= 2 && STAGES <= 4 && LDS + 2048 <= 160 * 1024, "LDS ring");
+  static_assert(STAGES >= 2 && STAGES <= 4 && LDS + BIAS_BYTES <= 160 * 1024, "LDS ring");
   static_assert(BN <= 256, "bias slot of 1 KB");
   __device__ static int key(int r) { return lds_key128(r); }
 };
@@ -202,11 +207,12 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
       b_row[q] = static_cast<uint32_t>(static_cast<size_t>(n0 + r) * K * 2) + ((pslot ^ C::key(r)) << 4);
     }
   };
-  // LDS after the ring: [RoPE table of the QKV epilogue] [two 1 KB bias slots] [pair map of
-  // the QKV epilogue].  The bias columns of tile i go to slot i & 1 by one DMA of wave 0,
-  // issued just before the tile's first slab: every wait for that slab or a later one in
-  // wave 0 covers it, and the barrier after that wait publishes it.  The slot is rewritten
-  // for tile i + 2 only after barriers that follow tile i's epilogue in every wave.
+  // LDS after the ring: [RoPE table of the QKV epilogue] [NBIAS 1 KB bias slots] [pair map
+  // of the QKV epilogue].  The bias columns of tile i go to slot i % NBIAS by one DMA of
+  // wave 0, issued just before the tile's first slab: every wait for that slab or a later
+  // one in wave 0 covers it, and the barrier after that wait publishes it.  The slot is
+  // rewritten for tile i + NBIAS only after barriers that follow tile i's epilogue in
+  // every wave (see GemmCfg::NBIAS).
   const int tab_bytes = (EPI == EPI_QKV64 || EPI == EPI_QKV32) ? 3 * qe.ts * kLdsTabRow * 8 : 0;
   const uint32_t bias_base = smem_base + C::LDS + tab_bytes;
   const bool has_bias = bias != nullptr;
@@ -214,7 +220,8 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     const uint32_t st = smem_base + (s_iss % STAGES) * STAGE_BYTES;
     const uint32_t k0 = kt_iss * BK * 2;
     if (kt_iss == 0 && has_bias && wave == 0)
-      dma16(bias, static_cast<uint32_t>(n0_iss * 4 + min(lane, BN / 4 - 1) * 16), bias_base + (it_iss & 1) * 1024);
+      dma16(bias, static_cast<uint32_t>(n0_iss * 4 + min(lane, BN / 4 - 1) * 16),
+            bias_base + (it_iss % C::NBIAS) * 1024);
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) dma16(A, a_row[q] + k0, st + (q * NWAVES + wave) * 1024);
 #pragma unroll
@@ -274,7 +281,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     if (tid < HD / 2) {
       const RopePairIdx r = rope_pair_idx<HD>(2 * tid, qe.ra.layout);
       const int row0 = r.axis * qe.ts * kLdsTabRow;
-      reinterpret_cast<int4*>(smem + C::LDS + tab_bytes + 2048)[tid] =
+      reinterpret_cast<int4*>(smem + C::LDS + tab_bytes + C::BIAS_BYTES)[tid] =
           make_int4((row0 + r.i0) * 8, (row0 + r.i1) * 8, 8 * r.axis, 0);
     }
     float2* tabs = reinterpret_cast<float2*>(smem + C::LDS);
@@ -288,9 +295,9 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   // bias of the tile's columns c .. c + 3 (c relative to the tile) for tile it; without a
   // bias the slots hold zeros (written here, published by the prologue's barrier)
   if (!has_bias)
-    for (int e = tid; e < 512; e += C::NT) reinterpret_cast<float*>(smem + C::LDS + tab_bytes)[e] = 0.f;
+    for (int e = tid; e < C::BIAS_BYTES / 4; e += C::NT) reinterpret_cast<float*>(smem + C::LDS + tab_bytes)[e] = 0.f;
   auto bias4 = [&](int it, int c) __attribute__((always_inline)) {
-    return *reinterpret_cast<const f32x4*>(smem + C::LDS + tab_bytes + (it & 1) * 1024 + c * 4);
+    return *reinterpret_cast<const f32x4*>(smem + C::LDS + tab_bytes + (it % C::NBIAS) * 1024 + c * 4);
   };
   if (total > 0) set_rows(0);
 #pragma unroll
@@ -347,7 +354,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     if constexpr (EPI == EPI_QKV64 || EPI == EPI_QKV32) {
       constexpr int HD = EPI == EPI_QKV64 ? 64 : 32;
       const unsigned char* tabs = smem + C::LDS;
-      const int4* pmap = reinterpret_cast<const int4*>(smem + C::LDS + tab_bytes + 2048);
+      const int4* pmap = reinterpret_cast<const int4*>(smem + C::LDS + tab_bytes + C::BIAS_BYTES);
       uint32_t g[FI];   // the row's t, h, w packed by thw_pack
       int clip[FI], nn[FI];
 #pragma unroll
@@ -485,7 +492,7 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
                               int M, int N, int K, hipStream_t s, const QkvEpi& qe = QkvEpi{}) {
   constexpr bool QKV = EPI == EPI_QKV64 || EPI == EPI_QKV32;
   constexpr int MAX_LDS = 160 * 1024;
-  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kLdsTabRow * 8 + kPairMapBytes + 2048 <= MAX_LDS,
+  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kLdsTabRow * 8 + kPairMapBytes + C::BIAS_BYTES <= MAX_LDS,
                 "LDS for the RoPE table");
   static bool configured = false;
   if (!configured) {
@@ -494,7 +501,7 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int lds = C::LDS + (QKV ? 3 * qe.ts * kLdsTabRow * 8 + kPairMapBytes : 0) + 2048;
+  const int lds = C::LDS + (QKV ? 3 * qe.ts * kLdsTabRow * 8 + kPairMapBytes : 0) + C::BIAS_BYTES;
   const int tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
   const dim3 grid(min(tiles, num_cus()));
   gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, lds, s>>>(A, W, bias, Cp, M, N, K, qe);

@@ -30,6 +30,18 @@ hipError_t launch_gemv_f32(const float* A, const float* W, const float* bias, fl
                            int N, int K, hipStream_t s);
 hipError_t launch_layernorm(const float* x, const float* w, const float* b, int M, int D,
                             float eps, void* out, int out_bf16, hipStream_t s);
+// Row lengths the LayerNorm kernel is instantiated for: D = 64 * vpt with vpt in this list
+// (D = 1408, vpt 22, is the ViT-g width).
+inline bool layernorm_width_ok(int D) {
+  if (D <= 0 || D % 64) return false;
+  switch (D / 64) {
+    case 1: case 2: case 3: case 4: case 5: case 6: case 8: case 10: case 12: case 16:
+    case 20: case 22: case 24: case 32: case 40: case 48: case 64:
+      return true;
+    default:
+      return false;
+  }
+}
 hipError_t launch_rope3d(const void* x, void* y, int bf16, int B, int N, int n_head,
                          int head_dim, int64_t row_stride, const int32_t* ids,
                          const RopeSpec& r, hipStream_t s);

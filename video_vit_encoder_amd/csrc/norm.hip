@@ -5,6 +5,8 @@
 // passes run over the row held in registers, so HBM sees one read and one write.
 // Lane l owns the vector chunks l, l+64, l+128, ... of VEC floats each (VEC = 4 when
 // D is a multiple of 256, else 2 or 1), so every wave-wide access is contiguous.
+// The final norm of a forward runs in place (out == x), so x and out may alias: neither
+// is declared __restrict__.
 #include "common.h"
 #include "kernels.h"
 
@@ -12,8 +14,8 @@ namespace jepa {
 
 template <int VPT, int VEC, bool OUT_BF16>
 __global__ __launch_bounds__(256)
-void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
-                      const float* __restrict__ b, int M, float eps, void* __restrict__ out) {
+void layernorm_kernel(const float* x, const float* __restrict__ w,
+                      const float* __restrict__ b, int M, float eps, void* out) {
   constexpr int D = VPT * 64;
   constexpr int NV = VPT / VEC;
   const int lane = threadIdx.x & 63;
@@ -95,6 +97,7 @@ static hipError_t ln_dispatch(const float* x, const float* w, const float* b, in
 hipError_t launch_layernorm(const float* x, const float* w, const float* b, int M, int D,
                             float eps, void* out, int out_bf16, hipStream_t s) {
   if (M <= 0) return hipSuccess;
+  if (!layernorm_width_ok(D)) return hipErrorInvalidValue;
   switch (D / 64) {
     case 1: return ln_dispatch<1>(x, w, b, M, eps, out, out_bf16, s);
     case 2: return ln_dispatch<2>(x, w, b, M, eps, out, out_bf16, s);
@@ -107,6 +110,7 @@ hipError_t launch_layernorm(const float* x, const float* w, const float* b, int 
     case 12: return ln_dispatch<12>(x, w, b, M, eps, out, out_bf16, s);
     case 16: return ln_dispatch<16>(x, w, b, M, eps, out, out_bf16, s);
     case 20: return ln_dispatch<20>(x, w, b, M, eps, out, out_bf16, s);
+    case 22: return ln_dispatch<22>(x, w, b, M, eps, out, out_bf16, s);
     case 24: return ln_dispatch<24>(x, w, b, M, eps, out, out_bf16, s);
     case 32: return ln_dispatch<32>(x, w, b, M, eps, out, out_bf16, s);
     case 40: return ln_dispatch<40>(x, w, b, M, eps, out, out_bf16, s);
