@@ -368,6 +368,28 @@ int jepa_attention_block_causal(const void* qkv_dev, void* out_dev, int dtype, i
                                 float theta, int ref_grid, void* work_dev, size_t work_bytes,
                                 void* stream);
 
+/* Bytes of the per-GPU scratch array jepa_attention_noalloc works in (64 MiB). */
+#define JEPA_ATTN_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* jepa_attention for callers that cannot allocate device memory: code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * layouts, results and errors as jepa_attention minus the workspace: the bf16 path works
+ * in a file-scope device array of JEPA_ATTN_SCRATCH_BYTES that each GPU holds until the
+ * process ends, and the call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  The caller still owns qkv_dev and out_dev.
+ *   Limit: jepa_attention_workspace_size(dtype, B, N, n_head, head_dim) must not exceed
+ *   JEPA_ATTN_SCRATCH_BYTES (e.g. B*N*n_head*head_dim up to about 11 M elements), else
+ *   JEPA_ERR_SHAPE and nothing is enqueued.
+ *   Every call on one GPU shares that GPU's array and leaves its contents behind (no
+ *   state is read back: every byte a call reads was written earlier in the same call, or
+ *   is masked); two calls that overlap on one GPU (different streams, or host threads
+ *   without ordering) race on it.  The first call on a device looks up the array's
+ *   address there (hipGetSymbolAddress), with that device current.
+ * Errors: as jepa_attention; JEPA_ERR_HIP if the array's address cannot be found. */
+int jepa_attention_noalloc(const void* qkv_dev, void* out_dev, int dtype, int B, int N,
+                           int n_head, int head_dim, const int32_t* ids_dev, int gt, int gh,
+                           int gw, int layout, float theta, int ref_grid, void* stream);
+
 /* ------------------------------------------------------------------ kernel timing */
 
 /* Kernel classes of the forwards, for jepa_timing_end. */

@@ -15,7 +15,7 @@ import numpy as np
 from ._lib import (  # noqa: F401
     DTYPES, JEPA_BF16, JEPA_EPI_GELU, JEPA_EPI_RESIDUAL, JEPA_EPI_STORE, JEPA_F32, LAYOUTS,
     KERNEL_CLASSES, JepaError, header_functions, jepa_attention, jepa_attention_block_causal,
-    jepa_attention_workspace_size,
+    jepa_attention_noalloc, jepa_attention_workspace_size,
     jepa_encode, jepa_encode_image, jepa_encode_masked, jepa_encode_tokens, jepa_predict_mod,
     jepa_head_config, jepa_head_create, jepa_head_forward, jepa_head_free, jepa_head_set_tensor,
     jepa_pool_mean,

@@ -86,6 +86,7 @@ _SIGS = {
     "jepa_rope3d": ([_P, _P, _I, _I, _I, _I, _I, _I64, _P, _I, _I, _I, _I, _F, _I, _P], _I),
     "jepa_layernorm": ([_P, _P, _P, _I, _I, _F, _P, _I, _P], _I),
     "jepa_linear": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
+    "jepa_attention_noalloc": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _I, _I, _F, _I, _P], _I),
     "jepa_attention": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t,
                         _P], _I),
     "jepa_attention_workspace_size": ([_I, _I, _I, _I, _I], ctypes.c_size_t),
@@ -431,6 +432,24 @@ def jepa_attention(qkv, out, B: int, N: int, n_head: int, head_dim: int, ids,
            load().jepa_attention(_ptr(qkv), _ptr(out), dt, B, N, n_head, head_dim, _ptr(ids),
                                  gt, gh, gw, LAYOUTS[layout], theta, ref_grid, _ptr(work), wbytes,
                                  _stream(stream)))
+
+
+def jepa_attention_noalloc(qkv, out, B: int, N: int, n_head: int, head_dim: int, ids,
+                           grid: Sequence[int], layout: str, theta: float = 10000.0,
+                           ref_grid: int = 0, stream=None) -> None:
+    """jepa_attention without a workspace: the library's per-GPU scratch array is used
+    and nothing is allocated."""
+    import torch
+    dt = JEPA_BF16 if qkv.dtype == torch.bfloat16 else JEPA_F32
+    D = n_head * head_dim
+    _need(qkv.numel() == B * N * 3 * D and out.numel() == B * N * D and out.dtype == qkv.dtype,
+          "qkv [B*N, 3D] and out [B*N, D] of one dtype")
+    _need(ids is None or (ids.numel() >= N and ids.dtype == torch.int32), "ids must be int32 [N]")
+    gt, gh, gw = grid
+    _check("jepa_attention_noalloc",
+           load().jepa_attention_noalloc(_ptr(qkv), _ptr(out), dt, B, N, n_head, head_dim, _ptr(ids),
+                                         gt, gh, gw, LAYOUTS[layout], theta, ref_grid,
+                                         _stream(stream)))
 
 
 def jepa_attention_block_causal(qkv, out, B: int, n_cls: int, n_head: int, head_dim: int,

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1038,6 +1039,62 @@ int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, 
   const RopeSpec rs{gt, gh, gw, layout, theta, ref_grid};
   return attention_common(qkv_dev, out_dev, dtype, B, N, n_head, head_dim, ids_dev, rs, 0, 0,
                           work_dev, work_bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// Scratch of jepa_attention_noalloc: one array per GPU, alive until the process ends.  In
+// host code `attn_scratch` names a host-side stand-in, not device memory: kernels and
+// copies get the address hipGetSymbolAddress returns for the current device instead.
+static __device__ __align__(256) unsigned char attn_scratch[JEPA_ATTN_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch array, looked up once per device.
+int scratch_for_current_device(void** ptr) {
+  int dev = 0;
+  JEPA_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return JEPA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    JEPA_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(attn_scratch)));
+    if (!p) return JEPA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return JEPA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int jepa_attention_noalloc(const void* qkv_dev, void* out_dev, int dtype, int B, int N,
+                           int n_head, int head_dim, const int32_t* ids_dev, int gt, int gh,
+                           int gw, int layout, float theta, int ref_grid, void* stream) {
+  JEPA_TRY(attention_args(qkv_dev, out_dev, dtype, n_head, head_dim, layout, theta));
+  if (B < 0 || N < 0) return JEPA_ERR_SHAPE;
+  JEPA_TRY(check_grid(gt, gh, gw, ref_grid));
+  if (!ids_dev && static_cast<long long>(N) > static_cast<long long>(gt) * gh * gw) return JEPA_ERR_SHAPE;
+  if (B == 0 || N == 0) return JEPA_OK;
+  void* work = nullptr;
+  size_t work_bytes = 0;
+  if (dtype == JEPA_BF16) {
+    size_t a, b;
+    // a coarse bound first (6 bytes per q|k|v element), so that the exact size below
+    // cannot overflow
+    const double need = static_cast<double>(B) * N * n_head * head_dim * 6.0;
+    if (need > static_cast<double>(JEPA_ATTN_SCRATCH_BYTES)) return JEPA_ERR_SHAPE;
+    if (attn_ws_parts(B, N, n_head * head_dim, &a, &b) > JEPA_ATTN_SCRATCH_BYTES) return JEPA_ERR_SHAPE;
+    JEPA_TRY(scratch_for_current_device(&work));
+    work_bytes = JEPA_ATTN_SCRATCH_BYTES;
+  }
+  const RopeSpec rs{gt, gh, gw, layout, theta, ref_grid};
+  return attention_common(qkv_dev, out_dev, dtype, B, N, n_head, head_dim, ids_dev, rs, 0, 0,
+                          work, work_bytes, static_cast<hipStream_t>(stream));
 }
 
 int jepa_attention_block_causal(const void* qkv_dev, void* out_dev, int dtype, int B, int n_cls,
