@@ -110,9 +110,10 @@ struct GemmCfg {
   // i's last one, i.e. after a barrier that follows tile i's epilogue, for every K.
   static constexpr int NBIAS = STAGES + 1;
   static constexpr int BIAS_BYTES = NBIAS * 1024;
+  static constexpr int EXTRA = BIAS_BYTES;
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && B_LOADS * NWAVES * 1024 == B_BYTES, "DMA split");
   static_assert(FI * 32 == WM && FJ * 32 == WN, "wave tile");
-  static_assert(STAGES >= 2 && STAGES <= 4 && LDS + BIAS_BYTES <= 160 * 1024, "LDS ring");
+  static_assert(STAGES >= 2 && STAGES <= 4 && LDS + EXTRA <= 160 * 1024, "LDS ring");
   static_assert(BN <= 256, "bias slot of 1 KB");
   __device__ static int key(int r) { return lds_key128(r); }
 };
@@ -216,22 +217,34 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   const int tab_bytes = (EPI == EPI_QKV64 || EPI == EPI_QKV32) ? 3 * qe.ts * kLdsTabRow * 8 : 0;
   const uint32_t bias_base = smem_base + C::LDS + tab_bytes;
   const bool has_bias = bias != nullptr;
-  auto issue_next = [&]() {
-    const uint32_t st = smem_base + (s_iss % STAGES) * STAGE_BYTES;
-    const uint32_t k0 = kt_iss * BK * 2;
+  // One slab's copies in three parts, so that the copies can be spread between MFMAs:
+  // issue_begin (the tile's bias, before its first slab), issue_load(q) for q < LOADS (q <
+  // A_LOADS: 1 KB of A, else 1 KB of W), issue_end (advance to the next slab).
+  auto issue_begin = [&]() __attribute__((always_inline)) {
     if (kt_iss == 0 && has_bias && wave == 0)
       dma16(bias, static_cast<uint32_t>(n0_iss * 4 + min(lane, BN / 4 - 1) * 16),
             bias_base + (it_iss % C::NBIAS) * 1024);
-#pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) dma16(A, a_row[q] + k0, st + (q * NWAVES + wave) * 1024);
-#pragma unroll
-    for (int q = 0; q < B_LOADS; ++q)
-      dma16(W, b_row[q] + k0, st + A_BYTES + (q * NWAVES + wave) * 1024);
+  };
+  auto issue_load = [&](int q) __attribute__((always_inline)) {
+    const uint32_t st = smem_base + (s_iss % STAGES) * STAGE_BYTES;
+    const uint32_t k0 = kt_iss * BK * 2;
+    if (q < A_LOADS)
+      dma16(A, a_row[q] + k0, st + (q * NWAVES + wave) * 1024);
+    else
+      dma16(W, b_row[q - A_LOADS] + k0, st + A_BYTES + ((q - A_LOADS) * NWAVES + wave) * 1024);
+  };
+  auto issue_end = [&]() __attribute__((always_inline)) {
     ++s_iss;
     if (++kt_iss == KT) {
       kt_iss = 0;
       if (++it_iss < n_my) set_rows(it_iss);
     }
+  };
+  auto issue_next = [&]() {
+    issue_begin();
+#pragma unroll
+    for (int q = 0; q < C::LOADS; ++q) issue_load(q);
+    issue_end();
   };
 
   // fragment rows of this lane inside the A / W tiles (32x32x16 operand: row l%32,
@@ -255,14 +268,16 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   };
   // Wait until slab s_ has landed in LDS for every lane of the workgroup: the slabs
   // issued after it (at most STAGES - 2, fewer near the end) may stay in flight.
+  constexpr int PF1 = 0;
+  constexpr int PER = C::LOADS;
   auto wait_slab = [&](int s_) __attribute__((always_inline)) {
     const int ahead = min(s_iss - 1 - s_, STAGES - 2);
     if (ahead >= 2)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER + PF1) : "memory");
     else if (ahead == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER + PF1) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PF1) : "memory");
     __syncthreads();
   };
 
@@ -324,18 +339,34 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int cur = ks & 1, nxt = cur ^ 1;
+        bool spread = false;
         if (ks + 1 < KSTEPS) {
           load_frags(s, ks + 1, af[nxt], bfr[nxt]);
         } else if (s + 1 < total) {
           wait_slab(s + 1);
-          if (s_iss < total) issue_next();
           load_frags(s + 1, 0, af[nxt], bfr[nxt]);
+          spread = s_iss < total;
+          if (spread) issue_begin();
         }
+        // After a slab's barrier every wave has LOADS copies to issue; issued in one burst
+        // they queue at the address unit while the matrix core waits, so they go out one
+        // per MFMA of this k-step instead (the rest, if any, after the last MFMA).
 #pragma unroll
         for (int i = 0; i < FI; ++i)
 #pragma unroll
-          for (int j = 0; j < FJ; ++j)
+          for (int j = 0; j < FJ; ++j) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+            if (ks + 1 == KSTEPS && i * FJ + j < C::LOADS) {
+              __builtin_amdgcn_sched_barrier(0);
+              if (spread) issue_load(i * FJ + j);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        if (spread) {
+#pragma unroll
+          for (int q = FI * FJ; q < C::LOADS; ++q) issue_load(q);
+          issue_end();
+        }
         if (ks + 1 == KSTEPS) {
           // the fragments loaded above for slab s + 1 move into slot 0
 #pragma unroll
@@ -492,7 +523,7 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
                               int M, int N, int K, hipStream_t s, const QkvEpi& qe = QkvEpi{}) {
   constexpr bool QKV = EPI == EPI_QKV64 || EPI == EPI_QKV32;
   constexpr int MAX_LDS = 160 * 1024;
-  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kLdsTabRow * 8 + kPairMapBytes + C::BIAS_BYTES <= MAX_LDS,
+  static_assert(!QKV || C::LDS + 3 * kMaxGridSide * kLdsTabRow * 8 + kPairMapBytes + C::EXTRA <= MAX_LDS,
                 "LDS for the RoPE table");
   static bool configured = false;
   if (!configured) {
@@ -501,7 +532,7 @@ static hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, const float*
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int lds = C::LDS + (QKV ? 3 * qe.ts * kLdsTabRow * 8 + kPairMapBytes : 0) + C::BIAS_BYTES;
+  const int lds = C::LDS + (QKV ? 3 * qe.ts * kLdsTabRow * 8 + kPairMapBytes : 0) + C::EXTRA;
   const int tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
   const dim3 grid(min(tiles, num_cus()));
   gemm_bf16_kernel<C, EPI, OUT_F32><<<grid, C::NT, lds, s>>>(A, W, bias, Cp, M, N, K, qe);
