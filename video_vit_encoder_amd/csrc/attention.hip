@@ -156,6 +156,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int K_INS = K_BYTES / 1024, V_INS = V_BYTES / 1024;  // DMA instructions per tile
   constexpr int LOADS = (K_INS + V_INS) / NW;   // per wave and tile
   constexpr float TAU = 8.0f;
+  constexpr float kTwoTau = 256.0f;   // 2^TAU
   static_assert(LOADS * NW == K_INS + V_INS, "DMA split");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
@@ -370,56 +371,76 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           for (int i = 0; i < 16; ++i)
             if (kb + t2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3) >= N) sc[g][t2][i] = -INFINITY;
     }
-    // Row max of the tile relative to the running max, one wave-uniform decision for both
-    // groups: the first tile sets the running max to its exact max; later tiles move it
-    // only for queries whose tile max exceeds it by more than TAU.
-    float mxs[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      // a linear chain of 3-input maxima (v_max3_f32): half an op per score
-      float mx = fmaxf(sc[g][0][0], sc[g][1][0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, sc[g][0][i]), sc[g][1][i]);
-      mxs[g] = max_halves(mx);
-    }
-    if (t == 0 || __ballot(mxs[0] > TAU || mxs[1] > TAU) != 0) {
+    // P = exp2(S - m) rounded to bf16, with each lane's sum of its 32 bf16 values per group
+    // in two chains (v_dot2_f32_bf16 adds a pair per step).
+    float lt[2][2];
+    auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const float d = t == 0 ? mxs[g] : (mxs[g] > TAU ? mxs[g] : 0.f);
-        const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-d);
-        m_run[g] += d;
-        l_run[g] *= alpha;
+        lt[g][0] = 0.f;
+        lt[g][1] = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int ks = 0; ks < 4; ++ks) {
+          // slot s of k-step ks = element 8 (ks % 2) + s of sc[g][ks / 2]; each pair is
+          // converted as one bf16x2 value that feeds both the dot product and the word
+          u32x4 w;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[g][dt][i] *= alpha;
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[g][t2][i] -= d;
-      }
-    }
-    // P = exp2(S - m) in (0, 2^TAU], rounded to bf16; the row sum adds those bf16 values
-    // two at a time
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        // slot s of k-step ks = element 8 (ks % 2) + s of sc[g][ks / 2]; each pair is
-        // converted as one bf16x2 value that feeds both the dot product and the word
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 8 * (ks & 1) + 2 * e;
-          const f32x2 pp = {__builtin_amdgcn_exp2f(sc[g][ks >> 1][i]),
-                            __builtin_amdgcn_exp2f(sc[g][ks >> 1][i + 1])};
-          const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-          l_run[g] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_run[g], false);
-          w[e] = __builtin_bit_cast(uint32_t, pb);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 8 * (ks & 1) + 2 * e;
+            const f32x2 pp = {__builtin_amdgcn_exp2f(sc[g][ks >> 1][i]),
+                              __builtin_amdgcn_exp2f(sc[g][ks >> 1][i + 1])};
+            const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+            lt[g][e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lt[g][e & 1], false);
+            w[e] = __builtin_bit_cast(uint32_t, pb);
+          }
+          pf[g][ks] = __builtin_bit_cast(bf16x8, w);
         }
-        pf[g][ks] = __builtin_bit_cast(bf16x8, w);
       }
+    };
+    // The running max moves only when a score of the tile exceeds it by more than TAU (a
+    // factor 2^TAU), and the first tile sets it to the tile's exact max.  After the first
+    // tile the probabilities are formed against the running max straight away: a lane
+    // whose 32 values sum to at most 2^TAU has none above 2^TAU, so the max (a serial
+    // chain in front of every exp2) is taken only when some lane's sum exceeds that, and
+    // then exactly as for the first tile, with the probabilities formed again.
+    bool exact = t == 0;
+    if (!exact) {
+      probs();
+      exact = __ballot(lt[0][0] + lt[0][1] > kTwoTau || lt[1][0] + lt[1][1] > kTwoTau) != 0;
     }
+    if (exact) {
+      // Row max of the tile relative to the running max, one wave-uniform decision for
+      // both groups.
+      float mxs[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        // a linear chain of 3-input maxima (v_max3_f32): half an op per score
+        float mx = fmaxf(sc[g][0][0], sc[g][1][0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, sc[g][0][i]), sc[g][1][i]);
+        mxs[g] = max_halves(mx);
+      }
+      if (t == 0 || __ballot(mxs[0] > TAU || mxs[1] > TAU) != 0) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const float d = t == 0 ? mxs[g] : (mxs[g] > TAU ? mxs[g] : 0.f);
+          const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-d);
+          m_run[g] += d;
+          l_run[g] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[g][dt][i] *= alpha;
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[g][t2][i] -= d;
+        }
+      }
+      probs();
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) l_run[g] += lt[g][0] + lt[g][1];
   };
 
   // Matrix phase of tile t: P V of tile t - 1 and K Q of tile t at raised wave priority.

@@ -114,6 +114,7 @@ struct GemmCfg {
   static_assert(A_LOADS * NWAVES * 1024 == A_BYTES && B_LOADS * NWAVES * 1024 == B_BYTES, "DMA split");
   static_assert(FI * 32 == WM && FJ * 32 == WN, "wave tile");
   static_assert(STAGES >= 2 && STAGES <= 4 && LDS + EXTRA <= 160 * 1024, "LDS ring");
+  // the ping-pong groups (waves 0-3, 4-7) are the two row halves of the tile
   static_assert(BN <= 256, "bias slot of 1 KB");
   __device__ static int key(int r) { return lds_key128(r); }
 };
@@ -315,68 +316,8 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     return *reinterpret_cast<const f32x4*>(smem + C::LDS + tab_bytes + (it % C::NBIAS) * 1024 + c * 4);
   };
   if (total > 0) set_rows(0);
-#pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < total) issue_next();
-  bf16x8 af[2][FI], bfr[2][FJ];
-  if (total > 0) {
-    wait_slab(0);
-    // slab STAGES - 1 goes into the buffer no slab has used yet
-    if (s_iss < total) issue_next();
-    load_frags(0, 0, af[0], bfr[0]);
-  }
-  int s = 0;  // position in this workgroup's slab stream
-  for (int it = 0; it < n_my; ++it) {
-    f32x16 acc[FI][FJ];
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-    for (int kt = 0; kt < KT; ++kt, ++s) {
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int cur = ks & 1, nxt = cur ^ 1;
-        bool spread = false;
-        if (ks + 1 < KSTEPS) {
-          load_frags(s, ks + 1, af[nxt], bfr[nxt]);
-        } else if (s + 1 < total) {
-          wait_slab(s + 1);
-          load_frags(s + 1, 0, af[nxt], bfr[nxt]);
-          spread = s_iss < total;
-          if (spread) issue_begin();
-        }
-        // After a slab's barrier every wave has LOADS copies to issue; issued in one burst
-        // they queue at the address unit while the matrix core waits, so they go out one
-        // per MFMA of this k-step instead (the rest, if any, after the last MFMA).
-#pragma unroll
-        for (int i = 0; i < FI; ++i)
-#pragma unroll
-          for (int j = 0; j < FJ; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
-            if (ks + 1 == KSTEPS && i * FJ + j < C::LOADS) {
-              __builtin_amdgcn_sched_barrier(0);
-              if (spread) issue_load(i * FJ + j);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-        if (spread) {
-#pragma unroll
-          for (int q = FI * FJ; q < C::LOADS; ++q) issue_load(q);
-          issue_end();
-        }
-        if (ks + 1 == KSTEPS) {
-          // the fragments loaded above for slab s + 1 move into slot 0
-#pragma unroll
-          for (int i = 0; i < FI; ++i) af[0][i] = af[nxt][i];
-#pragma unroll
-          for (int j = 0; j < FJ; ++j) bfr[0][j] = bfr[nxt][j];
-        }
-      }
-    }
-
+  // Epilogue of tile it from the accumulators acc (one wave's blocks).
+  auto epilogue = [&](int it, f32x16 (&acc)[FI][FJ]) __attribute__((always_inline)) {
     // Epilogue of tile it.  acc[i][j] is the 32 (W rows) x 32 (A rows) block with lane
     // l, element e at W row 8*(e/4) + 4*(l/32) + e%4 and A row l%32: runs of four
     // consecutive output columns per lane.
@@ -458,7 +399,7 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
           }
         }
       }
-      continue;
+      return;
     }
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
@@ -503,6 +444,74 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
           store_row32_bf16(static_cast<uint16_t*>(Cv) + static_cast<size_t>(row) * N + n0 + wn * WN + j * 32, pk, h);
       }
     }
+  };
+  auto zero_acc = [&](f32x16 (&acc)[FI][FJ]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  };
+
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < total) issue_next();
+  bf16x8 af[2][FI], bfr[2][FJ];
+  if (total > 0) {
+    wait_slab(0);
+    // slab STAGES - 1 goes into the buffer no slab has used yet
+    if (s_iss < total) issue_next();
+    load_frags(0, 0, af[0], bfr[0]);
+  }
+  int s = 0;  // position in this workgroup's slab stream
+  for (int it = 0; it < n_my; ++it) {
+    f32x16 acc[FI][FJ];
+    zero_acc(acc);
+
+    for (int kt = 0; kt < KT; ++kt, ++s) {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        bool spread = false;
+        if (ks + 1 < KSTEPS) {
+          load_frags(s, ks + 1, af[nxt], bfr[nxt]);
+        } else if (s + 1 < total) {
+          wait_slab(s + 1);
+          load_frags(s + 1, 0, af[nxt], bfr[nxt]);
+          spread = s_iss < total;
+          if (spread) issue_begin();
+        }
+        // After a slab's barrier every wave has LOADS copies to issue; issued in one burst
+        // they queue at the address unit while the matrix core waits, so they go out one
+        // per MFMA of this k-step instead (the rest, if any, after the last MFMA).
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+          for (int j = 0; j < FJ; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+            if (ks + 1 == KSTEPS && i * FJ + j < C::LOADS) {
+              __builtin_amdgcn_sched_barrier(0);
+              if (spread) issue_load(i * FJ + j);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        if (spread) {
+#pragma unroll
+          for (int q = FI * FJ; q < C::LOADS; ++q) issue_load(q);
+          issue_end();
+        }
+        if (ks + 1 == KSTEPS) {
+          // the fragments loaded above for slab s + 1 move into slot 0
+#pragma unroll
+          for (int i = 0; i < FI; ++i) af[0][i] = af[nxt][i];
+#pragma unroll
+          for (int j = 0; j < FJ; ++j) bfr[0][j] = bfr[nxt][j];
+        }
+      }
+    }
+
+    epilogue(it, acc);
   }
 }
 
