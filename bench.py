@@ -1,7 +1,8 @@
 """Throughput of the V-JEPA 2 ViT-L/16 encoder forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--masked | --image | --head | --block-causal | --predictor [--v21]]
+                    [--masked | --image | --head | --block-causal | --predictor [--v21] |
+                     --vitb384 | --rope3d]
 
 One step is one jepa_encode call on a batch of 4 synthetic clips of 16 frames x 256x256
 uint8 (2048 tokens per clip, 8192 token rows), already resident in HBM: patch
@@ -44,6 +45,10 @@ uniform uint8 images of 384x384 (576 tokens each, 12 layers); ``value`` is image
 interpolated to 16, video modality vector) on one uniform uint8 clip of 64 frames x 384x384
 (18,432 tokens), where attention is about 80 % of the work; the oracle baseline times the
 clip's embedding and final norm and one block on its own, scaled to 12 blocks.
+
+``--rope3d`` measures the stand-alone 3-D RoPE (jepa_rope3d, fp32, out of place) on the q
+tensor of the ViT-L batch, [4, 2048, 16, 64] in the tiled layout: an HBM-bound kernel with
+8*B*N*H*hd algorithmic bytes per call; ``value`` is GB/s.
 
 ``--block-causal`` measures the block-causal attention with a CLS row
 (jepa_attention_block_causal) at the LeVJEPA ViT-L/16 shape: 8 clips of 1 + 16 x 14 x 14 =
@@ -199,8 +204,10 @@ def cpu_baseline(w, W, clips, budget_layers=12, ids0=None, direct=False):
         what = "blocks timed on N(0,1) rows, "
     return {"value": N / t_clip, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": (f"float64 numpy oracle, {what}clip 0 only ({N} tokens): embedding+norm "
-                       f"{t_fixed:.2f} s, {budget_layers} blocks {t_run - t_fixed:.2f} s; "
-                       f"scaled to {e.n_layer} blocks = {t_clip:.1f} s/clip")}
+                       f"{t_fixed:.2f} s, {budget_layers} of the {e.n_layer} blocks run and timed "
+                       f"({t_run - t_fixed:.2f} s); the other {e.n_layer - budget_layers} blocks are "
+                       f"not run but extrapolated at the measured per-block time, giving "
+                       f"{t_clip:.1f} s/clip; host CPU {host_cpu()}, numpy BLAS on {cores} threads")}
 
 
 def predictor_work(n_ctx, n_tgt, Denc, E, F, L, Dout):
@@ -606,6 +613,84 @@ def bench_image(args, B=16):
     print(json.dumps(res), flush=True)
 
 
+def host_cpu() -> str:
+    """The host CPU's model name (/proc/cpuinfo), for the baseline record."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bench_rope3d(args, B=4, N=2048, H=16, hd=64, grid=(8, 16, 16)):
+    """The stand-alone 3-D RoPE (jepa_rope3d), fp32, out of place, on the q tensor of the
+    ViT-L batch: [B, N, H, hd] rows, tiled layout on the clip's grid.  HBM-bound:
+    8*B*N*H*hd algorithmic bytes per call (fp32 read and write)."""
+    import torch
+    import oracle
+    import video_vit_encoder_amd as J
+
+    log(f"rope3d workload: fp32 [{B}, {N}, {H}, {hd}], tiled, grid {grid}")
+    dev = torch.device("cuda:0")
+    x_h = np.random.default_rng(args.seed).standard_normal((B, N, H, hd)).astype(np.float32)
+    x = torch.from_numpy(x_h).to(dev)
+    y = torch.empty_like(x)
+
+    def step():
+        J.jepa_rope3d(x, y, B, N, H, hd, H * hd, None, grid, "tiled")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    nbytes = 8 * B * N * H * hd
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # one launch per call: the step is the kernel
+    roof = {"kernel": "rope3d", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("rope3d"),
+            "launch_ms": round(ms, 5), "bytes_per_launch": nbytes}
+    log(f"{ms * 1e3:.1f} us/call, {gbs:,.0f} GB/s ({gbs / PEAK_HBM_GBS:.3f} of HBM)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle rope_rotate on clip 0)")
+        pos = oracle.rope_positions(np.arange(N), grid[1], grid[2], 0)
+        u = np.transpose(x_h[0], (1, 0, 2))               # [H, N, hd]
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.rope_rotate(u, pos, "tiled")
+            reps += 1
+            if time.perf_counter() - t0 > 10.0:
+                break
+        t = (time.perf_counter() - t0) / reps
+        cpu = {"value": round(8 * N * H * hd / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"float64 numpy oracle rope_rotate on clip 0 ([{H}, {N}, {hd}]), {reps} repetitions "
+                         f"in {time.perf_counter() - t0:.1f} s, bytes counted as the fp32 call's; "
+                         f"host CPU {host_cpu()}"}
+    res = {
+        "metric": "stand-alone 3-D RoPE HBM GB/s at 1 GPU (fp32 q of the ViT-L 4 x 2048-token batch); "
+                  "% HBM peak",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (N(0,1) fp32 head vectors)",
+        "config": {"workload": f"jepa_rope3d fp32 out of place on [{B}, {N}, {H}, {hd}] (4 clips x 2048 "
+                               "tokens x 16 heads x 64), tiled, grid 8x16x16, no interpolation",
+                   "batch_clips": B, "tokens_per_clip": N, "heads": H, "head_dim": hd},
+        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": nbytes,
+        "roofline": roof, "cpu_baseline": cpu, "kernels": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -630,6 +715,8 @@ def main():
     ap.add_argument("--masked", action="store_true",
                     help="time the masked-encoder forward on tube-mask contexts (512 of 2048 "
                          "tokens per clip) instead of the full forward")
+    ap.add_argument("--rope3d", action="store_true",
+                    help="time the stand-alone 3-D RoPE (jepa_rope3d, fp32) on the ViT-L q tensor")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy 3 times, the "
                          "reference for scaling HBM traffic counters")
@@ -650,6 +737,9 @@ def main():
         return
     if args.block_causal:
         bench_block_causal(args)
+        return
+    if args.rope3d:
+        bench_rope3d(args)
         return
 
     import torch

@@ -93,6 +93,31 @@ def test_rope3d_in_place_strided_and_layout_swap_fails():
     assert metrics.max_abs(got[..., D:2 * D], wrong) > 1e-2
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope3d_pair_path_unaligned_rows_and_head_dim_6(dtype):
+    # rows starting 2 elements past an aligned address, and a head dim (6: 2 rotated dims
+    # per axis, no pass-through) that is not a multiple of 4, take the pair-at-a-time path
+    import torch
+    banner("rope3d pair path", dtype)
+    for hd, off in ((64, 2), (6, 0)):
+        grid, H, B = (3, 5, 6), 3, 2
+        N = 90
+        D = H * hd
+        x = synth.normal(4, (B * N * D + 2,), k=22)
+        if dtype == "bf16":
+            x = synth.round_to_bf16(x)
+        xd = (bf16 if dtype == "bf16" else f32)(x)
+        yd = torch.zeros_like(xd)
+        J.jepa_rope3d(xd[off:], yd[off:], B, N, H, hd, D, None, grid, "interleaved", ref_grid=16)
+        got = host(yd)[off:off + B * N * D].reshape(B, N, D)
+        ref = _rope_ref(x[off:off + B * N * D].astype(np.float64).reshape(B, N, D), B, N, H, hd,
+                        np.arange(N), grid, "interleaved", 16)
+        if dtype == "bf16":
+            assert np.all(np.abs(got - ref) <= BF16_ULP * np.abs(ref) + 1e-6), hd
+        else:
+            assert metrics.max_abs(got, ref) <= ROPE_F32_MAX_ABS, hd
+
+
 def test_rope3d_bf16():
     banner("rope3d bf16")
     grid, H, hd, B = (8, 16, 16), 16, 64, 1

@@ -19,7 +19,11 @@ struct RopeOmega {
   double w[16];
 };
 
-template <bool BF16>
+// VEC: each lane moves 4 consecutive elements (two pairs) per access, 16 bytes (fp32) or 8
+// (bf16), and issues the loads of up to 4 such chunks before rotating any, so that a wave
+// keeps several kilobytes in flight (rows 16-byte aligned, head dim a multiple of 4);
+// otherwise one pair per access.
+template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256)
 void rope3d_kernel(const void* __restrict__ xv, void* __restrict__ yv, long long n_tok, int N,
                    int n_head, int hd, long long row_stride, const int32_t* __restrict__ ids,
@@ -52,9 +56,71 @@ void rope3d_kernel(const void* __restrict__ xv, void* __restrict__ yv, long long
   }
   __syncthreads();
   if (!valid) return;
+  const long long base = tok * row_stride;
+  // rotation of the pair (x0, x1) at dims (j, j + 1) of a head, j even
+  auto rot = [&](float& x0, float& x1, int j) __attribute__((always_inline)) {
+    if (j < 3 * d) {
+      const int a = j / d, jl = j - a * d;
+      int i0, i1;
+      if (r.layout == 0) {
+        i0 = jl % m;
+        i1 = (jl + 1) % m;
+      } else {
+        i0 = i1 = jl >> 1;
+      }
+      const float c0 = tab[wave][a * m + i0][0], s0 = tab[wave][a * m + i0][1];
+      const float c1 = tab[wave][a * m + i1][0], s1 = tab[wave][a * m + i1][1];
+      const float y0 = x0 * c0 - x1 * s0;
+      const float y1 = x1 * c1 + x0 * s1;
+      x0 = y0;
+      x1 = y1;
+    }
+  };
+  if constexpr (VEC) {
+    // 4-element chunk c: elements 4c .. 4c + 3 of the token's row
+    const int nch = n_head * hd / 4;
+  auto load4 = [&](int c, float (&v)[4]) __attribute__((always_inline)) {
+    const long long off = base + 4LL * c;
+    if constexpr (BF16) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(xv) + off);
+      v[0] = bf16_to_f32(static_cast<uint16_t>(w[0] & 0xFFFF));
+      v[1] = bf16_to_f32(static_cast<uint16_t>(w[0] >> 16));
+      v[2] = bf16_to_f32(static_cast<uint16_t>(w[1] & 0xFFFF));
+      v[3] = bf16_to_f32(static_cast<uint16_t>(w[1] >> 16));
+    } else {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(static_cast<const float*>(xv) + off);
+      v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+    }
+  };
+    for (int c0 = lane; c0 < nch; c0 += 4 * 64) {
+      float v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c0 + 64 * u < nch) load4(c0 + 64 * u, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < nch) {
+          const int e4 = 4 * c;
+          const int j = e4 - (e4 / hd) * hd;
+          rot(v[u][0], v[u][1], j);
+          rot(v[u][2], v[u][3], j + 2);
+          const long long off = base + 4LL * c;
+          if constexpr (BF16) {
+            u32x2 w;
+            w[0] = pack_bf16x2(v[u][0], v[u][1]);
+            w[1] = pack_bf16x2(v[u][2], v[u][3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(yv) + off) = w;
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(yv) + off) = f32x4{v[u][0], v[u][1], v[u][2], v[u][3]};
+          }
+        }
+      }
+    }
+    return;
+  }
   const int half = hd / 2;
   const int npairs = n_head * half;
-  const long long base = tok * row_stride;
   for (int pi = lane; pi < npairs; pi += 64) {
     const int e = pi / half;
     const int j = 2 * (pi - e * half);
@@ -70,20 +136,7 @@ void rope3d_kernel(const void* __restrict__ xv, void* __restrict__ yv, long long
       x1 = t.y;
     }
     float y0 = x0, y1 = x1;
-    if (j < 3 * d) {
-      const int a = j / d, jl = j - a * d;
-      int i0, i1;
-      if (r.layout == 0) {
-        i0 = jl % m;
-        i1 = (jl + 1) % m;
-      } else {
-        i0 = i1 = jl >> 1;
-      }
-      const float c0 = tab[wave][a * m + i0][0], s0 = tab[wave][a * m + i0][1];
-      const float c1 = tab[wave][a * m + i1][0], s1 = tab[wave][a * m + i1][1];
-      y0 = x0 * c0 - x1 * s0;
-      y1 = x1 * c1 + x0 * s1;
-    }
+    rot(y0, y1, j);
     if constexpr (BF16) {
       *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(yv) + off) = pack_bf16x2(y0, y1);
     } else {
@@ -101,10 +154,17 @@ hipError_t launch_rope3d(const void* x, void* y, int bf16, int B, int N, int n_h
   RopeOmega om{};
   for (int k = 0; k < m && k < 16; ++k) om.w[k] = 1.0 / pow(static_cast<double>(r.theta), static_cast<double>(k) / m);
   const dim3 grid(static_cast<unsigned>((n_tok + 3) / 4));
-  if (bf16)
-    rope3d_kernel<true><<<grid, 256, 0, s>>>(x, y, n_tok, N, n_head, head_dim, row_stride, ids, r, om);
-  else
-    rope3d_kernel<false><<<grid, 256, 0, s>>>(x, y, n_tok, N, n_head, head_dim, row_stride, ids, r, om);
+  // 16-byte (fp32) or 8-byte (bf16) accesses need aligned rows and whole 4-element chunks
+  const uintptr_t align = bf16 ? 8 : 16;
+  const bool vec = head_dim % 4 == 0 && row_stride % 4 == 0 && reinterpret_cast<uintptr_t>(x) % align == 0 &&
+                   reinterpret_cast<uintptr_t>(y) % align == 0;
+  if (bf16) {
+    if (vec) rope3d_kernel<true, true><<<grid, 256, 0, s>>>(x, y, n_tok, N, n_head, head_dim, row_stride, ids, r, om);
+    else rope3d_kernel<true, false><<<grid, 256, 0, s>>>(x, y, n_tok, N, n_head, head_dim, row_stride, ids, r, om);
+  } else {
+    if (vec) rope3d_kernel<false, true><<<grid, 256, 0, s>>>(x, y, n_tok, N, n_head, head_dim, row_stride, ids, r, om);
+    else rope3d_kernel<false, false><<<grid, 256, 0, s>>>(x, y, n_tok, N, n_head, head_dim, row_stride, ids, r, om);
+  }
   return hipGetLastError();
 }
 
