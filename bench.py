@@ -18,8 +18,8 @@ on the stream the library launches on, bracketed by device synchronisation).  Be
     forwards in which the library records a HIP event pair around every launch on the
     stream it launches on (jepa_timing_begin / jepa_timing_end);
   * ``kernels``: the same figures for every kernel class of the step;
-  * ``cpu_baseline``: the float64 oracle timed on the host on one clip through a few
-    layers, scaled to the 24-layer forward (a reported baseline, not a target).
+  * ``cpu_baseline``: the float64 oracle timed on the host on one clip, the whole 24-layer
+    forward end to end (a reported baseline, not a target).
 
 ``--masked`` measures the masked-encoder forward instead (jepa_encode_masked, the
 pre-training path): the same clips, each with the context of a seeded tube mask (an 8x8
@@ -161,12 +161,13 @@ def measured_traffic(kind):
     return ent["read_bytes"] + ent["write_bytes"]
 
 
-def cpu_baseline(w, W, clips, budget_layers=12, ids0=None, direct=False):
-    """The float64 oracle on clip 0: patch embedding + final norm alone, then with
-    ``budget_layers`` blocks; the per-block time scales the forward to all its blocks.  With
-    ``ids0`` the masked forward on those context tokens.  ``direct``: the blocks are timed on
-    their own (oracle.encode_tokens on N(0,1) rows of the clip's grid), for clips whose
-    embedding takes longer than a block."""
+def cpu_baseline(w, W, clips, budget_layers=None, ids0=None, direct=False):
+    """The float64 oracle on clip 0.  By default the whole forward (embedding, every block,
+    final norm) is run and timed end to end.  With ``budget_layers``: the patch embedding +
+    final norm alone, then with that many blocks, the per-block time scaling the forward to
+    all its blocks.  With ``ids0`` the masked forward on those context tokens.  ``direct``:
+    the blocks are timed on their own (oracle.encode_tokens on N(0,1) rows of the clip's
+    grid), for clips whose embedding takes longer than a block."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -184,6 +185,17 @@ def cpu_baseline(w, W, clips, budget_layers=12, ids0=None, direct=False):
             return oracle.encoder_forward(clips[0], W, spec(n))
         return oracle.masked_encoder_forward(clips[0], W, spec(n), ids0)
 
+    N = w["grid"][0] * w["grid"][1] * w["grid"][2] if ids0 is None else len(ids0)
+    what = "masked forward, " if ids0 is not None else ""
+    if budget_layers is None and not direct:
+        t0 = time.perf_counter()
+        run(e.n_layer)
+        t_clip = time.perf_counter() - t0
+        return {"value": N / t_clip, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+                "sample": (f"float64 numpy oracle, {what}clip 0 only ({N} tokens): the whole "
+                           f"forward (embedding, all {e.n_layer} blocks, final norm) run and timed "
+                           f"end to end, {t_clip:.1f} s; host CPU {host_cpu()}, numpy BLAS on "
+                           f"{cores} threads")}
     t0 = time.perf_counter()
     run(0)
     t_fixed = time.perf_counter() - t0
@@ -198,8 +210,6 @@ def cpu_baseline(w, W, clips, budget_layers=12, ids0=None, direct=False):
         t_run = time.perf_counter() - t0
     t_layer = max(t_run - t_fixed, 1e-9) / budget_layers
     t_clip = t_fixed + e.n_layer * t_layer
-    N = w["grid"][0] * w["grid"][1] * w["grid"][2] if ids0 is None else len(ids0)
-    what = "masked forward, " if ids0 is not None else ""
     if direct:
         what = "blocks timed on N(0,1) rows, "
     return {"value": N / t_clip, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
