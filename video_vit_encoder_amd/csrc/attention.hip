@@ -352,13 +352,17 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       if (__ballot(kb + BKV > lim[0] || kb + BKV > lim[1] || kb < lo[0] || kb < lo[1]) != 0) {
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const uint32_t span = static_cast<uint32_t>(lim[g] - lo[g]);
+          // key k = kb + 4h + c (c the element's constant offset) is outside [lo, lim) iff
+          // k - lo or lim - 1 - k is negative: the sign of their OR picks -inf or +inf as
+          // the bound of a minimum, with no lane mask
+          const int a = kb + 4 * h - lo[g], bb = lim[g] - 1 - kb - 4 * h;
 #pragma unroll
           for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int key = kb + t2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-              if (static_cast<uint32_t>(key - lo[g]) >= span) sc[g][t2][i] = -INFINITY;
+              const int c = t2 * 32 + 8 * (i >> 2) + (i & 3);
+              const uint32_t sgn = static_cast<uint32_t>((a + c) | (bb - c)) & 0x80000000u;
+              sc[g][t2][i] = fminf(sc[g][t2][i], __uint_as_float(sgn | 0x7f800000u));
             }
         }
       }
