@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--masked | --image | --head | --block-causal | --predictor [--v21] |
-                     --vitb384 | --rope3d]
+                     --chain | --vitb384 | --rope3d]
 
 One step is one jepa_encode call on a batch of 4 synthetic clips of 16 frames x 256x256
 uint8 (2048 tokens per clip, 8192 token rows), already resident in HBM: patch
@@ -33,6 +33,10 @@ target tokens/s.  ``--predictor --v21`` runs the V-JEPA 2.1 ViT-B predictor inst
 8 mask tokens, output 1664, interleaved RoPE, modality vector on every row, context rows
 projected too) on the 8x24x24 grid of a 16-frame 384-px clip with the tube mask's 512
 context and 4096 target ids.
+
+``--chain`` measures configuration 5 as one step: the ViT-L/16 encoder on one 64-frame
+256-px clip (8192 tokens, 24 layers), then the masked predictor on that output (the tube
+mask's 2048 context and 6144 target ids); ``value`` is clip tokens/s through both.
 
 ``--head`` measures the attentive-pool classifier head of the V-JEPA 2 SSv2 classifier (3
 pool blocks, 16 heads, 174 classes) on 4 token maps of 2048 x 1024 (N(0,1) rows standing in
@@ -344,6 +348,124 @@ def bench_predictor(args):
         "config": {"workload": wl,
                    "context_tokens": n_ctx, "target_tokens": n_tgt, "embed_dim": p.embed_dim,
                    "layers": p.n_layer, "heads": p.n_head, "ffn_dim": p.ffn_dim},
+        "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": flops, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_chain(args):
+    """Configuration 5 as one step: the V-JEPA 2 ViT-L/16 encoder on one 64-frame 256-px clip
+    (32 x 16 x 16 = 8192 tokens, 24 layers), then the masked predictor on that output (the
+    seeded tube mask's 2048 context and 6144 target ids, 12 blocks at width 384, head dim 32).
+    ``value`` is clip tokens/s through both."""
+    import torch
+    import synth
+    import video_vit_encoder_amd as J
+
+    w = synth.workload("vitl16_64f256_pred")
+    e, p = w["enc"], w["pred"]
+    grid = w["grid"]
+    N = grid[0] * grid[1] * grid[2]
+    log(f"chain workload: 1 clip x {w['frames']} x {w['size']}^2 -> {N} tokens, encoder {e.n_layer} "
+        f"blocks, predictor {p.n_layer} blocks; drawing weights")
+    W = synth.encoder_weights(e, seed=args.seed, dtype="bf16")
+    Wp = synth.predictor_weights(p, seed=args.seed, dtype="bf16")
+    clips = synth.clip_u8(args.seed, 1, w["frames"], w["size"], w["size"])
+    ids_ctx, ids_tgt = synth.tube_mask(args.seed, *grid)
+    dev = torch.device("cuda:0")
+    enc = J.Encoder(e.embed_dim, e.n_layer, e.n_head, e.ffn_dim, dtype="bf16", max_rows=N)
+    enc.set_weights(W)
+    pred = J.Predictor(p.enc_dim, p.embed_dim, p.n_layer, p.n_head, p.ffn_dim, p.n_mask_tokens,
+                       p.out_dim, dtype="bf16", max_rows=len(ids_ctx) + len(ids_tgt))
+    pred.set_weights(Wp)
+    clip_d = torch.from_numpy(clips).to(dev)
+    ic = torch.from_numpy(ids_ctx.astype(np.int32)).to(dev)
+    it = torch.from_numpy(ids_tgt.astype(np.int32)).to(dev)
+    z = torch.empty((1, N, e.embed_dim), dtype=torch.float32, device=dev)
+    out = torch.empty((len(ids_tgt), p.out_dim), dtype=torch.float32, device=dev)
+
+    def step():
+        enc.encode(clip_d, out=z)
+        pred.predict(z[0], ic, it, w["mask_index"], grid, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("non-finite chain output")
+    n_ctx, n_tgt = len(ids_ctx), len(ids_tgt)
+    work = kernel_work(1, N, e.embed_dim, e.ffn_dim, e.n_layer)
+    for name, (bound, v) in predictor_work(n_ctx, n_tgt, p.enc_dim, p.embed_dim, p.ffn_dim,
+                                           p.n_layer, p.out_dim).items():
+        work[name] = (bound, work[name][1] + v)
+    flops = sum(v for b, v in work.values() if b == "mfma")
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{ms:.3f} ms/step, {N / (ms * 1e-3):,.0f} clip tokens/s, {tflops:.1f} TFLOP/s")
+    roof, kernels = None, None
+    if not args.no_kernels:
+        kernels, _ = kernel_timing(J, step, args.steps, work)
+        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+        k = kernels[dom]
+        roof = {"kernel": dom, "bound": k["bound"], "achieved": k.get("tflops", k.get("gbs")),
+                "peak": PEAK_BF16_TFLOPS if k["bound"] == "mfma" else PEAK_HBM_GBS,
+                "unit": "TFLOP/s" if k["bound"] == "mfma" else "GB/s", "frac": k["frac"],
+                "traffic": None, "launch_ms": k["avg_ms"]}
+        log(f"dominant kernel {dom}: {k['avg_ms'] * 1e3:.1f} us/launch, frac {k['frac']:.3f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline (oracle: encoder embedding + 1 block, predictor 0 and 1 blocks, scaled)")
+        spec = oracle.EncoderSpec(e.embed_dim, 1, e.n_head, e.ffn_dim)
+        t0 = time.perf_counter()
+        zo = oracle.encoder_forward(clips[0], W, spec)
+        t_enc1 = time.perf_counter() - t0
+        spec0 = oracle.EncoderSpec(e.embed_dim, 0, e.n_head, e.ffn_dim)
+        t0 = time.perf_counter()
+        oracle.encoder_forward(clips[0], W, spec0)
+        t_enc0 = time.perf_counter() - t0
+        t_enc = t_enc0 + e.n_layer * max(t_enc1 - t_enc0, 1e-9)
+
+        def pspec(n):
+            return oracle.PredictorSpec(p.enc_dim, p.embed_dim, n, p.n_head, p.ffn_dim,
+                                        p.n_mask_tokens, p.out_dim)
+        t0 = time.perf_counter()
+        oracle.predictor_forward(zo, Wp, pspec(0), ids_ctx, ids_tgt, w["mask_index"], grid)
+        t_p0 = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.predictor_forward(zo, Wp, pspec(1), ids_ctx, ids_tgt, w["mask_index"], grid)
+        t_p1 = time.perf_counter() - t0
+        t_pred = t_p0 + p.n_layer * max(t_p1 - t_p0, 1e-9)
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([q.get("num_threads", 1) for q in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        cpu = {"value": N / (t_enc + t_pred), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+               "sample": (f"float64 numpy oracle: encoder embedding+norm {t_enc0:.1f} s and one block "
+                          f"{t_enc1 - t_enc0:.1f} s run, scaled to {e.n_layer} blocks = {t_enc:.0f} s; "
+                          f"predictor without blocks {t_p0:.1f} s and one block {t_p1 - t_p0:.1f} s run, "
+                          f"scaled to {p.n_layer} blocks = {t_pred:.0f} s; the other blocks are not run; "
+                          f"host CPU {host_cpu()}, numpy BLAS on {cores} threads")}
+    res = {
+        "metric": ("encoder + predictor clip tokens/sec at 1 GPU (V-JEPA 2 ViT-L/16 on a 64-frame "
+                   "256-px clip, then the masked predictor); % bf16 MFMA peak"),
+        "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (uniform uint8 clip, random N(0,0.02) bf16 weights, seeded tube mask)",
+        "config": {"workload": ("V-JEPA 2 ViT-L/16 encoder on 1 clip x 64 x 256x256 (8192 tokens, 24 "
+                                "layers), then the masked predictor on its output: 2048 context + 6144 "
+                                "target rows, width 384, 12 heads of 32, 12 blocks, bf16 MFMA"),
+                   "clips": 1, "tokens": N, "context_tokens": n_ctx, "target_tokens": n_tgt},
+        "clips_per_s": round(1.0 / (ms * 1e-3), 2),
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "flops_per_step": flops, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
     }
@@ -713,6 +835,9 @@ def main():
                     help="time the masked predictor (jepa_predict) on its 8192-token workload")
     ap.add_argument("--v21", action="store_true",
                     help="with --predictor: the V-JEPA 2.1 ViT-B predictor (jepa_predict_mod)")
+    ap.add_argument("--chain", action="store_true",
+                    help="time configuration 5 as one step: the ViT-L encoder on one 64-frame "
+                         "256-px clip (8192 tokens), then the masked predictor on its output")
     ap.add_argument("--head", action="store_true",
                     help="time the attentive-pool classifier head on 4 ViT-L token maps")
     ap.add_argument("--image", action="store_true",
@@ -736,6 +861,9 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    if args.chain:
+        bench_chain(args)
+        return
     if args.predictor:
         bench_predictor(args)
         return
