@@ -34,9 +34,9 @@ target tokens/s.  ``--predictor --v21`` runs the V-JEPA 2.1 ViT-B predictor inst
 projected too) on the 8x24x24 grid of a 16-frame 384-px clip with the tube mask's 512
 context and 4096 target ids.
 
-``--chain`` measures configuration 5 as one step: the ViT-L/16 encoder on one 64-frame
-256-px clip (8192 tokens, 24 layers), then the masked predictor on that output (the tube
-mask's 2048 context and 6144 target ids); ``value`` is clip tokens/s through both.
+``--chain`` measures the encoder + predictor chain as one step: the ViT-L/16 encoder on one
+64-frame 256-px clip (8192 tokens, 24 layers), then the masked predictor on that output (the
+tube mask's 2048 context and 6144 target ids); ``value`` is clip tokens/s through both.
 
 ``--head`` measures the attentive-pool classifier head of the V-JEPA 2 SSv2 classifier (3
 pool blocks, 16 heads, 174 classes) on 4 token maps of 2048 x 1024 (N(0,1) rows standing in
@@ -355,7 +355,7 @@ def bench_predictor(args):
 
 
 def bench_chain(args):
-    """Configuration 5 as one step: the V-JEPA 2 ViT-L/16 encoder on one 64-frame 256-px clip
+    """The encoder + predictor chain as one step: the V-JEPA 2 ViT-L/16 encoder on one 64-frame 256-px clip
     (32 x 16 x 16 = 8192 tokens, 24 layers), then the masked predictor on that output (the
     seeded tube mask's 2048 context and 6144 target ids, 12 blocks at width 384, head dim 32).
     ``value`` is clip tokens/s through both."""
@@ -836,8 +836,8 @@ def main():
     ap.add_argument("--v21", action="store_true",
                     help="with --predictor: the V-JEPA 2.1 ViT-B predictor (jepa_predict_mod)")
     ap.add_argument("--chain", action="store_true",
-                    help="time configuration 5 as one step: the ViT-L encoder on one 64-frame "
-                         "256-px clip (8192 tokens), then the masked predictor on its output")
+                    help="time the ViT-L encoder on one 64-frame 256-px clip (8192 tokens), "
+                         "then the masked predictor on its output, as one step")
     ap.add_argument("--head", action="store_true",
                     help="time the attentive-pool classifier head on 4 ViT-L token maps")
     ap.add_argument("--image", action="store_true",
