@@ -339,7 +339,8 @@ int jepa_linear(const void* A_dev, const void* W_dev, const float* bias_dev, voi
  * uses the same kernel with the rotation done by the QKV projection's epilogue.
  * JEPA_F32 (plain fp32 FMA, RoPE applied as q and k are loaded): work_dev is unused and
  * may be NULL.
- * Errors: JEPA_ERR_ARG also when the bf16 workspace is NULL or smaller than needed. */
+ * Errors: JEPA_ERR_ARG also when the bf16 workspace is NULL or smaller than needed, or
+ * when a bf16 call's qkv_dev, out_dev or work_dev is not 16-byte aligned. */
 int jepa_attention(const void* qkv_dev, void* out_dev, int dtype, int B, int N, int n_head,
                    int head_dim, const int32_t* ids_dev, int gt, int gh, int gw, int layout,
                    float theta, int ref_grid, void* work_dev, size_t work_bytes, void* stream);

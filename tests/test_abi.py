@@ -112,6 +112,11 @@ def test_standalone_ops_validate_before_launch():
     assert need > 8 * 3 * 64 * 2
     assert lib.jepa_attention(fake, fake, 1, 1, 8, 1, 64, None, 1, 2, 4, 0, 1e4, 0, None, 0, None) == _lib.JEPA_ERR_ARG
     assert lib.jepa_attention(fake, fake, 1, 1, 8, 1, 64, None, 1, 2, 4, 0, 1e4, 0, fake, need - 1, None) == _lib.JEPA_ERR_ARG
+    # bf16 buffers must be 16-byte aligned (checked before anything is launched)
+    odd = ctypes.c_void_p(fake.value + 8)
+    assert lib.jepa_attention(fake, odd, 1, 1, 8, 1, 64, None, 1, 2, 4, 0, 1e4, 0, fake, need, None) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_attention(odd, fake, 1, 1, 8, 1, 64, None, 1, 2, 4, 0, 1e4, 0, fake, need, None) == _lib.JEPA_ERR_ARG
+    assert lib.jepa_attention(fake, fake, 1, 1, 8, 1, 64, None, 1, 2, 4, 0, 1e4, 0, odd, need, None) == _lib.JEPA_ERR_ARG
     assert lib.jepa_attention_workspace_size(0, 1, 8, 1, 64) == 0
     assert lib.jepa_attention_workspace_size(1, 0, 8, 1, 64) == 0
 

@@ -1003,6 +1003,10 @@ static int attention_common(const void* qkv_dev, void* out_dev, int dtype, int B
   size_t off_qk, off_vt;
   const size_t need = attn_ws_parts(B, N, D, &off_qk, &off_vt);
   if (!work_dev || work_bytes < need) return JEPA_ERR_ARG;
+  // the kernels move 16-byte vectors
+  if ((reinterpret_cast<uintptr_t>(qkv_dev) | reinterpret_cast<uintptr_t>(out_dev) |
+       reinterpret_cast<uintptr_t>(work_dev)) % 16)
+    return JEPA_ERR_ARG;
   unsigned char* w = static_cast<unsigned char*>(work_dev);
   uint16_t* qk = reinterpret_cast<uint16_t*>(w + off_qk);
   uint16_t* vt = reinterpret_cast<uint16_t*>(w + off_vt);

@@ -498,14 +498,16 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (qok[g]) {
       uint16_t* dst = out + (static_cast<size_t>(b) * N + qrow[g]) * D + head * HD;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt) {
+        u32x2 pk[4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[g][dt][4 * g4] * inv, o[g][dt][4 * g4 + 1] * inv);
-          pk[1] = pack_bf16x2(o[g][dt][4 * g4 + 2] * inv, o[g][dt][4 * g4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g4 + 4 * h) = pk;
+          pk[g4][0] = pack_bf16x2(o[g][dt][4 * g4] * inv, o[g][dt][4 * g4 + 1] * inv);
+          pk[g4][1] = pack_bf16x2(o[g][dt][4 * g4 + 2] * inv, o[g][dt][4 * g4 + 3] * inv);
         }
+        // lanes l and l + 32 hold the same query row (qok is the same for both)
+        store_row32_bf16(dst + dt * 32, pk, h);
+      }
     }
   }
 }

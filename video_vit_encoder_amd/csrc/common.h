@@ -61,6 +61,22 @@ __device__ __forceinline__ int thw_coord(uint32_t pk, int a) {
 // writes LDS bytes [lds + 16p, lds + 16p + 16) from base + voff.  Issued through inline
 // asm so that the kernel, not the compiler, decides how many of these may still be in
 // flight at each barrier (s_waitcnt vmcnt).  lds must be wave-uniform.
+// Store of one row's 32 bf16 columns of a 32 x 32 MFMA block.  Lane l (h = l / 32) holds
+// the packed columns 8 gq + 4 h .. + 3 in pk[gq]; lanes l and l + 32 hold the same row.
+// v_permlane32_swap trades the upper half of one word with the lower half of the next, so
+// that each lane ends up with 8 contiguous columns: 16 p + 8 h .. + 7 for p = 0, 1, and
+// two 16-byte stores per lane write the row in 32-byte pieces (four 8-byte stores
+// otherwise).  Both lanes of a pair must be active.
+__device__ __forceinline__ void store_row32_bf16(uint16_t* dst /* row, column 0 */, const u32x2 (&pk)[4], int h) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const auto w0 = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0], false, false);
+    const auto w1 = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1], false, false);
+    const u32x4 w = {w0[0], w1[0], w0[1], w1[1]};
+    *reinterpret_cast<u32x4*>(dst + 16 * p + 8 * h) = w;
+  }
+}
+
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
   // both operands live in SGPRs: make their uniformity explicit
   // (readfirstlane returns int: widen through uint32_t, never by sign extension)
