@@ -481,6 +481,20 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
               __builtin_amdgcn_sched_barrier(0);
             }
           }
+        if (ks + 1 < KSTEPS) {
+          // Scheduling groups: the next k-step's fragment reads go out between the first
+          // two MFMAs of this k-step (half of them after each), so their LDS latency has
+          // the rest of the k-step to pass.  Left to itself the scheduler moved most of
+          // them behind the last MFMA, right before their use.
+          constexpr int NR = FI + FJ, R = (NR + 1) / 2;
+#pragma unroll
+          for (int m = 0; m < FI * FJ; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              if (R * m + r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          }
+        }
         if (spread) {
 #pragma unroll
           for (int q = FI * FJ; q < C::LOADS; ++q) issue_load(q);
