@@ -269,8 +269,17 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[g][dt][i] = 0.f;
   float m_run[2] = {0.f, 0.f}, l_run[2] = {0.f, 0.f};
-  f32x16 sc[2][2];   // scores of the tile this wave multiplied last
-  bf16x8 pf[2][4];   // probabilities of the tile whose softmax this wave ran last
+  // Scores of the tile this wave multiplied last; after its softmax the same registers hold
+  // the tile's bf16 probabilities (words 0-3 and 8-11 of each block, see probs below) until
+  // the next P V reads them.
+  f32x16 sc[2][2];
+  // -m_run[g] in all 16 slots: the C operand of each score chain's first MFMA, rewritten
+  // only when the running max moves
+  f32x16 negm[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[g][i] = 0.f;
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   int issued = 0;
@@ -307,7 +316,14 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     }
   };
-  // O^T += V^T P^T for tile t (probabilities pf)
+  // probabilities of k-step ks of group g: words 8 (ks % 2) .. + 3 of sc[g][ks / 2]
+  auto pfrag = [&](int g, int ks) __attribute__((always_inline)) {
+    const int b = 8 * (ks & 1);
+    const u32x4 w = {__float_as_uint(sc[g][ks >> 1][b]), __float_as_uint(sc[g][ks >> 1][b + 1]),
+                     __float_as_uint(sc[g][ks >> 1][b + 2]), __float_as_uint(sc[g][ks >> 1][b + 3])};
+    return __builtin_bit_cast(bf16x8, w);
+  };
+  // O^T += V^T P^T for tile t (probabilities in sc)
   auto mma_pv = [&](int t) __attribute__((always_inline)) {
     const unsigned char* st = smem + (t % S) * STAGE;
 #pragma unroll
@@ -318,7 +334,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + K_BYTES + dim * 128 + (((2 * ks + h) ^ lds_key128(dim)) << 4));
 #pragma unroll
         for (int g = 0; g < 2; ++g)
-          o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g][ks], o[g][dt], 0, 0, 0);
+          o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pfrag(g, ks), o[g][dt], 0, 0, 0);
       }
     }
   };
@@ -328,12 +344,6 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   auto mma_qk = [&](int t) __attribute__((always_inline)) {
     const unsigned char* st = smem + (t % S) * STAGE;
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[g][t2][i] = -m_run[g];
-#pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int r = t2 * 32 + l32;
 #pragma unroll
@@ -341,13 +351,15 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + r * KROW + (((2 * kk + h) ^ kkey(r)) << 4));
 #pragma unroll
         for (int g = 0; g < 2; ++g)
-          sc[g][t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][kk], sc[g][t2], 0, 0, 0);
+          sc[g][t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][kk], kk == 0 ? negm[g] : sc[g][t2], 0, 0, 0);
       }
     }
   };
-  // Softmax of tile t's scores into pf, updating m_run, l_run (and o on a rescale).
+  // Softmax of tile t's scores, the bf16 probabilities written over them, updating m_run,
+  // l_run (and o on a rescale).
   auto softmax = [&](int t) __attribute__((always_inline)) {
     const int kb = t * BKV;
+    auto mask = [&]() __attribute__((always_inline)) {
     if (BC) {
       if (__ballot(kb + BKV > lim[0] || kb + BKV > lim[1] || kb < lo[0] || kb < lo[1]) != 0) {
 #pragma unroll
@@ -375,6 +387,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           for (int i = 0; i < 16; ++i)
             if (kb + t2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3) >= N) sc[g][t2][i] = -INFINITY;
     }
+    };
+    mask();
     // P = exp2(S - m) rounded to bf16, with each lane's sum of its 32 bf16 values per group
     // in two chains (v_dot2_f32_bf16 adds a pair per step).
     float lt[2][2];
@@ -397,7 +411,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             lt[g][e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lt[g][e & 1], false);
             w[e] = __builtin_bit_cast(uint32_t, pb);
           }
-          pf[g][ks] = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[g][ks >> 1][8 * (ks & 1) + e] = __uint_as_float(w[e]);
         }
       }
     };
@@ -411,6 +426,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (!exact) {
       probs();
       exact = __ballot(lt[0][0] + lt[0][1] > kTwoTau || lt[1][0] + lt[1][1] > kTwoTau) != 0;
+      if (exact) {
+        // the probabilities replaced the scores: form them again (tile t's K stays in its
+        // ring buffer until phase 2t + 4 refills it)
+        mma_qk(t);
+        mask();
+      }
     }
     if (exact) {
       // Row max of the tile relative to the running max, one wave-uniform decision for
@@ -431,6 +452,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-d);
           m_run[g] += d;
           l_run[g] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) negm[g][i] = -m_run[g];
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
