@@ -478,6 +478,19 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __builtin_amdgcn_s_setprio(1);
     if (t > 0) mma_pv(t - 1);
     mma_qk(t);
+    if (t > 0) {
+      // Scheduling groups: each K or V^T fragment read feeds two MFMAs; issue the reads LA
+      // steps ahead of their MFMAs instead of one, so that their LDS latency passes behind
+      // the matrix work (left alone, the scheduler waited on each read one step later).
+      constexpr int NRD = DT * 4 + 2 * KS, LA = 3;
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+      for (int i = 0; i < NRD - LA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * LA, 0);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
