@@ -15,6 +15,7 @@ and position (0, 0, 0) for the CLS rows.
   * causality, bit for bit: changing the keys and values of later slots leaves the patch
     rows of the first slot unchanged (the CLS row moves), changing the CLS key and value
     leaves every patch row unchanged;
+  * growing key norms, so that the lazy rescale runs on tiles that straddle a slot limit;
   * argument errors.
 """
 import numpy as np
@@ -111,6 +112,25 @@ def test_block_causal_levjepa_shape():
     ref = _ref(qkv.astype(np.float64), n_cls, grid, H, hd, "tiled", 0, rows=rows)
     assert_bf16_gate(got[:, rows], ref, "LeVJEPA 3137 rows (sampled)")
     assert np.isfinite(got).all()
+
+
+def test_block_causal_growing_scores():
+    # key norms grow along the clip: later key tiles raise a query's running maximum past
+    # the kernel's lazy-rescale threshold, so tiles that straddle a slot limit get their
+    # scores formed a second time and masked again
+    B, n_cls, grid, H, hd = 1, 1, (6, 10, 10), 2, 64
+    banner("block-causal attention growing scores", B, n_cls, grid, H, hd)
+    N, D = n_cls + grid[0] * grid[1] * grid[2], H * hd
+    rng = np.random.default_rng(33)
+    qkv = rng.standard_normal((B, N, 3 * D))
+    qkv[..., :D] *= 2.0
+    qkv[..., D:2 * D] *= (4.0 * np.arange(N) / N)[:, None]
+    qkv = synth.round_to_bf16(qkv.astype(np.float32))
+    got = _run(qkv, n_cls, grid, H, hd, "tiled", 0, "bf16")
+    ref = _ref(qkv.astype(np.float64), n_cls, grid, H, hd, "tiled", 0)
+    assert_bf16_gate(got, ref, "block-causal growing scores")
+    unmasked = _ref(qkv.astype(np.float64), n_cls, grid, H, hd, "tiled", 0, masked=False)
+    assert metrics.rel_max(got, unmasked) > 5e-2
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])

@@ -314,13 +314,16 @@ def test_attention_softmax_properties_identical_keys():
     assert np.array_equal(got, np.broadcast_to(vrow.astype(np.float64), (N, D)))
 
 
-def test_attention_growing_scores_rescale():
+@pytest.mark.parametrize("grid", [(4, 12, 16), (4, 12, 15)], ids=["768 rows", "720 rows ragged"])
+def test_attention_growing_scores_rescale(grid):
     # key norms grow along the clip, so later key tiles keep raising each query's running
     # maximum by more than 2^8 (the kernel's lazy-rescale threshold, in log2 units) and
-    # the rescale path runs many times; the first tile's scores are small
-    banner("attention growing scores")
-    B, grid, H, hd = 1, (4, 12, 16), 2, 64
-    N, D = 768, 128
+    # the rescale path runs many times; the first tile's scores are small.  With 720 rows
+    # the last key tile is ragged, so its scores are masked again after they are formed
+    # a second time.
+    banner("attention growing scores", grid)
+    B, H, hd = 1, 2, 64
+    N, D = grid[0] * grid[1] * grid[2], 128
     rng = np.random.default_rng(21)
     qkv = rng.standard_normal((N, 3 * D))
     qkv[:, :D] *= 2.0
