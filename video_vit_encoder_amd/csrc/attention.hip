@@ -128,8 +128,9 @@ __device__ __forceinline__ float max_halves(float x) {
 //     exceeds it by more than 8: between moves the probabilities stay in (0, 256] and
 //     neither the scores nor the output accumulators are touched before exp2.  The first
 //     tile sets the max exactly, so the running sum never underflows;
-//   * the row sum adds the bf16-rounded probabilities (the values the second product
-//     uses) with v_dot2_f32_bf16.
+//   * the row sum adds the fp32 probabilities with plain adds in four chains: beside the
+//     other wave's MFMAs, v_dot2_f32_bf16 on the rounded pairs (one instruction per pair)
+//     took longer than two adds.
 // BC: the block-causal mask of [Parity] "LeVJEPA ViT-L/16 — CLS, block-causal attention,
 // tubelet 1".  Rows [0, n_cls) are CLS rows that see every key; row r >= n_cls is a patch
 // token of temporal slot s = (r - n_cls) / slot and sees the keys [n_cls, lim(r)), lim(r) =
@@ -280,7 +281,6 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int i = 0; i < 16; ++i) negm[g][i] = 0.f;
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   int issued = 0;
   for (; issued < 2 && issued < ntiles; ++issued) issue(issued);
@@ -389,18 +389,19 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
     };
     mask();
-    // P = exp2(S - m) rounded to bf16, with each lane's sum of its 32 bf16 values per group
-    // in two chains (v_dot2_f32_bf16 adds a pair per step).
-    float lt[2][2];
+    // P = exp2(S - m) rounded to bf16, with each lane's sum of its 32 fp32 values per group
+    // in four chains of adds.
+    float lt[2][4];
+    auto lsum = [&](int g) __attribute__((always_inline)) { return (lt[g][0] + lt[g][1]) + (lt[g][2] + lt[g][3]); };
     auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        lt[g][0] = 0.f;
-        lt[g][1] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lt[g][c] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           // slot s of k-step ks = element 8 (ks % 2) + s of sc[g][ks / 2]; each pair is
-          // converted as one bf16x2 value that feeds both the dot product and the word
+          // converted as one bf16x2 word
           u32x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -408,7 +409,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             const f32x2 pp = {__builtin_amdgcn_exp2f(sc[g][ks >> 1][i]),
                               __builtin_amdgcn_exp2f(sc[g][ks >> 1][i + 1])};
             const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-            lt[g][e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lt[g][e & 1], false);
+            lt[g][2 * (e & 1)] += pp[0];
+            lt[g][2 * (e & 1) + 1] += pp[1];
             w[e] = __builtin_bit_cast(uint32_t, pb);
           }
 #pragma unroll
@@ -425,7 +427,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     bool exact = t == 0;
     if (!exact) {
       probs();
-      exact = __ballot(lt[0][0] + lt[0][1] > kTwoTau || lt[1][0] + lt[1][1] > kTwoTau) != 0;
+      exact = __ballot(lsum(0) > kTwoTau || lsum(1) > kTwoTau) != 0;
       if (exact) {
         // the probabilities replaced the scores: form them again (tile t's K stays in its
         // ring buffer until phase 2t + 4 refills it)
@@ -467,7 +469,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       probs();
     }
 #pragma unroll
-    for (int g = 0; g < 2; ++g) l_run[g] += lt[g][0] + lt[g][1];
+    for (int g = 0; g < 2; ++g) l_run[g] += lsum(g);
   };
 
   // Matrix phase of tile t: P V of tile t - 1 and K Q of tile t at raised wave priority.
@@ -482,7 +484,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       // Scheduling groups: each K or V^T fragment read feeds two MFMAs; issue the reads LA
       // steps ahead of their MFMAs instead of one, so that their LDS latency passes behind
       // the matrix work (left alone, the scheduler waited on each read one step later).
-      constexpr int NRD = DT * 4 + 2 * KS, LA = 3;
+      // (two steps for the block-causal kernel, whose range registers leave less room)
+      constexpr int NRD = DT * 4 + 2 * KS, LA = BC ? 2 : 3;
       __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
       for (int i = 0; i < NRD - LA; ++i) {
