@@ -6,10 +6,11 @@
 // bf16 path (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //   * a workgroup of 8 wavefronts (2 per SIMD) computes 256 (rows of A) x 256, 192 or
 //     128 (rows of W) output tiles, the width chosen by the rounds of the CUs its tiles
-//     need times the rows a tile streams per K slab: the bytes a CU pulls from L2 per
-//     MFMA fall as the tile grows, and the L2 -> LDS path, not the LDS or the MFMAs,
-//     limits the main loop; each wave owns a 128x64, 64x96 or 64x64 part of the tile as
-//     32x32 blocks;
+//     need times the rows a tile streams per K slab: the bytes a CU copies into LDS per
+//     MFMA fall as the tile grows, and the slab copies (their LDS writes and their issue
+//     beside the fragment reads), not the MFMAs or the copies' latency, set the pace of
+//     the main loop; each wave owns a 128x64, 64x96 or 64x64 part of the tile as 32x32
+//     blocks;
 //   * the kernel is persistent: one workgroup per CU walks its tiles, and the 64-deep
 //     K-slabs of all its tiles form one stream through a ring of 2 or 3 LDS buffers,
 //     filled by global_load_lds_dwordx4 (HBM/L2 -> LDS, no register staging) up to
@@ -560,8 +561,8 @@ static hipError_t gemm_dispatch(const uint16_t* A, const uint16_t* W, const floa
 
 // Width of the 256-row tile (256, 192 or 128, at most max_w): the one with the least
 // estimated time, taken as the rounds of the CUs the tiles need times the rows a tile
-// streams into LDS per K slab (256 + width), since the L2 -> LDS path bounds the main
-// loop; ties go to the wider tile.
+// streams into LDS per K slab (256 + width), since the slab copies set the pace of the
+// main loop; ties go to the wider tile.
 static int tile_width(int M, int N, int max_w = 256) {
   const long long cus = num_cus();
   const long long tm = (M + 255) / 256;
