@@ -248,6 +248,9 @@ ATTN_CASES = [
     ("hd64 one tile", 1, (1, 2, 3), 2, 64, "tiled", 0, None, "bf16"),
     ("hd64 two 2048-token clips", 2, (8, 16, 16), 2, 64, "tiled", 0, None, "bf16"),
     ("hd32 interleaved 1000 tokens", 1, (10, 10, 10), 3, 32, "interleaved", 16, None, "bf16"),
+    # the longest clip of 256-query workgroups, and the shortest of 512-query ones (ragged)
+    ("hd64 1024 tokens", 1, (4, 16, 16), 2, 64, "tiled", 0, None, "bf16"),
+    ("hd32 1058 tokens", 1, (2, 23, 23), 2, 32, "tiled", 0, None, "bf16"),
     ("hd64 f32 tiny grid", 1, (2, 4, 4), 12, 64, "tiled", 0, None, "f32"),
     ("hd64 f32 ragged", 2, (3, 7, 5), 2, 64, "interleaved", 16, None, "f32"),
     ("hd32 f32 ids", 1, (2, 6, 6), 3, 32, "tiled", 0, "perm", "f32"),

@@ -104,9 +104,10 @@ __device__ __forceinline__ float max_halves(float x) {
 // on inputs prepared once per token (the QKV projection's epilogue or qkv_prepare_kernel):
 // q rotated and scaled by log2(e)/sqrt(hd), k rotated, v transposed per (clip, head) with
 // the keys of each 16-group in vt_pos order.
-//   * a workgroup of 8 wavefronts owns 512 queries of one (clip, head); each wave keeps
-//     two groups of 32 as bf16 MFMA B operands in registers, and every K or V fragment it
-//     reads from LDS feeds the MFMAs of both groups;
+//   * a workgroup of 8 wavefronts owns 256 NG queries of one (clip, head); each wave keeps
+//     NG groups of 32 as bf16 MFMA B operands in registers, and every K or V fragment it
+//     reads from LDS feeds the MFMAs of all its groups (NG = 2, except NG = 1 for clips
+//     short enough that 512-query blocks would leave most compute units idle);
 //   * the waves form two halves of four (one wave of each half per SIMD) that take turns
 //     between workgroup barriers: in one phase half A runs the matrix products of a key
 //     tile (P V of the previous tile, then S = K Q of this one) while half B runs the
@@ -141,12 +142,12 @@ __device__ __forceinline__ float max_halves(float x) {
 // last slot, needs them all), so the work follows the mask's density.  Scores outside
 // [lo, lim) become -inf in the tiles that straddle a limit.  The heaviest blocks start
 // first.
-template <int HD, bool BC>
+template <int HD, bool BC, int NG>
 __global__ __launch_bounds__(512, 1)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int ld,
                      const uint16_t* __restrict__ vt, int Ns, uint16_t* __restrict__ out, int N,
                      int H, int nqb, int n_cls, int slot) {
-  constexpr int NW = 8, BQ = NW * 64, BKV = 64, S = 4;
+  constexpr int NW = 8, BQ = NW * 32 * NG, BKV = 64, S = 4;
   constexpr int KS = HD / 16;                   // MFMA k-steps over the head dim
   constexpr int DT = HD / 32;                   // 32-dim blocks of the output
   constexpr int KROW = HD * 2;                  // LDS bytes per K row (128 / 64)
@@ -192,11 +193,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int jbase = (BC ? N - nqb * BQ : 0) + qblk * BQ;
   auto row_of = [&](int j) { return j < N - n_cls ? j + n_cls : j - (N - n_cls); };
   auto limit_of = [&](int r) { return r < n_cls ? N : min(N, n_cls + ((r - n_cls) / slot + 1) * slot); };
-  int qrow[2], lo[2], lim[2];
-  bool qok[2];
+  int qrow[NG], lo[NG], lim[NG];
+  bool qok[NG];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int j = jbase + wave * 64 + g * 32 + l32;
+  for (int g = 0; g < NG; ++g) {
+    const int j = jbase + wave * (32 * NG) + g * 32 + l32;
     if (BC) {
       qok[g] = j >= 0;
       qrow[g] = row_of(max(j, 0));
@@ -245,10 +246,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   };
 
-  // ---- queries: two groups of 32 per wave, B operands (dims 16kk + 8h .. +8)
-  bf16x8 qf[2][KS];
+  // ---- queries: NG groups of 32 per wave, B operands (dims 16kk + 8h .. +8)
+  bf16x8 qf[NG][KS];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < NG; ++g) {
     const uint16_t* src = q + (static_cast<size_t>(b) * N + qrow[g]) * ld + head * HD;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) qf[g][kk] = *reinterpret_cast<const bf16x8*>(src + (2 * kk + h) * 8);
@@ -258,27 +259,29 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // also wait for the tiles in flight.  The empty asm takes the fragments as outputs, so
   // nothing after it depends on the loads.
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[g][kk]));
 
-  f32x16 o[2][DT];
+  f32x16 o[NG][DT];
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[g][dt][i] = 0.f;
-  float m_run[2] = {0.f, 0.f}, l_run[2] = {0.f, 0.f};
+  float m_run[NG], l_run[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) m_run[g] = l_run[g] = 0.f;
   // Scores of the tile this wave multiplied last; after its softmax the same registers hold
   // the tile's bf16 probabilities (words 0-3 and 8-11 of each block, see probs below) until
   // the next P V reads them.
-  f32x16 sc[2][2];
+  f32x16 sc[NG][2];
   // -m_run[g] in all 16 slots: the C operand of each score chain's first MFMA, rewritten
   // only when the running max moves
-  f32x16 negm[2];
+  f32x16 negm[NG];
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int i = 0; i < 16; ++i) negm[g][i] = 0.f;
 
@@ -333,7 +336,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + K_BYTES + dim * 128 + (((2 * ks + h) ^ lds_key128(dim)) << 4));
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < NG; ++g)
           o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pfrag(g, ks), o[g][dt], 0, 0, 0);
       }
     }
@@ -350,7 +353,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int kk = 0; kk < KS; ++kk) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + r * KROW + (((2 * kk + h) ^ kkey(r)) << 4));
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < NG; ++g)
           sc[g][t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][kk], kk == 0 ? negm[g] : sc[g][t2], 0, 0, 0);
       }
     }
@@ -361,9 +364,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int kb = t * BKV;
     auto mask = [&]() __attribute__((always_inline)) {
     if (BC) {
-      if (__ballot(kb + BKV > lim[0] || kb + BKV > lim[1] || kb < lo[0] || kb < lo[1]) != 0) {
+      bool straddle = false;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) straddle = straddle || kb + BKV > lim[g] || kb < lo[g];
+      if (__ballot(straddle) != 0) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
           // key k = kb + 4h + c (c the element's constant offset) is outside [lo, lim) iff
           // k - lo or lim - 1 - k is negative: the sign of their OR picks -inf or +inf as
           // the bound of a minimum, with no lane mask
@@ -380,7 +386,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     } else if (kb + BKV > N) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -391,11 +397,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     mask();
     // P = exp2(S - m) rounded to bf16, with each lane's sum of its 32 fp32 values per group
     // in four chains of adds.
-    float lt[2][4];
+    float lt[NG][4];
     auto lsum = [&](int g) __attribute__((always_inline)) { return (lt[g][0] + lt[g][1]) + (lt[g][2] + lt[g][3]); };
     auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) lt[g][c] = 0.f;
 #pragma unroll
@@ -427,7 +433,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     bool exact = t == 0;
     if (!exact) {
       probs();
-      exact = __ballot(lsum(0) > kTwoTau || lsum(1) > kTwoTau) != 0;
+      bool big = false;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) big = big || lsum(g) > kTwoTau;
+      exact = __ballot(big) != 0;
       if (exact) {
         // the probabilities replaced the scores: form them again (tile t's K stays in its
         // ring buffer until phase 2t + 4 refills it)
@@ -437,19 +446,22 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
     if (exact) {
       // Row max of the tile relative to the running max, one wave-uniform decision for
-      // both groups.
-      float mxs[2];
+      // all the wave's groups.
+      float mxs[NG];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         // a linear chain of 3-input maxima (v_max3_f32): half an op per score
         float mx = fmaxf(sc[g][0][0], sc[g][1][0]);
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, sc[g][0][i]), sc[g][1][i]);
         mxs[g] = max_halves(mx);
       }
-      if (t == 0 || __ballot(mxs[0] > TAU || mxs[1] > TAU) != 0) {
+      bool moved = false;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) moved = moved || mxs[g] > TAU;
+      if (t == 0 || __ballot(moved) != 0) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
           const float d = t == 0 ? mxs[g] : (mxs[g] > TAU ? mxs[g] : 0.f);
           const float alpha = t == 0 ? 0.f : __builtin_amdgcn_exp2f(-d);
           m_run[g] += d;
@@ -469,7 +481,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       probs();
     }
 #pragma unroll
-    for (int g = 0; g < 2; ++g) l_run[g] += lsum(g);
+    for (int g = 0; g < NG; ++g) l_run[g] += lsum(g);
   };
 
   // Matrix phase of tile t: P V of tile t - 1 and K Q of tile t at raised wave priority.
@@ -481,7 +493,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (t > 0) mma_pv(t - 1);
     mma_qk(t);
     if (t > 0) {
-      // Scheduling groups: each K or V^T fragment read feeds two MFMAs; issue the reads LA
+      // Scheduling groups: each K or V^T fragment read feeds NG MFMAs; issue the reads LA
       // steps ahead of their MFMAs instead of one, so that their LDS latency passes behind
       // the matrix work (left alone, the scheduler waited on each read one step later).
       // (two steps for the block-causal kernel, whose range registers leave less room)
@@ -489,10 +501,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
       for (int i = 0; i < NRD - LA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * LA, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NG * LA, 0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -532,7 +544,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   // ---- normalise and store: element i of o[g][dt] is dim 32 dt + 8(i/4) + 4h + i%4
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < NG; ++g) {
     const float inv = 1.0f / (l_run[g] + __shfl_xor(l_run[g], 32));
     if (qok[g]) {
       uint16_t* dst = out + (static_cast<size_t>(b) * N + qrow[g]) * D + head * HD;
@@ -551,24 +563,26 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 }
 
-template <int HD, bool BC>
+template <int HD, bool BC, int NG>
 static hipError_t attn_launch(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt, int Ns,
                               uint16_t* out, int B, int N, int n_head, int n_cls, int slot,
                               hipStream_t s) {
   constexpr int LDS = 4 * (64 * HD * 2 + HD * 64 * 2);
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<HD, BC>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<HD, BC, NG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int nqb = (N + 511) / 512;
+  constexpr int BQ = 8 * 32 * NG;   // queries per workgroup
+  const int nqb = (N + BQ - 1) / BQ;
   const dim3 grid(nqb * n_head * B);
-  attn_fwd_kernel<HD, BC><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb, n_cls, slot);
+  attn_fwd_kernel<HD, BC, NG><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb, n_cls, slot);
   return hipGetLastError();
 }
 
+constexpr int kAttnShortN = 1024;   // longest clip that takes 256-query workgroups
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
                                 int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
                                 hipStream_t s, int n_cls, int slot) {
@@ -581,11 +595,18 @@ hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, co
   if (slot > 0) {
     // the first key tile must hold a key every query sees (key n_cls)
     if (n_cls < 0 || n_cls >= 64 || n_cls >= N) return hipErrorInvalidValue;
-    if (head_dim == 64) return attn_launch<64, true>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, s);
-    return attn_launch<32, true>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, s);
+    if (head_dim == 64) return attn_launch<64, true, 2>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, s);
+    return attn_launch<32, true, 2>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, s);
   }
-  if (head_dim == 64) return attn_launch<64, false>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
-  return attn_launch<32, false>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
+  // Short clips (at most 1024 keys) take 256-query workgroups, one group of 32 queries per
+  // wave: twice the workgroups for the few (clip, head) pairs.  The choice depends on N
+  // only, so a clip's result does not depend on the batch it comes in.
+  if (N <= kAttnShortN) {
+    if (head_dim == 64) return attn_launch<64, false, 1>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
+    return attn_launch<32, false, 1>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
+  }
+  if (head_dim == 64) return attn_launch<64, false, 2>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
+  return attn_launch<32, false, 2>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
 }
 
 // Attention inputs from a projection already in memory (the stand-alone entry point): one
