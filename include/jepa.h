@@ -336,7 +336,11 @@ int jepa_linear(const void* A_dev, const void* W_dev, const float* bias_dev, voi
  * log2(e)/sqrt(head_dim)) and v transposed into work_dev, a device buffer of at least
  * jepa_attention_workspace_size(...) bytes owned by the caller (contents on entry do not
  * matter; overwritten); then the flash-attention kernel runs on it.  The encoder forward
- * uses the same kernel with the rotation done by the QKV projection's epilogue.
+ * uses the same kernel with the rotation done by the QKV projection's epilogue.  Clips of
+ * 4096 tokens or more whose (head, 512-query block) pairs would leave many of the GPU's
+ * 256 compute units idle take each block's keys in 2-8 pieces, whose fp32 partial states
+ * a second kernel merges in piece order (the workspace then also holds them); the choice
+ * depends on N and n_head only, so a clip's output does not depend on B.
  * JEPA_F32 (plain fp32 FMA, RoPE applied as q and k are loaded): work_dev is unused and
  * may be NULL.
  * Errors: JEPA_ERR_ARG also when the bf16 workspace is NULL or smaller than needed, or
@@ -362,7 +366,8 @@ size_t jepa_attention_workspace_size(int dtype, int B, int N, int n_head, int he
  *   theta, ref_grid and the workspace (jepa_attention_workspace_size(dtype, B, N, ...))
  *   as jepa_attention.  0 <= n_cls < 64.
  * With n_cls = 0 and gt = 1 every row sees every key and the result equals
- * jepa_attention on the same rows.
+ * jepa_attention on the same rows (bit for bit when jepa_attention takes the keys in one
+ * piece, as it always does below 4096 rows; up to rounding otherwise).
  * Errors: as jepa_attention; JEPA_ERR_SHAPE for n_cls outside [0, 64). */
 int jepa_attention_block_causal(const void* qkv_dev, void* out_dev, int dtype, int B, int n_cls,
                                 int n_head, int head_dim, int gt, int gh, int gw, int layout,
@@ -379,8 +384,9 @@ int jepa_attention_block_causal(const void* qkv_dev, void* out_dev, int dtype, i
  * process ends, and the call allocates nothing (no hipMalloc, hipFree or allocating
  * library routine).  The caller still owns qkv_dev and out_dev.
  *   Limit: jepa_attention_workspace_size(dtype, B, N, n_head, head_dim) must not exceed
- *   JEPA_ATTN_SCRATCH_BYTES (e.g. B*N*n_head*head_dim up to about 11 M elements), else
- *   JEPA_ERR_SHAPE and nothing is enqueued.
+ *   JEPA_ATTN_SCRATCH_BYTES (e.g. B*N*n_head*head_dim up to about 11 M elements when the
+ *   keys are taken whole; long clips whose keys go in pieces need more per element),
+ *   else JEPA_ERR_SHAPE and nothing is enqueued.
  *   Every call on one GPU shares that GPU's array and leaves its contents behind (no
  *   state is read back: every byte a call reads was written earlier in the same call, or
  *   is masked); two calls that overlap on one GPU (different streams, or host threads

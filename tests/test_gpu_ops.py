@@ -251,6 +251,10 @@ ATTN_CASES = [
     # the longest clip of 256-query workgroups, and the shortest of 512-query ones (ragged)
     ("hd64 1024 tokens", 1, (4, 16, 16), 2, 64, "tiled", 0, None, "bf16"),
     ("hd32 1058 tokens", 1, (2, 23, 23), 2, 32, "tiled", 0, None, "bf16"),
+    # long clips with few heads: the keys of each query block go in 8 pieces (the last
+    # piece short, its last tile ragged at 4205 tokens), merged at the end
+    ("hd64 4205 tokens in key pieces", 1, (5, 29, 29), 2, 64, "tiled", 0, None, "bf16"),
+    ("hd32 2 x 4608 tokens in key pieces", 2, (8, 24, 24), 2, 32, "interleaved", 16, None, "bf16"),
     ("hd64 f32 tiny grid", 1, (2, 4, 4), 12, 64, "tiled", 0, None, "f32"),
     ("hd64 f32 ragged", 2, (3, 7, 5), 2, 64, "interleaved", 16, None, "f32"),
     ("hd32 f32 ids", 1, (2, 6, 6), 3, 32, "tiled", 0, "perm", "f32"),
@@ -317,19 +321,27 @@ def test_attention_softmax_properties_identical_keys():
     assert np.array_equal(got, np.broadcast_to(vrow.astype(np.float64), (N, D)))
 
 
-@pytest.mark.parametrize("grid", [(4, 12, 16), (4, 12, 15)], ids=["768 rows", "720 rows ragged"])
+@pytest.mark.parametrize("grid", [(4, 12, 16), (4, 12, 15), (4, 32, 36), (5, 29, 29)],
+                         ids=["768 rows", "720 rows ragged", "4608 rows in key pieces",
+                              "4205 rows ragged in key pieces"])
 def test_attention_growing_scores_rescale(grid):
     # key norms grow along the clip, so later key tiles keep raising each query's running
     # maximum by more than 2^8 (the kernel's lazy-rescale threshold, in log2 units) and
     # the rescale path runs many times; the first tile's scores are small.  With 720 rows
     # the last key tile is ragged, so its scores are masked again after they are formed
-    # a second time.
+    # a second time.  From 4096 rows on (two heads) the keys go in 8 pieces whose maxima
+    # differ by 2^8.6 to 2^31 (median 2^15; 4608 rows, head 0), so the merge weights of
+    # the early pieces are tiny.  There q is not doubled: the bf16 rounding of the rotated
+    # q and k (the kernel's inputs) moves each score by an amount that grows with its
+    # size, and over these longer clips the largest scores would put that error alone at
+    # 2.3-2.7 % of the output's scale (exact softmax on the rounded inputs), beyond the
+    # gate.
     banner("attention growing scores", grid)
     B, H, hd = 1, 2, 64
     N, D = grid[0] * grid[1] * grid[2], 128
     rng = np.random.default_rng(21)
     qkv = rng.standard_normal((N, 3 * D))
-    qkv[:, :D] *= 2.0
+    qkv[:, :D] *= 2.0 if N < 4096 else 1.0
     qkv[:, D:2 * D] *= (4.0 * np.arange(N) / N)[:, None]
     qkv = synth.round_to_bf16(qkv.astype(np.float32))
     import torch
@@ -339,3 +351,23 @@ def test_attention_growing_scores_rescale(grid):
     ref = _attn_ref(qkv.astype(np.float64).reshape(B, N, 3 * D), B, N, H, hd,
                     np.arange(N, dtype=np.int32), grid, "tiled", 0)
     assert_bf16_gate(got, ref, "growing scores")
+
+
+def test_attention_key_pieces_batch_invariant():
+    # 4608 tokens, two heads of 32: the keys of each query block go in pieces, chosen from
+    # the clip length and head count only, so a clip's output is the same bits alone and
+    # as the middle clip of three
+    import torch
+    banner("attention key pieces, batch invariance, 1 and 3 clips of 8 x 24 x 24")
+    grid, H, hd = (8, 24, 24), 2, 32
+    N, D = grid[0] * grid[1] * grid[2], 2 * 32
+    rng = np.random.default_rng(33)
+    qkv = synth.round_to_bf16(rng.standard_normal((3, N, 3 * D)).astype(np.float32))
+    one = torch.empty((N, D), dtype=torch.bfloat16, device="cuda:0")
+    three = torch.empty((3 * N, D), dtype=torch.bfloat16, device="cuda:0")
+    J.jepa_attention(bf16(qkv[1]), one, 1, N, H, hd, None, grid, "interleaved", ref_grid=16)
+    J.jepa_attention(bf16(qkv.reshape(3 * N, 3 * D)), three, 3, N, H, hd, None, grid,
+                     "interleaved", ref_grid=16)
+    a, b = host(one), host(three).reshape(3, N, D)[1]
+    assert np.all(np.isfinite(a))
+    assert np.array_equal(a, b), float(np.max(np.abs(a - b)))

@@ -3,8 +3,9 @@ against jepa_attention with a caller workspace, through the C ABI.
 
 Both run the same kernels on the same inputs, so the outputs must agree bit for bit.
 Two calls in a row, the second on a smaller input, show that what the first call left in
-the shared array does not leak into the second.  A size beyond the array is refused with
-JEPA_ERR_SHAPE and leaves the output untouched.
+the shared array does not leak into the second; a third, longer clip takes its keys in
+pieces, whose partial results live in the same array.  A size beyond the
+array is refused with JEPA_ERR_SHAPE and leaves the output untouched.
 """
 import numpy as np
 import pytest
@@ -25,6 +26,7 @@ CASES = [
     # B, grid, n_head, head_dim, layout, ref_grid, ids
     (2, (8, 16, 16), 16, 64, "tiled", 0, False),          # 2 clips x 2048 tokens, 24 MiB
     (1, (3, 10, 10), 4, 32, "interleaved", 16, True),      # ragged 300 tokens, shuffled ids
+    (1, (5, 29, 29), 2, 64, "tiled", 0, False),            # 4205 tokens, keys in 8 pieces
 ]
 
 

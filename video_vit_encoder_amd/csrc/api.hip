@@ -10,6 +10,7 @@
 // compute dtype (bf16 on the MFMA path).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -267,7 +268,7 @@ int check_grid(int gt, int gh, int gw, int ref_grid) {
 
 // Workspace of the block sequence for `rows` token rows.
 struct Workspace {
-  DevBuf h, qkv, o, g, a, vt, tab;
+  DevBuf h, qkv, o, g, a, vt, tab, split;
   int rows = 0;
   size_t vt_rows = 0;  // capacity of vt in (clip, key) rows of D values
   ~Workspace() {
@@ -278,8 +279,9 @@ struct Workspace {
     dev_free(a);
     dev_free(vt);
     dev_free(tab);
+    dev_free(split);
   }
-  int alloc(int max_rows, int D, int F, int a_cols, int compute) {
+  int alloc(int max_rows, int D, int F, int a_cols, int compute, int n_head) {
     rows = max_rows;
     const size_t es = compute == JEPA_BF16 ? 2 : 4;
     const size_t m = static_cast<size_t>(max_rows);
@@ -295,6 +297,12 @@ struct Workspace {
       JEPA_TRY(dev_alloc(vt, vt_rows * D * 2 + kVtSlackBytes));
       if (hipMemset(vt.p, 0, vt.bytes) != hipSuccess) return JEPA_ERR_HIP;
       JEPA_TRY(dev_alloc(tab, static_cast<size_t>(kRopeTabEntries) * 8));
+      // key pieces of long clips: the most any B clips of N tokens with B N <= max_rows
+      // need
+      size_t most = 0;
+      for (int n = 1; n <= max_rows; ++n)
+        most = std::max(most, attention_split_bytes(max_rows / n, n, n_head, D / n_head));
+      if (most > 0) JEPA_TRY(dev_alloc(split, most));
     }
     return JEPA_OK;
   }
@@ -326,6 +334,7 @@ int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_r
   const int Ns = vt_stride(N);
   if (bf && n_run > 0) {
     if (!ws.vt_fits(B, N)) return JEPA_ERR_SHAPE;
+    if (attention_split_bytes(B, N, n_head, hd) > ws.split.bytes) return JEPA_ERR_SHAPE;
     JEPA_LAUNCH(JEPA_KC_OTHER, s, launch_rope_table(ws.tab.p, rs, hd, s));
   }
   for (int l = 0; l < n_run; ++l) {
@@ -342,7 +351,7 @@ int run_blocks(const TensorSet& ts, const std::vector<BlockIdx>& blocks, int n_r
                                        attn_qscale(hd), s));
       JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
                   launch_attention_fwd(qkv, qkv + D, 3 * D, vt, Ns, static_cast<uint16_t*>(ws.o.p), B,
-                                       N, n_head, hd, s));
+                                       N, n_head, hd, s, 0, 0, ws.split.p));
     } else {
       JEPA_LAUNCH(JEPA_KC_GEMM_QKV, s,
                   linear(compute, ws.h.p, ts.dev(b.qkvw), ts.devf(b.qkvb), ws.qkv.p, M, 3 * D, D,
@@ -434,7 +443,7 @@ int jepa_encoder_create(const jepa_encoder_config* cfg, jepa_encoder** out) {
     e->img_b = e->ts.add("enc.patch_embed_img.bias", {D}, false, true);
     if (c.has_mod_embed) e->img_mod = e->ts.add("enc.mod_embed_img", {D}, false, true);
   }
-  int st = e->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, static_cast<int>(feat), c.compute);
+  int st = e->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, static_cast<int>(feat), c.compute, c.n_head);
   if (st == JEPA_OK) st = dev_alloc(e->pe_bias_eff, static_cast<size_t>(D) * 4);
   if (st == JEPA_OK && c.has_image_embed) st = dev_alloc(e->img_bias_eff, static_cast<size_t>(D) * 4);
   if (st != JEPA_OK) {
@@ -662,7 +671,7 @@ int jepa_predictor_create(const jepa_predictor_config* cfg, jepa_predictor** out
     p->pctx_w = p->ts.add("pred.proj_context.weight", {c.out_dim, E}, true);
     p->pctx_b = p->ts.add("pred.proj_context.bias", {c.out_dim}, false);
   }
-  int st = p->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, c.enc_dim, c.compute);
+  int st = p->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, c.enc_dim, c.compute, c.n_head);
   if (st == JEPA_OK) st = dev_alloc(p->x, static_cast<size_t>(c.max_rows) * E * 4);
   if (st == JEPA_OK) st = dev_alloc(p->ids, static_cast<size_t>(c.max_rows) * 4);
   if (st == JEPA_OK) st = dev_alloc(p->emb_bias, static_cast<size_t>(2) * E * 4);
@@ -833,7 +842,7 @@ int jepa_head_create(const jepa_head_config* cfg, jepa_head** out) {
   h->cls_w = h->ts.add("head.cls.weight", {c.n_classes, D}, false);
   h->cls_b = h->ts.add("head.cls.bias", {c.n_classes}, false);
   const size_t m = static_cast<size_t>(c.max_rows);
-  int st = h->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, 0, c.compute);
+  int st = h->ws.alloc(c.max_rows, c.embed_dim, c.ffn_dim, 0, c.compute, c.n_head);
   if (st == JEPA_OK) st = dev_alloc(h->x, m * D * 4);
   if (st == JEPA_OK) st = dev_alloc(h->kv, m * 2 * D * 4);
   if (st == JEPA_OK) st = dev_alloc(h->q, static_cast<size_t>(D) * 4);
@@ -970,21 +979,25 @@ int jepa_linear(const void* A_dev, const void* W_dev, const float* bias_dev, voi
                            out_dtype == JEPA_F32, static_cast<hipStream_t>(stream)));
 }
 
-// Workspace of the bf16 stand-alone attention: RoPE table | q', k' [M, 2D] | V^T rows.
-static size_t attn_ws_parts(int B, int N, int D, size_t* off_qk, size_t* off_vt) {
+// Workspace of the bf16 stand-alone attention: RoPE table | q', k' [M, 2D] | V^T rows |
+// key-piece buffer (long clips only).
+static size_t attn_ws_parts(int B, int N, int n_head, int head_dim, size_t* off_qk,
+                            size_t* off_vt, size_t* off_split) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const int D = n_head * head_dim;
   const size_t tab = up(static_cast<size_t>(kRopeTabEntries) * 8);
   const size_t qk = up(static_cast<size_t>(B) * N * 2 * D * 2);
-  const size_t vt = static_cast<size_t>(B) * D * vt_stride(N) * 2 + kVtSlackBytes;
+  const size_t vt = up(static_cast<size_t>(B) * D * vt_stride(N) * 2 + kVtSlackBytes);
   *off_qk = tab;
   *off_vt = tab + qk;
-  return tab + qk + vt;
+  *off_split = tab + qk + vt;
+  return tab + qk + vt + attention_split_bytes(B, N, n_head, head_dim);
 }
 
 size_t jepa_attention_workspace_size(int dtype, int B, int N, int n_head, int head_dim) {
   if (dtype != JEPA_BF16 || B <= 0 || N <= 0 || n_head <= 0 || head_dim <= 0) return 0;
-  size_t a, b;
-  return attn_ws_parts(B, N, n_head * head_dim, &a, &b);
+  size_t a, b, c;
+  return attn_ws_parts(B, N, n_head, head_dim, &a, &b, &c);
 }
 
 // Shared by jepa_attention and jepa_attention_block_causal: ids (NULL: row n is grid
@@ -1000,8 +1013,8 @@ static int attention_common(const void* qkv_dev, void* out_dev, int dtype, int B
   }
   const int D = n_head * head_dim;
   if (D % 32) return JEPA_ERR_SHAPE;
-  size_t off_qk, off_vt;
-  const size_t need = attn_ws_parts(B, N, D, &off_qk, &off_vt);
+  size_t off_qk, off_vt, off_split;
+  const size_t need = attn_ws_parts(B, N, n_head, head_dim, &off_qk, &off_vt, &off_split);
   if (!work_dev || work_bytes < need) return JEPA_ERR_ARG;
   // the kernels move 16-byte vectors
   if ((reinterpret_cast<uintptr_t>(qkv_dev) | reinterpret_cast<uintptr_t>(out_dev) |
@@ -1015,9 +1028,10 @@ static int attention_common(const void* qkv_dev, void* out_dev, int dtype, int B
   JEPA_LAUNCH(JEPA_KC_OTHER, s,
               launch_qkv_prepare(static_cast<const uint16_t*>(qkv_dev), qk, vt, Ns, B, N, n_head,
                                  head_dim, ids_dev, rs, w, attn_qscale(head_dim), s, n_cls));
+  void* split = slot > 0 ? nullptr : w + off_split;
   JEPA_LAUNCH(JEPA_KC_ATTENTION, s,
               launch_attention_fwd(qk, qk + D, 2 * D, vt, Ns, static_cast<uint16_t*>(out_dev), B, N,
-                                   n_head, head_dim, s, n_cls, slot));
+                                   n_head, head_dim, s, n_cls, slot, split));
   return JEPA_OK;
 }
 
@@ -1087,12 +1101,12 @@ int jepa_attention_noalloc(const void* qkv_dev, void* out_dev, int dtype, int B,
   void* work = nullptr;
   size_t work_bytes = 0;
   if (dtype == JEPA_BF16) {
-    size_t a, b;
+    size_t a, b, c;
     // a coarse bound first (6 bytes per q|k|v element), so that the exact size below
     // cannot overflow
     const double need = static_cast<double>(B) * N * n_head * head_dim * 6.0;
     if (need > static_cast<double>(JEPA_ATTN_SCRATCH_BYTES)) return JEPA_ERR_SHAPE;
-    if (attn_ws_parts(B, N, n_head * head_dim, &a, &b) > JEPA_ATTN_SCRATCH_BYTES) return JEPA_ERR_SHAPE;
+    if (attn_ws_parts(B, N, n_head, head_dim, &a, &b, &c) > JEPA_ATTN_SCRATCH_BYTES) return JEPA_ERR_SHAPE;
     JEPA_TRY(scratch_for_current_device(&work));
     work_bytes = JEPA_ATTN_SCRATCH_BYTES;
   }

@@ -100,6 +100,8 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+constexpr int kMaxSplit = 8;   // most key pieces per query block
+
 // Flash attention, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 softmax and accumulators,
 // on inputs prepared once per token (the QKV projection's epilogue or qkv_prepare_kernel):
 // q rotated and scaled by log2(e)/sqrt(hd), k rotated, v transposed per (clip, head) with
@@ -146,7 +148,8 @@ template <int HD, bool BC, int NG>
 __global__ __launch_bounds__(512, 1)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int ld,
                      const uint16_t* __restrict__ vt, int Ns, uint16_t* __restrict__ out, int N,
-                     int H, int nqb, int n_cls, int slot) {
+                     int H, int nqb, int n_cls, int slot, int nsplit, int tps,
+                     float* __restrict__ part) {
   constexpr int NW = 8, BQ = NW * 32 * NG, BKV = 64, S = 4;
   constexpr int KS = HD / 16;                   // MFMA k-steps over the head dim
   constexpr int DT = HD / 32;                   // 32-dim blocks of the output
@@ -170,6 +173,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // blocks of one (clip, head), which read the same keys and values, share an XCD's L2.
   int wg = blockIdx.x;
   if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
+  // the key pieces of one query block are neighbours in this order (the same XCD)
+  const int piece = BC ? 0 : wg % nsplit;
+  if (!BC) wg /= nsplit;
   int qblk = wg % nqb, bh = wg / nqb;
   if (BC) {
     // heaviest blocks first: on the XCD it lands on (blockIdx.x % 8), workgroup i takes
@@ -222,6 +228,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int jl = jbase + BQ - 1;   // the block's last query, in [0, N)
     if (jl < N - n_cls) ntiles = (limit_of(row_of(jl)) + BKV - 1) / BKV;
   }
+  // this piece's key tiles: tps from tile t0 on (all of them when nsplit is 1); below, t
+  // counts the piece's tiles and key0 + t BKV is the first key of tile t
+  const int t0 = piece * tps;
+  if (!BC) ntiles = min(tps, ntiles - t0);
+  const int key0 = t0 * BKV;
 
   // Tile t into buffer t % S: instruction i = qd*NW + wave of the tile fills 1 KB of K
   // (i < K_INS) or of V^T.  K rows past N repeat row N - 1 (their scores are masked); V^T
@@ -229,7 +240,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // launch_attention_fwd); positions of keys past N are zeroed in LDS below.
   auto issue = [&](int t) {
     const uint32_t st = sbase + (t % S) * STAGE;
-    const int kb = t * BKV;
+    const int kb = key0 + t * BKV;
 #pragma unroll
     for (int qd = 0; qd < LOADS; ++qd) {
       const int ins = qd * NW + wave;
@@ -308,9 +319,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         issue(issued);
         ++issued;
       }
-      if (t == ntiles - 1 && t * BKV + BKV > N) {
+      if (t == ntiles - 1 && key0 + t * BKV + BKV > N) {
         unsigned char* st = smem + (t % S) * STAGE;
-        const int kb = t * BKV;
+        const int kb = key0 + t * BKV;
         for (int e = tid; e < HD * BKV; e += NW * 64) {
           const int dim = e / BKV, pos = e - dim * BKV;
           if (kb + vt_pos(pos) >= N)
@@ -361,7 +372,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // Softmax of tile t's scores, the bf16 probabilities written over them, updating m_run,
   // l_run (and o on a rescale).
   auto softmax = [&](int t) __attribute__((always_inline)) {
-    const int kb = t * BKV;
+    const int kb = key0 + t * BKV;
     auto mask = [&]() __attribute__((always_inline)) {
     if (BC) {
       bool straddle = false;
@@ -543,30 +554,180 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 
   // ---- normalise and store: element i of o[g][dt] is dim 32 dt + 8(i/4) + 4h + i%4
+  auto store_out = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const float inv = 1.0f / (l_run[g] + __shfl_xor(l_run[g], 32));
+      if (qok[g]) {
+        uint16_t* dst = out + (static_cast<size_t>(b) * N + qrow[g]) * D + head * HD;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          u32x2 pk[4];
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            pk[g4][0] = pack_bf16x2(o[g][dt][4 * g4] * inv, o[g][dt][4 * g4 + 1] * inv);
+            pk[g4][1] = pack_bf16x2(o[g][dt][4 * g4 + 2] * inv, o[g][dt][4 * g4 + 3] * inv);
+          }
+          // lanes l and l + 32 hold the same query row (qok is the same for both)
+          store_row32_bf16(dst + dt * 32, pk, h);
+        }
+      }
+    }
+  };
+  if (BC || nsplit == 1) {
+    store_out();
+    return;
+  }
+
+  // ---- key pieces: each leaves its unnormalised state (o, and the lane's m_run, l_run) in
+  // `part`, one record per (query block, piece, wave, group) in the lanes' register order;
+  // attn_merge_kernel combines them after this launch.
+  constexpr int REC = (DT * 16 + 2) * 64;       // floats per (wave, group) record
+  float* r = part + ((static_cast<size_t>(bh * nqb + qblk) * nsplit + piece) * NW + wave) * (NG * REC);
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const float inv = 1.0f / (l_run[g] + __shfl_xor(l_run[g], 32));
-    if (qok[g]) {
-      uint16_t* dst = out + (static_cast<size_t>(b) * N + qrow[g]) * D + head * HD;
+    f32x4* po = reinterpret_cast<f32x4*>(r + g * REC);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 v = {o[g][dt][4 * i4], o[g][dt][4 * i4 + 1], o[g][dt][4 * i4 + 2], o[g][dt][4 * i4 + 3]};
+        po[(dt * 4 + i4) * 64 + lane] = v;
+      }
+    const f32x2 ml = {m_run[g], l_run[g]};
+    reinterpret_cast<f32x2*>(r + g * REC + DT * 16 * 64)[lane] = ml;
+  }
+}
+
+// The pieces of one (query block, wave) merged in piece order: the running states are
+// brought to their largest max, summed, normalised and stored as the kernel above stores
+// a block it took whole.  One 64-thread workgroup per (query block, wave); lane l plays
+// the part of lane l of that wave.
+template <int HD, int NG>
+__global__ __launch_bounds__(64)
+void attn_merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ out, int N, int H,
+                       int nqb, int nsplit) {
+  constexpr int NW = 8, BQ = NW * 32 * NG, DT = HD / 32;
+  constexpr int REC = (DT * 16 + 2) * 64;
+  const int lane = threadIdx.x, h = lane >> 5, l32 = lane & 31;
+  const int wave = blockIdx.x % NW, unit = blockIdx.x / NW;
+  const int qblk = unit % nqb, bh = unit / nqb;
+  const int head = bh % H, b = bh / H;
+  const int D = H * HD;
+  auto rec = [&](int p, int g) __attribute__((always_inline)) {
+    return part + ((static_cast<size_t>(unit) * nsplit + p) * NW + wave) * (NG * REC) + g * REC;
+  };
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int j = qblk * BQ + wave * (32 * NG) + g * 32 + l32;
+    // (loops unrolled over the largest piece count, so that mp stays in registers)
+    float mp[kMaxSplit];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kMaxSplit; ++p)
+      if (p < nsplit) {
+        mp[p] = reinterpret_cast<const f32x2*>(rec(p, g) + DT * 16 * 64)[lane][0];
+        mx = fmaxf(mx, mp[p]);
+      }
+    f32x16 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+    float l = 0.f;
+#pragma unroll
+    for (int p = 0; p < kMaxSplit; ++p) {
+      if (p >= nsplit) break;
+      const float w = __builtin_amdgcn_exp2f(mp[p] - mx);
+      l = fmaf(reinterpret_cast<const f32x2*>(rec(p, g) + DT * 16 * 64)[lane][1], w, l);
+      const f32x4* po = reinterpret_cast<const f32x4*>(rec(p, g));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 v = po[(dt * 4 + i4) * 64 + lane];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o[dt][4 * i4 + c] = fmaf(v[c], w, o[dt][4 * i4 + c]);
+        }
+    }
+    // element i of o[dt] is dim 32 dt + 8(i/4) + 4h + i%4 of query j; lanes l and l + 32
+    // hold the same query and split its row sum
+    const float inv = 1.0f / (l + __shfl_xor(l, 32));
+    if (j < N) {
+      uint16_t* dst = out + (static_cast<size_t>(b) * N + j) * D + head * HD;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         u32x2 pk[4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          pk[g4][0] = pack_bf16x2(o[g][dt][4 * g4] * inv, o[g][dt][4 * g4 + 1] * inv);
-          pk[g4][1] = pack_bf16x2(o[g][dt][4 * g4 + 2] * inv, o[g][dt][4 * g4 + 3] * inv);
+          pk[g4][0] = pack_bf16x2(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv);
+          pk[g4][1] = pack_bf16x2(o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv);
         }
-        // lanes l and l + 32 hold the same query row (qok is the same for both)
         store_row32_bf16(dst + dt * 32, pk, h);
       }
     }
   }
 }
 
+// How the bf16 kernel covers a clip of N tokens: NG query groups of 32 per wave (256 NG
+// queries per workgroup), nqb query blocks, and the keys of each block in nsplit pieces
+// of tps tiles.  Everything here follows from N and the head count, never from the
+// batch, so a clip's result does not depend on the batch it comes in.
+//   * Short clips (at most 1024 keys) take one group per wave: twice the workgroups for the
+//     few (clip, head) pairs.
+//   * From 4096 keys on, when one clip's (head, query block) pairs would leave compute
+//     units idle in the last round (the 2048 + 6144-token predictor: 192 pairs on 256
+//     units), the keys are cut into pieces if the estimated time of one clip, rounds of
+//     the units times (tiles per piece + a piece's fixed cost), drops by a tenth or more.
+//     A large batch of such clips then pays that fixed cost per piece.
+struct AttnPlan {
+  int ng, nqb, nsplit, tps;
+};
+constexpr int kAttnShortN = 1024;   // longest clip that takes 256-query workgroups
+constexpr int kSplitMinN = 4096;    // shortest clip whose keys may be cut into pieces
+constexpr int kSplitCUs = 256;      // compute units the pieces are counted against
+constexpr int kPieceCost = 4;       // a piece's prologue, record and merge, in key tiles
+
+static AttnPlan attn_plan(int N, int n_head, bool bc) {
+  AttnPlan p;
+  p.ng = (!bc && N <= kAttnShortN) ? 1 : 2;
+  const int bq = 256 * p.ng, ntiles = (N + 63) / 64;
+  p.nqb = (N + bq - 1) / bq;
+  p.nsplit = 1;
+  p.tps = ntiles;
+  if (bc || N < kSplitMinN) return p;
+  const long long pairs = static_cast<long long>(n_head) * p.nqb;
+  auto cost = [&](int tps) {
+    const long long wgs = pairs * ((ntiles + tps - 1) / tps);
+    return (wgs + kSplitCUs - 1) / kSplitCUs * (tps + kPieceCost);
+  };
+  const long long whole = cost(ntiles);
+  long long best = whole;
+  for (int sp = 2; sp <= kMaxSplit; ++sp) {
+    const int tps = (ntiles + sp - 1) / sp;
+    const long long c = cost(tps);
+    if (10 * c <= 9 * whole && c < best) {
+      best = c;
+      p.tps = tps;
+      p.nsplit = (ntiles + tps - 1) / tps;
+    }
+  }
+  return p;
+}
+
+size_t attention_split_bytes(int B, int N, int n_head, int head_dim) {
+  if (B <= 0 || N <= 0 || n_head <= 0 || (head_dim != 64 && head_dim != 32)) return 0;
+  const AttnPlan p = attn_plan(N, n_head, false);
+  if (p.nsplit == 1) return 0;
+  // one fp32 record of (o, m_run, l_run) per (query block, piece, wave, group, lane)
+  const size_t units = static_cast<size_t>(B) * n_head * p.nqb;
+  return units * p.nsplit * 8 * p.ng * static_cast<size_t>(head_dim / 2 + 2) * 64 * 4;
+}
+
 template <int HD, bool BC, int NG>
 static hipError_t attn_launch(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt, int Ns,
                               uint16_t* out, int B, int N, int n_head, int n_cls, int slot,
-                              hipStream_t s) {
+                              const AttnPlan& p, void* split_ws, hipStream_t s) {
   constexpr int LDS = 4 * (64 * HD * 2 + HD * 64 * 2);
   static bool configured = false;
   if (!configured) {
@@ -575,17 +736,26 @@ static hipError_t attn_launch(const uint16_t* q, const uint16_t* k, int ld, cons
     if (e != hipSuccess) return e;
     configured = true;
   }
-  constexpr int BQ = 8 * 32 * NG;   // queries per workgroup
-  const int nqb = (N + BQ - 1) / BQ;
-  const dim3 grid(nqb * n_head * B);
-  attn_fwd_kernel<HD, BC, NG><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, nqb, n_cls, slot);
+  const size_t units = static_cast<size_t>(p.nqb) * n_head * B;
+  if (units * p.nsplit * 8 > 0x7fffffffu) return hipErrorInvalidValue;
+  float* part = static_cast<float*>(split_ws);
+  if (p.nsplit > 1 && (!part || reinterpret_cast<uintptr_t>(part) % 16)) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(units * p.nsplit));
+  attn_fwd_kernel<HD, BC, NG><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, p.nqb, n_cls,
+                                                      slot, p.nsplit, p.tps, part);
+  if (p.nsplit == 1) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (!BC) {
+    attn_merge_kernel<HD, NG><<<static_cast<unsigned>(units * 8), 64, 0, s>>>(part, out, N, n_head,
+                                                                             p.nqb, p.nsplit);
+  }
   return hipGetLastError();
 }
 
-constexpr int kAttnShortN = 1024;   // longest clip that takes 256-query workgroups
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
                                 int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
-                                hipStream_t s, int n_cls, int slot) {
+                                hipStream_t s, int n_cls, int slot, void* split_ws) {
   if (B <= 0 || N <= 0) return hipSuccess;
   if ((head_dim != 64 && head_dim != 32) || Ns < vt_stride(N) || Ns % 16 || ld % 8) return hipErrorInvalidValue;
   // 32-bit DMA offsets: one clip's rows of q/k and one (clip, head)'s V^T rows
@@ -595,18 +765,17 @@ hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, co
   if (slot > 0) {
     // the first key tile must hold a key every query sees (key n_cls)
     if (n_cls < 0 || n_cls >= 64 || n_cls >= N) return hipErrorInvalidValue;
-    if (head_dim == 64) return attn_launch<64, true, 2>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, s);
-    return attn_launch<32, true, 2>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, s);
+    const AttnPlan p = attn_plan(N, n_head, true);
+    if (head_dim == 64) return attn_launch<64, true, 2>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, p, nullptr, s);
+    return attn_launch<32, true, 2>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, p, nullptr, s);
   }
-  // Short clips (at most 1024 keys) take 256-query workgroups, one group of 32 queries per
-  // wave: twice the workgroups for the few (clip, head) pairs.  The choice depends on N
-  // only, so a clip's result does not depend on the batch it comes in.
-  if (N <= kAttnShortN) {
-    if (head_dim == 64) return attn_launch<64, false, 1>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
-    return attn_launch<32, false, 1>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
+  const AttnPlan p = attn_plan(N, n_head, false);
+  if (p.ng == 1) {
+    if (head_dim == 64) return attn_launch<64, false, 1>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, p, split_ws, s);
+    return attn_launch<32, false, 1>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, p, split_ws, s);
   }
-  if (head_dim == 64) return attn_launch<64, false, 2>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
-  return attn_launch<32, false, 2>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, s);
+  if (head_dim == 64) return attn_launch<64, false, 2>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, p, split_ws, s);
+  return attn_launch<32, false, 2>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, p, split_ws, s);
 }
 
 // Attention inputs from a projection already in memory (the stand-alone entry point): one

@@ -65,9 +65,17 @@ hipError_t launch_qkv_prepare(const uint16_t* qkv, uint16_t* qk, uint16_t* vt, i
 // out [B*N, H*hd] bf16.  slot > 0: block-causal mask with n_cls (< 64) leading CLS rows
 // that see every key, the other rows in temporal slots of `slot` tokens that see the
 // non-CLS keys of their own and earlier slots.
+// Long clips whose (head, query block) pairs would fill the compute units poorly take
+// their keys in pieces, merged by a second kernel (a choice made from N and n_head
+// only); those need split_ws, attention_split_bytes(B, N, n_head, head_dim) bytes
+// (16-byte aligned, contents on entry do not matter).  Calls that overlap on one split_ws
+// race.
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt,
                                 int Ns, uint16_t* out, int B, int N, int n_head, int head_dim,
-                                hipStream_t s, int n_cls = 0, int slot = 0);
+                                hipStream_t s, int n_cls = 0, int slot = 0,
+                                void* split_ws = nullptr);
+// Bytes of split_ws for B unmasked clips of N tokens (0: the keys are taken whole).
+size_t attention_split_bytes(int B, int N, int n_head, int head_dim);
 // Row stride (keys) of the transposed V layout for N tokens.
 inline int vt_stride(int N) { return (N + 15) / 16 * 16; }
 // Scale folded into q: log2(e) / sqrt(head_dim).
