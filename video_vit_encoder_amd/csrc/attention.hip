@@ -144,7 +144,7 @@ constexpr int kMaxSplit = 8;   // most key pieces per query block
 // last slot, needs them all), so the work follows the mask's density.  Scores outside
 // [lo, lim) become -inf in the tiles that straddle a limit.  The heaviest blocks start
 // first.
-template <int HD, bool BC, int NG>
+template <int HD, bool BC, int NG, bool SPLIT>
 __global__ __launch_bounds__(512, 1)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int ld,
                      const uint16_t* __restrict__ vt, int Ns, uint16_t* __restrict__ out, int N,
@@ -173,9 +173,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // blocks of one (clip, head), which read the same keys and values, share an XCD's L2.
   int wg = blockIdx.x;
   if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
-  // the key pieces of one query block are neighbours in this order (the same XCD)
-  const int piece = BC ? 0 : wg % nsplit;
-  if (!BC) wg /= nsplit;
+  // SPLIT: the key pieces of one query block are neighbours in this order (the same XCD)
+  const int piece = SPLIT ? wg % nsplit : 0;
+  if (SPLIT) wg /= nsplit;
   int qblk = wg % nqb, bh = wg / nqb;
   if (BC) {
     // heaviest blocks first: on the XCD it lands on (blockIdx.x % 8), workgroup i takes
@@ -228,10 +228,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int jl = jbase + BQ - 1;   // the block's last query, in [0, N)
     if (jl < N - n_cls) ntiles = (limit_of(row_of(jl)) + BKV - 1) / BKV;
   }
-  // this piece's key tiles: tps from tile t0 on (all of them when nsplit is 1); below, t
-  // counts the piece's tiles and key0 + t BKV is the first key of tile t
-  const int t0 = piece * tps;
-  if (!BC) ntiles = min(tps, ntiles - t0);
+  // SPLIT: this piece's key tiles, tps from tile t0 on; below, t counts the piece's tiles
+  // and key0 + t BKV is the first key of tile t
+  const int t0 = SPLIT ? piece * tps : 0;
+  if (SPLIT) ntiles = min(tps, ntiles - t0);
   const int key0 = t0 * BKV;
 
   // Tile t into buffer t % S: instruction i = qd*NW + wave of the tile fills 1 KB of K
@@ -574,7 +574,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     }
   };
-  if (BC || nsplit == 1) {
+  if (!SPLIT) {
     store_out();
     return;
   }
@@ -687,6 +687,7 @@ constexpr int kAttnShortN = 1024;   // longest clip that takes 256-query workgro
 constexpr int kSplitMinN = 4096;    // shortest clip whose keys may be cut into pieces
 constexpr int kSplitCUs = 256;      // compute units the pieces are counted against
 constexpr int kPieceCost = 4;       // a piece's prologue, record and merge, in key tiles
+static_assert(kSplitMinN > kAttnShortN, "clips in pieces take two query groups per wave");
 
 static AttnPlan attn_plan(int N, int n_head, bool bc) {
   AttnPlan p;
@@ -724,29 +725,29 @@ size_t attention_split_bytes(int B, int N, int n_head, int head_dim) {
   return units * p.nsplit * 8 * p.ng * static_cast<size_t>(head_dim / 2 + 2) * 64 * 4;
 }
 
-template <int HD, bool BC, int NG>
+template <int HD, bool BC, int NG, bool SPLIT = false>
 static hipError_t attn_launch(const uint16_t* q, const uint16_t* k, int ld, const uint16_t* vt, int Ns,
                               uint16_t* out, int B, int N, int n_head, int n_cls, int slot,
                               const AttnPlan& p, void* split_ws, hipStream_t s) {
   constexpr int LDS = 4 * (64 * HD * 2 + HD * 64 * 2);
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<HD, BC, NG>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<HD, BC, NG, SPLIT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const size_t units = static_cast<size_t>(p.nqb) * n_head * B;
   if (units * p.nsplit * 8 > 0x7fffffffu) return hipErrorInvalidValue;
+  if ((p.nsplit > 1) != SPLIT) return hipErrorInvalidValue;
   float* part = static_cast<float*>(split_ws);
-  if (p.nsplit > 1 && (!part || reinterpret_cast<uintptr_t>(part) % 16)) return hipErrorInvalidValue;
+  if (SPLIT && (!part || reinterpret_cast<uintptr_t>(part) % 16)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(units * p.nsplit));
-  attn_fwd_kernel<HD, BC, NG><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, p.nqb, n_cls,
-                                                      slot, p.nsplit, p.tps, part);
-  if (p.nsplit == 1) return hipGetLastError();
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if constexpr (!BC) {
+  attn_fwd_kernel<HD, BC, NG, SPLIT><<<grid, 512, LDS, s>>>(q, k, ld, vt, Ns, out, N, n_head, p.nqb,
+                                                             n_cls, slot, p.nsplit, p.tps, part);
+  if constexpr (SPLIT) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     attn_merge_kernel<HD, NG><<<static_cast<unsigned>(units * 8), 64, 0, s>>>(part, out, N, n_head,
                                                                              p.nqb, p.nsplit);
   }
@@ -770,6 +771,10 @@ hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, int ld, co
     return attn_launch<32, true, 2>(q, k, ld, vt, Ns, out, B, N, n_head, n_cls, slot, p, nullptr, s);
   }
   const AttnPlan p = attn_plan(N, n_head, false);
+  if (p.nsplit > 1) {   // (only from 4096 keys on, so with two query groups per wave)
+    if (head_dim == 64) return attn_launch<64, false, 2, true>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, p, split_ws, s);
+    return attn_launch<32, false, 2, true>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, p, split_ws, s);
+  }
   if (p.ng == 1) {
     if (head_dim == 64) return attn_launch<64, false, 1>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, p, split_ws, s);
     return attn_launch<32, false, 1>(q, k, ld, vt, Ns, out, B, N, n_head, 0, 0, p, split_ws, s);
