@@ -580,10 +580,17 @@ static int tile_width(int M, int N, int max_w = 256) {
   return best;
 }
 
-// Whether 256 x 128 tiles would be fewer than the CUs: then 128-row tiles are used.  The
-// tile shape does not change the order in which an output element sums over K.
+// Whether 128-row tiles are used: only when 256 x 128 tiles would be fewer than the CUs,
+// and then by the same estimate as tile_width (rounds of the CUs times the rows a tile
+// streams per slab), so that 9216 rows of N = 768 take one round of 216 tiles of 256 x 128
+// rather than 1.7 rounds of 432 tiles of 128 x 128, while 2048 rows keep the small tiles.
+// The tile shape does not change the order in which an output element sums over K.
 static bool short_rows(int M, int N) {
-  return static_cast<long long>((M + 255) / 256) * (N / 128) < num_cus();
+  const long long cus = num_cus();
+  const long long t256 = static_cast<long long>((M + 255) / 256) * (N / 128);
+  if (t256 >= cus) return false;
+  const long long t128 = static_cast<long long>((M + 127) / 128) * (N / 128);
+  return (t128 + cus - 1) / cus * (128 + 128) < (t256 + cus - 1) / cus * (256 + 128);
 }
 
 static bool gemm_shape_ok(int M, int N, int K) {
