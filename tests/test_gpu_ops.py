@@ -186,6 +186,9 @@ LINEAR_CASES = [
     (8192 - 5, 4096, 1024, J.JEPA_EPI_GELU, "bf16"),
     (8192 - 77, 3072, 1024, J.JEPA_EPI_STORE, "bf16"),
     (8192 - 130, 1024, 4096, J.JEPA_EPI_RESIDUAL, "f32"),
+    # fewer 256 x 128 tiles than CUs (216), yet one round of them beats 1.7 rounds of
+    # 128 x 128 tiles: the 2.1 image path's down-projection shape, ragged
+    (9216 - 19, 768, 3072, J.JEPA_EPI_RESIDUAL, "f32"),
     # shallow K with many tiles per workgroup: K = 64 (one slab per tile) on 256x256 tiles
     # (4 tiles per CU) and K = 128 on 256x128 tiles (3-slab ring, 2-3 tiles per CU); every
     # tile's bias must be its own although the slab ring runs several tiles ahead

@@ -5,7 +5,8 @@ forward").
 
   * tiny fp32 encoder (interleaved, interpolated, modality vectors) on a 64x64 image:
     fp32 gate;
-  * 2.1 ViT-B/16 on a 384x384 image (576 tokens, 12 layers, bf16): bf16 gate;
+  * 2.1 ViT-B/16 on a 384x384 image (576 tokens, 12 layers, bf16): bf16 gate; 16 such
+    images give each image's tokens bit for bit as it alone does (other GEMM tiles);
   * 2.1 ViT-B predictor, full 12 blocks, on the 24x24 image grid (64 context, 512 targets,
     image vector): predictions and projected context rows within the bf16 gate, while
     the oracle's video-vector output fails it (the pages' wrong-vector case); AUTO picks
@@ -57,6 +58,26 @@ def test_vitb16_image_384():
     ref = oracle.encoder_forward_image(img[0], W, spec)
     assert_bf16_gate(got, ref, "vitb image 384")
 
+
+
+def test_vitb16_image_384_batch_of_16_equals_single():
+    # 16 images (9216 rows) take one round of 256 x 128 tiles in the N = 768 projections and
+    # 256-row tiles in QKV, a single image (576 rows) 128 x 128 tiles; every output element
+    # sums over K in the same order with any tile, so each image's tokens are the same bits
+    # alone and in the batch
+    w = synth.workload("vitb16_img384")
+    banner("2.1 ViT-B image 384x384: 16 images against images 0 and 15 alone")
+    e = w["enc"]
+    W = synth.encoder_weights(e, seed=0, dtype="bf16")
+    imgs = synth.clip_u8(33, 16, 1, 384, 384)[:, 0]
+    enc = J.Encoder(e.embed_dim, e.n_layer, e.n_head, e.ffn_dim, layout="interleaved", ref_grid=16,
+                    has_mod_embed=True, dtype="bf16", max_rows=16 * 576, has_image_embed=True)
+    enc.set_weights(W)
+    batch = host(enc.encode_image(u8(imgs)))
+    assert batch.shape == (16, 576, e.embed_dim) and np.all(np.isfinite(batch))
+    for i in (0, 15):
+        one = host(enc.encode_image(u8(imgs[i:i + 1])))[0]
+        assert np.array_equal(one, batch[i]), (i, float(np.max(np.abs(one - batch[i]))))
 
 def _pred(w, n_layer=None):
     p = w["pred"]
