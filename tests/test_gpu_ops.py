@@ -258,6 +258,9 @@ ATTN_CASES = [
     # piece short, its last tile ragged at 4205 tokens), merged at the end
     ("hd64 4205 tokens in key pieces", 1, (5, 29, 29), 2, 64, "tiled", 0, None, "bf16"),
     ("hd32 2 x 4608 tokens in key pieces", 2, (8, 24, 24), 2, 32, "interleaved", 16, None, "bf16"),
+    # 4225 tokens: 8 pieces of 9 tiles but the last, of 4 tiles whose last holds one key
+    ("hd32 4225 tokens, one key in the last piece's last tile", 1, (25, 13, 13), 2, 32, "tiled", 0,
+     None, "bf16"),
     ("hd64 f32 tiny grid", 1, (2, 4, 4), 12, 64, "tiled", 0, None, "f32"),
     ("hd64 f32 ragged", 2, (3, 7, 5), 2, 64, "interleaved", 16, None, "f32"),
     ("hd32 f32 ids", 1, (2, 6, 6), 3, 32, "tiled", 0, "perm", "f32"),
