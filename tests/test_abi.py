@@ -121,6 +121,36 @@ def test_standalone_ops_validate_before_launch():
     assert lib.jepa_attention_workspace_size(1, 0, 8, 1, 64) == 0
 
 
+
+def _attn_ws_without_pieces(B, N, H, hd):
+    # RoPE table (3 axes x 64 coordinates x 16 frequencies of (cos, sin)) | q', k' bf16
+    # [B N, 2 D] | V^T bf16 [B][H][hd][N up to 16] + 4 KB read past the last row, each part
+    # rounded up to 256 bytes
+    up = lambda v: (v + 255) // 256 * 256
+    D = H * hd
+    return up(3 * 64 * 16 * 8) + up(B * N * 2 * D * 2) + up(B * D * ((N + 15) // 16 * 16) * 2 + 4096)
+
+
+@pytest.mark.parametrize("B,N,H,hd,blocks,pieces", [
+    # (clip, head) pairs of 512-query blocks against 256 compute units
+    (4, 2048, 16, 64, 4, 1),     # ViT-L at 16 frames: below 4096 tokens, keys whole
+    (1, 18432, 12, 64, 36, 1),   # 2.1 ViT-B at 18,432: 432 pairs, pieces would not save a tenth
+    (1, 8192, 16, 64, 16, 1),    # ViT-L at 64 frames: 256 pairs, one full round
+    (1, 8192, 12, 32, 16, 4),    # V-JEPA 2 predictor: 192 pairs -> 768 workgroups, 3 rounds
+    (1, 4608, 12, 32, 9, 2),     # 2.1 predictor: 108 pairs -> 216 workgroups
+    (3, 4608, 12, 32, 9, 2),     # the same clips in a batch: the same pieces
+    (1, 4096, 16, 64, 8, 2),     # ViT-L at 32 frames, one clip: 128 pairs -> 256
+    (1, 4225, 2, 32, 9, 8),      # few heads: 18 pairs, the most pieces
+    (1, 4095, 2, 32, 8, 1),      # below 4096 tokens
+])
+def test_attention_key_pieces_follow_clip_length_and_heads(B, N, H, hd, blocks, pieces):
+    """The flash kernel's key pieces, read off the workspace size on the host: the records
+    take (hd/2 + 2) fp32 values per lane, 64 lanes, 2 query groups and 8 waves per (clip,
+    head, query block, piece), and the piece count depends on N and the head count only."""
+    got = _lib.load().jepa_attention_workspace_size(1, B, N, H, hd)
+    rec = 0 if pieces == 1 else B * H * blocks * pieces * 8 * 2 * (hd // 2 + 2) * 64 * 4
+    assert got == _attn_ws_without_pieces(B, N, H, hd) + rec
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libjepa.so"))
     monkeypatch.setattr(_lib, "_lib", None)
