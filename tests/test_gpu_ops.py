@@ -189,6 +189,9 @@ LINEAR_CASES = [
     # fewer 256 x 128 tiles than CUs (216), yet one round of them beats 1.7 rounds of
     # 128 x 128 tiles: the 2.1 image path's down-projection shape, ragged
     (9216 - 19, 768, 3072, J.JEPA_EPI_RESIDUAL, "f32"),
+    # 2048 rows (the masked forward) at N = 1024: one round of 256 tiles of 128 x 64, ragged
+    (2048 - 3, 1024, 4096, J.JEPA_EPI_RESIDUAL, "f32"),
+    (2048 - 3, 1024, 1024, J.JEPA_EPI_STORE, "bf16"),
     # shallow K with many tiles per workgroup: K = 64 (one slab per tile) on 256x256 tiles
     # (4 tiles per CU) and K = 128 on 256x128 tiles (3-slab ring, 2-3 tiles per CU); every
     # tile's bias must be its own although the slab ring runs several tiles ahead

@@ -116,6 +116,9 @@ using Cfg256x128q = GemmCfg<256, 128, 2, 4, 2>;
 // token rows, as in the masked forward, or narrow outputs such as N = 384)
 using Cfg128x128 = GemmCfg<128, 128, 4, 2, 4>;
 using Cfg128x128q = GemmCfg<128, 128, 3, 2, 4>;
+// 128 x 64 (waves of 32 x 32): twice the 128 x 128 tiles where those would still leave
+// CUs idle (the masked forward's 2048 rows at N = 1024)
+using Cfg128x64 = GemmCfg<128, 64, 4, 4, 2>;
 
 template <class C, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(C::NT)
@@ -604,7 +607,14 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* W, const float* b
                             int M, int N, int K, int epi, int out_f32, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (!gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
-  if (short_rows(M, N)) return gemm_dispatch<Cfg128x128>(A, W, bias, C, M, N, K, epi, out_f32, s);
+  if (short_rows(M, N)) {
+    // 128 x 64 tiles when they take fewer rounds x rows streamed per slab (128 + 64)
+    const long long cus = num_cus(), tm = (M + 127) / 128;
+    const long long r128 = (tm * (N / 128) + cus - 1) / cus, r64 = (tm * (N / 64) + cus - 1) / cus;
+    if (r64 * (128 + 64) < r128 * (128 + 128))
+      return gemm_dispatch<Cfg128x64>(A, W, bias, C, M, N, K, epi, out_f32, s);
+    return gemm_dispatch<Cfg128x128>(A, W, bias, C, M, N, K, epi, out_f32, s);
+  }
   const int tw = tile_width(M, N);
   if (tw == 256) return gemm_dispatch<Cfg256x256>(A, W, bias, C, M, N, K, epi, out_f32, s);
   if (tw == 192) return gemm_dispatch<Cfg256x192>(A, W, bias, C, M, N, K, epi, out_f32, s);
