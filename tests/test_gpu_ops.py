@@ -143,7 +143,11 @@ def test_rope3d_empty_and_errors():
 
 
 @pytest.mark.parametrize("D,M,out", [(1024, 2048 + 37, "f32"), (768, 301, "bf16"),
-                                     (384, 130, "bf16"), (1024, 5, "bf16"), (768, 64, "f32")])
+                                     (384, 130, "bf16"), (1024, 5, "bf16"), (768, 64, "f32"),
+                                     # two rows per wavefront (half-wave rows, 16-byte chunks),
+                                     # an odd row count leaving the last half wave idle
+                                     (384, 8192 + 3, "f32"), (640, 77, "bf16"), (128, 9, "f32"),
+                                     (1408, 33, "bf16")])
 def test_layernorm(D, M, out):
     import torch
     banner("layernorm", D, M, out)

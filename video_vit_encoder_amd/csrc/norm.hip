@@ -1,10 +1,12 @@
-// LayerNorm over rows of an fp32 [M, D] matrix, one wavefront per row.
+// LayerNorm over rows of an fp32 [M, D] matrix, one wavefront (or half of one) per row.
 //
 // [Notes §1]: eps = 1e-6.  The variance is centred (mean first, then the mean of the
 // squared deviations), as the CPU backend of [Parity "Parity on a GPU"] does; both
 // passes run over the row held in registers, so HBM sees one read and one write.
-// Lane l owns the vector chunks l, l+64, l+128, ... of VEC floats each (VEC = 4 when
-// D is a multiple of 256, else 2 or 1), so every wave-wide access is contiguous.
+// Lane l of a row's LANES lanes owns the vector chunks l, l+LANES, l+2 LANES, ... of VEC
+// floats each, so every access of those lanes is contiguous.  LANES is 64 (VEC = 4 when D is
+// a multiple of 256, else 2 or 1), or 32 where that gives 16-byte chunks instead of 8-byte
+// ones (D = 384, 640, 1408): two rows per wavefront, and one reduction step fewer.
 // The final norm of a forward runs in place (out == x), so x and out may alias: neither
 // is declared __restrict__.
 #include "common.h"
@@ -12,20 +14,23 @@
 
 namespace jepa {
 
-template <int VPT, int VEC, bool OUT_BF16>
+template <int VPT, int VEC, int LANES, bool OUT_BF16>
 __global__ __launch_bounds__(256)
 void layernorm_kernel(const float* x, const float* __restrict__ w,
                       const float* __restrict__ b, int M, float eps, void* out) {
-  constexpr int D = VPT * 64;
+  static_assert(LANES == 64 || LANES == 32, "a row takes a wavefront or half of one");
+  constexpr int D = VPT * LANES;
   constexpr int NV = VPT / VEC;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & (LANES - 1);
+  const int row = blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
+  // (a half wave that returns here leaves the other half's reductions intact: they
+  // exchange only within their own LANES lanes)
   if (row >= M) return;
   const float* xr = x + static_cast<size_t>(row) * D;
   float v[VPT];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int c = (j * 64 + lane) * VEC;
+    const int c = (j * LANES + lane) * VEC;
     if constexpr (VEC == 4) {
       const f32x4 t = *reinterpret_cast<const f32x4*>(xr + c);
       v[j * 4 + 0] = t[0]; v[j * 4 + 1] = t[1]; v[j * 4 + 2] = t[2]; v[j * 4 + 3] = t[3];
@@ -40,7 +45,7 @@ void layernorm_kernel(const float* x, const float* __restrict__ w,
 #pragma unroll
   for (int i = 0; i < VPT; ++i) s += v[i];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  for (int o = LANES / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
   const float mean = s * (1.0f / D);
   float q = 0.f;
 #pragma unroll
@@ -49,11 +54,11 @@ void layernorm_kernel(const float* x, const float* __restrict__ w,
     q += v[i] * v[i];
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) q += __shfl_xor(q, o);
+  for (int o = LANES / 2; o > 0; o >>= 1) q += __shfl_xor(q, o);
   const float rstd = 1.0f / sqrtf(q * (1.0f / D) + eps);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int c = (j * 64 + lane) * VEC;
+    const int c = (j * LANES + lane) * VEC;
     float y[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) y[e] = v[j * VEC + e] * rstd * w[c + e] + b[c + e];
@@ -82,15 +87,19 @@ void layernorm_kernel(const float* x, const float* __restrict__ w,
   }
 }
 
-template <int VPT>
+template <int VPT64>
 static hipError_t ln_dispatch(const float* x, const float* w, const float* b, int M, float eps,
                               void* out, int out_bf16, hipStream_t s) {
+  // D = 64 VPT64: half-wave rows where that turns 8-byte chunks into 16-byte ones
+  constexpr int LANES = (VPT64 % 4 == 2) ? 32 : 64;
+  constexpr int VPT = VPT64 * 64 / LANES;
   constexpr int VEC = (VPT % 4 == 0) ? 4 : ((VPT % 2 == 0) ? 2 : 1);
-  const dim3 grid((M + 3) / 4);
+  constexpr int RPB = 256 / LANES;   // rows per workgroup
+  const dim3 grid((M + RPB - 1) / RPB);
   if (out_bf16)
-    layernorm_kernel<VPT, VEC, true><<<grid, 256, 0, s>>>(x, w, b, M, eps, out);
+    layernorm_kernel<VPT, VEC, LANES, true><<<grid, 256, 0, s>>>(x, w, b, M, eps, out);
   else
-    layernorm_kernel<VPT, VEC, false><<<grid, 256, 0, s>>>(x, w, b, M, eps, out);
+    layernorm_kernel<VPT, VEC, LANES, false><<<grid, 256, 0, s>>>(x, w, b, M, eps, out);
   return hipGetLastError();
 }
 
