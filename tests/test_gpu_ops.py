@@ -265,6 +265,9 @@ ATTN_CASES = [
     # piece short, its last tile ragged at 4205 tokens), merged at the end
     ("hd64 4205 tokens in key pieces", 1, (5, 29, 29), 2, 64, "tiled", 0, None, "bf16"),
     ("hd32 2 x 4608 tokens in key pieces", 2, (8, 24, 24), 2, 32, "interleaved", 16, None, "bf16"),
+    # a ViT-L clip of 32 frames: 16 heads of 64 over 4096 tokens, keys in 2 pieces
+    ("hd64 4096 tokens, 16 heads, keys in 2 pieces", 1, (16, 16, 16), 16, 64, "tiled", 0, None,
+     "bf16"),
     # 4225 tokens: 8 pieces of 9 tiles but the last, of 4 tiles whose last holds one key
     ("hd32 4225 tokens, one key in the last piece's last tile", 1, (25, 13, 13), 2, 32, "tiled", 0,
      None, "bf16"),
