@@ -166,14 +166,15 @@ def test_layernorm(D, M, out):
         assert np.all(np.abs(got - ref) <= BF16_ULP * np.abs(ref) + 1e-5)
 
 
-def test_layernorm_in_place():
-    banner("layernorm in place")
+@pytest.mark.parametrize("D", [1024, 384])   # a row per wavefront; two per wavefront
+def test_layernorm_in_place(D):
+    banner("layernorm in place", D)
     rng = np.random.default_rng(2)
-    x = rng.standard_normal((77, 1024)).astype(np.float32)
+    x = rng.standard_normal((77, D)).astype(np.float32)
     xd = f32(x)
-    ones, zeros = f32(np.ones(1024)), f32(np.zeros(1024))
+    ones, zeros = f32(np.ones(D)), f32(np.zeros(D))
     J.jepa_layernorm(xd, ones, zeros, 1e-6, xd)
-    ref = oracle.layer_norm(x.astype(np.float64), np.ones(1024), np.zeros(1024), 1e-6)
+    ref = oracle.layer_norm(x.astype(np.float64), np.ones(D), np.zeros(D), 1e-6)
     assert metrics.rel_max(host(xd), ref) <= 2e-6
 
 
