@@ -599,10 +599,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 }
 
-// The pieces of one (query block, wave) merged in piece order: the running states are
-// brought to their largest max, summed, normalised and stored as the kernel above stores
-// a block it took whole.  One 64-thread workgroup per (query block, wave); lane l plays
-// the part of lane l of that wave.
+// The pieces of one (query block, wave, group) merged in piece order: the running states
+// are brought to their largest max, summed, normalised and stored as the kernel above
+// stores a block it took whole.  One 64-thread workgroup per (query block, wave, group),
+// so that many waves keep record reads in flight; lane l plays the part of lane l of that
+// wave.
 template <int HD, int NG>
 __global__ __launch_bounds__(64)
 void attn_merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ out, int N, int H,
@@ -610,15 +611,14 @@ void attn_merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ ou
   constexpr int NW = 8, BQ = NW * 32 * NG, DT = HD / 32;
   constexpr int REC = (DT * 16 + 2) * 64;
   const int lane = threadIdx.x, h = lane >> 5, l32 = lane & 31;
-  const int wave = blockIdx.x % NW, unit = blockIdx.x / NW;
+  const int g = blockIdx.x % NG, wave = (blockIdx.x / NG) % NW, unit = blockIdx.x / (NG * NW);
   const int qblk = unit % nqb, bh = unit / nqb;
   const int head = bh % H, b = bh / H;
   const int D = H * HD;
   auto rec = [&](int p, int g) __attribute__((always_inline)) {
     return part + ((static_cast<size_t>(unit) * nsplit + p) * NW + wave) * (NG * REC) + g * REC;
   };
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
+  {
     const int j = qblk * BQ + wave * (32 * NG) + g * 32 + l32;
     // (loops unrolled over the largest piece count, so that mp stays in registers)
     float mp[kMaxSplit];
@@ -738,7 +738,7 @@ static hipError_t attn_launch(const uint16_t* q, const uint16_t* k, int ld, cons
     configured = true;
   }
   const size_t units = static_cast<size_t>(p.nqb) * n_head * B;
-  if (units * p.nsplit * 8 > 0x7fffffffu) return hipErrorInvalidValue;
+  if (units * p.nsplit * 8 * NG > 0x7fffffffu) return hipErrorInvalidValue;
   if ((p.nsplit > 1) != SPLIT) return hipErrorInvalidValue;
   float* part = static_cast<float*>(split_ws);
   if (SPLIT && (!part || reinterpret_cast<uintptr_t>(part) % 16)) return hipErrorInvalidValue;
@@ -748,7 +748,7 @@ static hipError_t attn_launch(const uint16_t* q, const uint16_t* k, int ld, cons
   if constexpr (SPLIT) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    attn_merge_kernel<HD, NG><<<static_cast<unsigned>(units * 8), 64, 0, s>>>(part, out, N, n_head,
+    attn_merge_kernel<HD, NG><<<static_cast<unsigned>(units * 8 * NG), 64, 0, s>>>(part, out, N, n_head,
                                                                              p.nqb, p.nsplit);
   }
   return hipGetLastError();
